@@ -1,0 +1,406 @@
+// libdflash C ABI: argument checks, workspace layout and the launch sequence
+// of each call.  See include/dflash.h for the contract.
+//
+// Pages: [DflashDraft] (docs.rs memra_engine::dflash::DflashDraft) sections
+// "ctx_features", "forward", "ingest_ctx", "forward_round", "rope_yarn";
+// [memra dflash module] "DflashKv"; [atlas dflash_head] "DflashScratch".
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dflash.h"
+#include "kernels.h"
+
+struct dflash_model {
+    dflash_cfg cfg;
+    dflash_weights w;
+    std::vector<dflash_layer_weights> layers;
+    double inv_freq[dfl::MAX_HALF_DIM];
+    double mscale;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *where) {
+    return fail(DFLASH_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int MAX_BLOCK = 16;
+constexpr int MAX_ATTN_SPLITS = 64;
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct WsLayout {
+    size_t x, xn, qkv, q, o, z, feats, part_o, part_ml, gpart, gcnt, total;
+};
+
+WsLayout ws_layout(const dflash_cfg &c, int max_rows) {
+    const size_t H = c.hidden, qd = (size_t)c.n_q_heads * c.head_dim, kvd = (size_t)c.n_kv_heads * c.head_dim;
+    const size_t G = c.n_q_heads / c.n_kv_heads;
+    const size_t qpad = (MAX_BLOCK * G + 15) / 16 * 16;
+    const size_t rows = (size_t)(max_rows > MAX_BLOCK ? max_rows : MAX_BLOCK);
+    WsLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    // fixed-size regions first, so their offsets do not depend on max_rows
+    L.gcnt = take(sizeof(unsigned) * dfl::GEMM_MAX_COUNTERS);
+    L.x = take(4 * MAX_BLOCK * H);
+    L.xn = take(4 * MAX_BLOCK * H);
+    L.q = take(4 * MAX_BLOCK * qd);
+    L.o = take(4 * MAX_BLOCK * qd);
+    L.z = take(4 * MAX_BLOCK * (size_t)c.intermediate);
+    L.part_o = take(4 * (size_t)c.n_kv_heads * MAX_ATTN_SPLITS * qpad * c.head_dim);
+    L.part_ml = take(4 * (size_t)c.n_kv_heads * MAX_ATTN_SPLITS * qpad * 2);
+    L.gpart = take(4 * dfl::GEMM_PART_FLOATS);
+    // row-dependent regions
+    size_t qkv_rows = MAX_BLOCK * (qd + 2 * kvd), ing = rows * 2 * kvd;
+    L.qkv = take(4 * (qkv_rows > ing ? qkv_rows : ing));
+    L.feats = take(4 * rows * H);
+    L.total = off;
+    return L;
+}
+
+int wtype(const dflash_cfg &c) { return c.weight_dtype; }
+
+int check_matrix(const dflash_cfg &c, const dflash_matrix &m, const char *name, int layer) {
+    if (!aligned(m.data, 16)) return fail(DFLASH_E_INVAL, "layer %d %s: data pointer null or not 16-byte aligned", layer, name);
+    if (c.weight_dtype == DFLASH_FP8_E4M3) {
+        if (!aligned(m.scale, 4)) return fail(DFLASH_E_INVAL, "layer %d %s: fp8 weights need a row-scale pointer", layer, name);
+    } else if (m.scale) {
+        return fail(DFLASH_E_INVAL, "layer %d %s: scale given for non-fp8 weights", layer, name);
+    }
+    return DFLASH_OK;
+}
+
+int check_vec(const float *p, const char *name, int layer) {
+    if (!aligned(p, 16)) return fail(DFLASH_E_INVAL, "layer %d %s: gain pointer null or not 16-byte aligned", layer, name);
+    return DFLASH_OK;
+}
+
+int check_cfg(const dflash_cfg &c) {
+    if (c.n_layers < 0 || c.n_layers > 4096) return fail(DFLASH_E_INVAL, "n_layers %d out of range", c.n_layers);
+    if (c.hidden <= 0 || c.hidden % 256) return fail(DFLASH_E_UNSUPPORTED, "hidden %d must be a positive multiple of 256", c.hidden);
+    if (c.intermediate <= 0 || c.intermediate % 256)
+        return fail(DFLASH_E_UNSUPPORTED, "intermediate %d must be a positive multiple of 256", c.intermediate);
+    if (c.head_dim != 64 && c.head_dim != 128) return fail(DFLASH_E_UNSUPPORTED, "head_dim %d: only 64 and 128 are built", c.head_dim);
+    if (c.n_q_heads <= 0 || c.n_kv_heads <= 0 || c.n_q_heads % c.n_kv_heads)
+        return fail(DFLASH_E_INVAL, "n_q_heads %d must be a positive multiple of n_kv_heads %d", c.n_q_heads, c.n_kv_heads);
+    if (c.n_q_heads / c.n_kv_heads > 16) return fail(DFLASH_E_UNSUPPORTED, "more than 16 q heads per kv head");
+    if ((c.n_q_heads * c.head_dim) % 256) return fail(DFLASH_E_UNSUPPORTED, "n_q_heads*head_dim must be a multiple of 256");
+    if (c.n_taps <= 0 || ((size_t)c.n_taps * c.hidden) % 256) return fail(DFLASH_E_INVAL, "n_taps %d invalid", c.n_taps);
+    if (!(c.rms_eps > 0.f) || !std::isfinite(c.rms_eps)) return fail(DFLASH_E_INVAL, "rms_eps must be positive");
+    if (!(c.rope_base > 1.0) || !std::isfinite(c.rope_base)) return fail(DFLASH_E_INVAL, "rope_base must be > 1");
+    if (c.rope_type == DFLASH_ROPE_YARN) {
+        if (!(c.yarn_factor >= 1.0) || c.yarn_orig_ctx <= 0 || !(c.yarn_beta_fast > 0) || !(c.yarn_beta_slow > 0))
+            return fail(DFLASH_E_INVAL, "bad YaRN parameters");
+    } else if (c.rope_type != DFLASH_ROPE_PLAIN) {
+        return fail(DFLASH_E_INVAL, "unknown rope_type %d", c.rope_type);
+    }
+    const bool ok_types = (c.weight_dtype == DFLASH_F32 && c.kv_dtype == DFLASH_F32) ||
+                          (c.weight_dtype == DFLASH_BF16 && c.kv_dtype == DFLASH_BF16) ||
+                          (c.weight_dtype == DFLASH_FP8_E4M3 && c.kv_dtype == DFLASH_BF16);
+    if (!ok_types) return fail(DFLASH_E_UNSUPPORTED, "weight/kv dtype combination %d/%d not built", c.weight_dtype, c.kv_dtype);
+    if (c.d2_groups < 0) return fail(DFLASH_E_INVAL, "d2_groups must be >= 0");
+    if (c.d2_groups > 0) return fail(DFLASH_E_UNSUPPORTED, "the DFlash2 conv wrap is not built yet");
+    return DFLASH_OK;
+}
+
+// YaRN frequency remap (Peng et al., "YaRN", 2023): dimension pairs that
+// turn fewer than beta_slow times over the original context are divided by
+// the factor, pairs that turn more than beta_fast times keep their
+// frequency, and a linear ramp over the pair index blends the two.
+void rope_table(const dflash_cfg &c, double *inv_freq, double *mscale) {
+    const int half = c.head_dim / 2;
+    const double base = c.rope_base, d = c.head_dim;
+    for (int j = 0; j < half; ++j) inv_freq[j] = std::pow(base, -2.0 * j / d);
+    *mscale = 1.0;
+    if (c.rope_type != DFLASH_ROPE_YARN) return;
+    const double L0 = c.yarn_orig_ctx, f = c.yarn_factor;
+    auto pair_index = [&](double turns) { return d * std::log(L0 / (2.0 * M_PI * turns)) / (2.0 * std::log(base)); };
+    double lo = std::floor(pair_index(c.yarn_beta_fast));
+    double hi = std::ceil(pair_index(c.yarn_beta_slow));
+    if (lo < 0) lo = 0;
+    if (hi > d - 1) hi = d - 1;
+    if (hi == lo) hi = lo + 0.001;
+    for (int j = 0; j < half; ++j) {
+        double ramp = (j - lo) / (hi - lo);
+        ramp = ramp < 0 ? 0 : ramp > 1 ? 1 : ramp;
+        inv_freq[j] *= ramp / f + (1.0 - ramp);
+    }
+    *mscale = 0.1 * std::log(f) + 1.0;
+}
+
+size_t kv_elem(const dflash_cfg &c) { return c.kv_dtype == DFLASH_F32 ? 4 : 2; }
+
+int check_kv(const dflash_model *m, const dflash_kv *kv) {
+    if (!kv) return fail(DFLASH_E_INVAL, "kv is null");
+    if (!aligned(kv->k, 16) || !aligned(kv->v, 16)) return fail(DFLASH_E_INVAL, "kv->k / kv->v null or not 16-byte aligned");
+    if (kv->capacity <= 0 || kv->capacity % 64) return fail(DFLASH_E_INVAL, "kv capacity %d must be a positive multiple of 64", kv->capacity);
+    if (kv->len < 0 || kv->len > kv->capacity) return fail(DFLASH_E_INVAL, "kv len %d outside [0, capacity]", kv->len);
+    (void)m;
+    return DFLASH_OK;
+}
+
+int check_ws(const dflash_model *m, void *ws, size_t ws_bytes, int rows) {
+    if (!aligned(ws, 256)) return fail(DFLASH_E_INVAL, "workspace null or not 256-byte aligned");
+    const size_t need = ws_layout(m->cfg, rows).total;
+    if (ws_bytes < need) return fail(DFLASH_E_INVAL, "workspace of %zu bytes is smaller than the %zu needed for %d rows", ws_bytes, need, rows);
+    return DFLASH_OK;
+}
+
+template <class T>
+T *at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
+
+void *layer_ptr(void *base, const dflash_cfg &c, int cap, int l) {
+    return static_cast<char *>(base) + (size_t)l * c.n_kv_heads * cap * c.head_dim * kv_elem(c);
+}
+
+dfl::GemmSeg seg(const dflash_matrix &m, int n) { return dfl::GemmSeg{m.data, m.scale, n}; }
+
+// ---- launch sequences (arguments already checked) ---------------------------
+
+hipError_t run_ctx_features(const dflash_model *m, const float *taps, int t, float *feats, void *ws, const WsLayout &L,
+                            hipStream_t s) {
+    const dflash_cfg &c = m->cfg;
+    dfl::GemmArgs g{};
+    g.A = taps; g.lda = c.n_taps * c.hidden; g.M = t; g.K = c.n_taps * c.hidden;
+    g.seg[0] = seg(m->w.fc, c.hidden); g.nseg = 1;
+    g.Y = feats; g.ldy = c.hidden; g.epi = dfl::EPI_STORE; g.wtype = wtype(c);
+    hipError_t e = dfl::gemm(g, at<float>(ws, L.gpart), at<unsigned>(ws, L.gcnt), s);
+    if (e != hipSuccess) return e;
+    return dfl::rmsnorm(feats, c.hidden, m->w.g_hidden_norm, feats, c.hidden, nullptr, t, c.hidden, c.rms_eps, s);
+}
+
+hipError_t run_ingest(const dflash_model *m, dflash_kv *kv, const float *feats, const int32_t *pos, int t, void *ws,
+                      const WsLayout &L, hipStream_t s) {
+    const dflash_cfg &c = m->cfg;
+    const int kvd = c.n_kv_heads * c.head_dim;
+    float *kvbuf = at<float>(ws, L.qkv);
+    for (int l = 0; l < c.n_layers; ++l) {
+        const dflash_layer_weights &W = m->layers[l];
+        dfl::GemmArgs g{};
+        g.A = feats; g.lda = c.hidden; g.M = t; g.K = c.hidden;
+        g.seg[0] = seg(W.wk, kvd); g.seg[1] = seg(W.wv, kvd); g.nseg = 2;
+        g.Y = kvbuf; g.ldy = 2 * kvd; g.epi = dfl::EPI_STORE; g.wtype = wtype(c);
+        hipError_t e = dfl::gemm(g, at<float>(ws, L.gpart), at<unsigned>(ws, L.gcnt), s);
+        if (e != hipSuccess) return e;
+        dfl::RopeArgs r{};
+        r.src = kvbuf; r.ld = 2 * kvd; r.q_off = -1; r.k_off = 0; r.v_off = kvd;
+        r.g_q = nullptr; r.g_k = W.g_k; r.pos = pos; r.rows = t;
+        r.nq = c.n_q_heads; r.nkv = c.n_kv_heads; r.d = c.head_dim; r.eps = c.rms_eps; r.mscale = (float)m->mscale;
+        r.q_out = nullptr; r.kc = layer_ptr(kv->k, c, kv->capacity, l); r.vc = layer_ptr(kv->v, c, kv->capacity, l);
+        r.cap = kv->capacity; r.row0 = kv->len; r.kv_f32 = c.kv_dtype == DFLASH_F32;
+        memcpy(r.inv_freq, m->inv_freq, sizeof r.inv_freq);
+        e = dfl::qk_norm_rope(r, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *noise, const int32_t *pos, int b, float *out,
+                     void *ws, const WsLayout &L, hipStream_t s) {
+    const dflash_cfg &c = m->cfg;
+    const int H = c.hidden, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim, I = c.intermediate;
+    float *X = at<float>(ws, L.x), *XN = at<float>(ws, L.xn), *QKV = at<float>(ws, L.qkv);
+    float *Q = at<float>(ws, L.q), *O = at<float>(ws, L.o), *Z = at<float>(ws, L.z);
+    float *gp = at<float>(ws, L.gpart);
+    unsigned *gc = at<unsigned>(ws, L.gcnt);
+    const int wt = wtype(c);
+    hipError_t e;
+    if (c.n_layers == 0) return dfl::rmsnorm(noise, H, m->w.g_norm, out, H, nullptr, b, H, c.rms_eps, s);
+
+    for (int l = 0; l < c.n_layers; ++l) {
+        const dflash_layer_weights &W = m->layers[l];
+        // input norm (layer 0 also copies the block embeddings into the residual stream)
+        e = l == 0 ? dfl::rmsnorm(noise, H, W.g_in, XN, H, X, b, H, c.rms_eps, s)
+                   : dfl::rmsnorm(X, H, W.g_in, XN, H, nullptr, b, H, c.rms_eps, s);
+        if (e != hipSuccess) return e;
+        // q | k | v projections of the block rows
+        dfl::GemmArgs g{};
+        g.A = XN; g.lda = H; g.M = b; g.K = H;
+        g.seg[0] = seg(W.wq, qd); g.seg[1] = seg(W.wk, kvd); g.seg[2] = seg(W.wv, kvd); g.nseg = 3;
+        g.Y = QKV; g.ldy = qd + 2 * kvd; g.epi = dfl::EPI_STORE; g.wtype = wt;
+        if ((e = dfl::gemm(g, gp, gc, s)) != hipSuccess) return e;
+        // q/k head norm + rope; block K/V into cache rows [len, len + b)
+        dfl::RopeArgs r{};
+        r.src = QKV; r.ld = qd + 2 * kvd; r.q_off = 0; r.k_off = qd; r.v_off = qd + kvd;
+        r.g_q = W.g_q; r.g_k = W.g_k; r.pos = pos; r.rows = b;
+        r.nq = c.n_q_heads; r.nkv = c.n_kv_heads; r.d = c.head_dim; r.eps = c.rms_eps; r.mscale = (float)m->mscale;
+        r.q_out = Q; r.kc = layer_ptr(kv->k, c, kv->capacity, l); r.vc = layer_ptr(kv->v, c, kv->capacity, l);
+        r.cap = kv->capacity; r.row0 = kv->len; r.kv_f32 = c.kv_dtype == DFLASH_F32;
+        memcpy(r.inv_freq, m->inv_freq, sizeof r.inv_freq);
+        if ((e = dfl::qk_norm_rope(r, s)) != hipSuccess) return e;
+        // attention over all len + b keys
+        dfl::AttnArgs a{};
+        a.q = Q; a.kc = r.kc; a.vc = r.vc; a.cap = kv->capacity; a.n_keys = kv->len + b;
+        a.b = b; a.nq = c.n_q_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim; a.kv_f32 = r.kv_f32;
+        a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+        dfl::attn_plan(a, MAX_ATTN_SPLITS);
+        a.part_o = at<float>(ws, L.part_o); a.part_ml = at<float>(ws, L.part_ml); a.out = O;
+        if ((e = dfl::attention(a, s)) != hipSuccess) return e;
+        // o_proj + residual
+        g = dfl::GemmArgs{};
+        g.A = O; g.lda = qd; g.M = b; g.K = qd; g.seg[0] = seg(W.wo, H); g.nseg = 1;
+        g.Y = X; g.ldy = H; g.epi = dfl::EPI_ADD; g.wtype = wt;
+        if ((e = dfl::gemm(g, gp, gc, s)) != hipSuccess) return e;
+        // post-attention norm, gate|up + SwiGLU, down + residual
+        if ((e = dfl::rmsnorm(X, H, W.g_post, XN, H, nullptr, b, H, c.rms_eps, s)) != hipSuccess) return e;
+        g = dfl::GemmArgs{};
+        g.A = XN; g.lda = H; g.M = b; g.K = H; g.seg[0] = seg(W.wg, I); g.seg[1] = seg(W.wu, I); g.nseg = 2;
+        g.Y = Z; g.ldy = I; g.epi = dfl::EPI_SWIGLU; g.wtype = wt;
+        if ((e = dfl::gemm(g, gp, gc, s)) != hipSuccess) return e;
+        g = dfl::GemmArgs{};
+        g.A = Z; g.lda = I; g.M = b; g.K = I; g.seg[0] = seg(W.wd, H); g.nseg = 1;
+        g.Y = X; g.ldy = H; g.epi = dfl::EPI_ADD; g.wtype = wt;
+        if ((e = dfl::gemm(g, gp, gc, s)) != hipSuccess) return e;
+    }
+    return dfl::rmsnorm(X, H, m->w.g_norm, out, H, nullptr, b, H, c.rms_eps, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dflash_last_error(void) { return g_err.c_str(); }
+
+int dflash_load_weights(const dflash_cfg *cfg, const dflash_weights *w, dflash_model **out) {
+    g_err.clear();
+    if (!cfg || !w || !out) return fail(DFLASH_E_INVAL, "null argument");
+    *out = nullptr;
+    int rc = check_cfg(*cfg);
+    if (rc) return rc;
+    const dflash_cfg &c = *cfg;
+    if ((rc = check_matrix(c, w->fc, "fc", -1))) return rc;
+    if ((rc = check_vec(w->g_hidden_norm, "hidden_norm", -1)) || (rc = check_vec(w->g_norm, "norm", -1))) return rc;
+    if (c.n_layers > 0 && !w->layers) return fail(DFLASH_E_INVAL, "layers array is null");
+    for (int l = 0; l < c.n_layers; ++l) {
+        const dflash_layer_weights &L = w->layers[l];
+        const dflash_matrix *mats[] = {&L.wq, &L.wk, &L.wv, &L.wo, &L.wg, &L.wu, &L.wd};
+        const char *names[] = {"wq", "wk", "wv", "wo", "wg", "wu", "wd"};
+        for (int i = 0; i < 7; ++i)
+            if ((rc = check_matrix(c, *mats[i], names[i], l))) return rc;
+        if ((rc = check_vec(L.g_in, "g_in", l)) || (rc = check_vec(L.g_post, "g_post", l)) ||
+            (rc = check_vec(L.g_q, "g_q", l)) || (rc = check_vec(L.g_k, "g_k", l)))
+            return rc;
+    }
+    dflash_model *m = new dflash_model{};
+    m->cfg = c;
+    m->w = *w;
+    m->layers.assign(w->layers, w->layers + c.n_layers);
+    m->w.layers = m->layers.data();
+    rope_table(c, m->inv_freq, &m->mscale);
+    *out = m;
+    return DFLASH_OK;
+}
+
+void dflash_free(dflash_model *m) { delete m; }
+
+size_t dflash_workspace_bytes(const dflash_model *m, int32_t max_rows) {
+    if (!m || max_rows < 0) return 0;
+    return ws_layout(m->cfg, max_rows).total;
+}
+
+int dflash_rope_table(const dflash_model *m, double *inv_freq, int32_t n, double *mscale) {
+    g_err.clear();
+    if (!m || !inv_freq || !mscale) return fail(DFLASH_E_INVAL, "null argument");
+    if (n != m->cfg.head_dim / 2) return fail(DFLASH_E_INVAL, "table has head_dim/2 = %d entries", m->cfg.head_dim / 2);
+    memcpy(inv_freq, m->inv_freq, sizeof(double) * n);
+    *mscale = m->mscale;
+    return DFLASH_OK;
+}
+
+int dflash_ctx_features(const dflash_model *m, const float *taps, int32_t t, float *feats, void *ws, size_t ws_bytes,
+                        void *stream) {
+    g_err.clear();
+    if (!m) return fail(DFLASH_E_INVAL, "model is null");
+    if (t < 0) return fail(DFLASH_E_INVAL, "t = %d is negative", t);
+    if (t == 0) return DFLASH_OK;
+    if (!aligned(taps, 16) || !aligned(feats, 16)) return fail(DFLASH_E_INVAL, "taps / feats null or not 16-byte aligned");
+    int rc = check_ws(m, ws, ws_bytes, t);
+    if (rc) return rc;
+    hipError_t e = run_ctx_features(m, taps, t, feats, ws, ws_layout(m->cfg, t), (hipStream_t)stream);
+    return e == hipSuccess ? DFLASH_OK : hip_fail(e, "ctx_features");
+}
+
+int dflash_ingest_ctx(const dflash_model *m, dflash_kv *kv, const float *feats, const int32_t *pos_new, int32_t t,
+                      void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    if (!m) return fail(DFLASH_E_INVAL, "model is null");
+    int rc = check_kv(m, kv);
+    if (rc) return rc;
+    if (t < 0) return fail(DFLASH_E_INVAL, "t = %d is negative", t);
+    if ((int64_t)kv->len + t > kv->capacity)
+        return fail(DFLASH_E_CAPACITY, "len %d + t %d exceeds capacity %d", kv->len, t, kv->capacity);
+    if (t == 0) return DFLASH_OK;
+    if (!aligned(feats, 16) || !aligned(pos_new, 4)) return fail(DFLASH_E_INVAL, "feats / pos_new null or misaligned");
+    if ((rc = check_ws(m, ws, ws_bytes, t))) return rc;
+    hipError_t e = run_ingest(m, kv, feats, pos_new, t, ws, ws_layout(m->cfg, t), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ingest_ctx");
+    kv->len += t;
+    return DFLASH_OK;
+}
+
+int dflash_forward_round(const dflash_model *m, dflash_kv *kv, const float *noise_emb, const int32_t *pos_block,
+                         int32_t b, float *out, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    if (!m) return fail(DFLASH_E_INVAL, "model is null");
+    int rc = check_kv(m, kv);
+    if (rc) return rc;
+    if (b < 1 || b > MAX_BLOCK) return fail(DFLASH_E_INVAL, "block size b = %d outside [1, 16]", b);
+    if ((int64_t)kv->len + b > kv->capacity)
+        return fail(DFLASH_E_CAPACITY, "len %d + b %d exceeds capacity %d", kv->len, b, kv->capacity);
+    if (!aligned(noise_emb, 16) || !aligned(out, 16) || !aligned(pos_block, 4))
+        return fail(DFLASH_E_INVAL, "noise_emb / out / pos_block null or misaligned");
+    if ((rc = check_ws(m, ws, ws_bytes, 0))) return rc;
+    hipError_t e = run_round(m, kv, noise_emb, pos_block, b, out, ws, ws_layout(m->cfg, 0), (hipStream_t)stream);
+    return e == hipSuccess ? DFLASH_OK : hip_fail(e, "forward_round");
+}
+
+int dflash_forward_full(const dflash_model *m, const float *taps, const float *noise_emb, const int32_t *pos, int32_t n,
+                        int32_t b, float *out, dflash_kv *scratch, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    if (!m) return fail(DFLASH_E_INVAL, "model is null");
+    int rc = check_kv(m, scratch);
+    if (rc) return rc;
+    if (n < 0) return fail(DFLASH_E_INVAL, "n = %d is negative", n);
+    if (b < 1 || b > MAX_BLOCK) return fail(DFLASH_E_INVAL, "block size b = %d outside [1, 16]", b);
+    if ((int64_t)n + b > scratch->capacity)
+        return fail(DFLASH_E_CAPACITY, "n %d + b %d exceeds scratch capacity %d", n, b, scratch->capacity);
+    if ((n > 0 && !aligned(taps, 16)) || !aligned(noise_emb, 16) || !aligned(out, 16) || !aligned(pos, 4))
+        return fail(DFLASH_E_INVAL, "taps / noise_emb / out / pos null or misaligned");
+    if ((rc = check_ws(m, ws, ws_bytes, n))) return rc;
+    const WsLayout L = ws_layout(m->cfg, n);
+    hipStream_t s = (hipStream_t)stream;
+    float *feats = at<float>(ws, L.feats);
+    hipError_t e = hipSuccess;
+    dflash_kv kv = *scratch;
+    kv.len = 0;
+    if (n > 0) {
+        e = run_ctx_features(m, taps, n, feats, ws, L, s);
+        if (e == hipSuccess) e = run_ingest(m, &kv, feats, pos, n, ws, L, s);
+        kv.len = n;
+    }
+    if (e == hipSuccess) e = run_round(m, &kv, noise_emb, pos + n, b, out, ws, L, s);
+    if (e != hipSuccess) return hip_fail(e, "forward_full");
+    scratch->len = n;
+    return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Device-side helpers shared by the gfx950 kernels of libdflash.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define DFL_WAVE 64
+
+// storage types (same values as the public DFLASH_* constants)
+enum { WT_F32 = 0, WT_BF16 = 1, WT_FP8 = 2 };
+
+// ---------------------------------------------------------------------------
+// MFMA on gfx950.  Lane layouts (lane l, g = l / 16):
+//   16x16x32 bf16: A[row l%16][k 8g..8g+7], B[k 8g..8g+7][col l%16],
+//                  C[row 4g+j][col l%16], j = 0..3.
+//   16x16x4 f32:   A[row l%16][k g], B[k g][col l%16], C as above.
+// Any permutation of the reduction index k is allowed, as long as A and B
+// use the same one.  The kernels rely on this to load each lane's operands
+// as contiguous 16-byte pieces.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// bf16 bit patterns <-> float
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// round-to-nearest-even f32 -> bf16 bits (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Split 8 floats into bf16 hi + lo parts, hi = rne(x), lo = rne(x - hi).
+// hi + lo carries about 16 significant bits, so a bf16 MFMA over (hi, lo)
+// keeps the activation side close to f32 precision.
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t h0 = f32_to_bf16_bits(x[2 * i]), h1 = f32_to_bf16_bits(x[2 * i + 1]);
+        float r0 = x[2 * i] - bf16_bits_to_f32(h0), r1 = x[2 * i + 1] - bf16_bits_to_f32(h1);
+        h[i] = h0 | (h1 << 16);
+        l[i] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
+    }
+    u32x4 hv = {h[0], h[1], h[2], h[3]};
+    u32x4 lv = {l[0], l[1], l[2], l[3]};
+    hi = __builtin_bit_cast(bf16x8, hv);
+    lo = __builtin_bit_cast(bf16x8, lv);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = f32_to_bf16_bits(x[2 * i]) | (f32_to_bf16_bits(x[2 * i + 1]) << 16);
+    u32x4 v = {h[0], h[1], h[2], h[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// 8 fp8 e4m3fn codes (two 32-bit words) -> 8 bf16.  The hardware converts
+// to f32 (OCP e4m3fn on gfx950); e4m3 has 4 significant bits, so truncating
+// the f32 to bf16 is exact.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+    auto a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+    auto b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+    auto c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+    auto d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+    u32x4 v;
+    v.x = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xFFFF0000u);
+    v.y = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xFFFF0000u);
+    v.z = (__float_as_uint(c[0]) >> 16) | (__float_as_uint(c[1]) & 0xFFFF0000u);
+    v.w = (__float_as_uint(d[0]) >> 16) | (__float_as_uint(d[1]) & 0xFFFF0000u);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------------------
+// wave reductions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, DFL_WAVE);
+    return v;
+}
+
+// sum / max over the 4 lane groups that share l % 16 (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float group4_sum(float v) {
+    v += __shfl_xor(v, 16, DFL_WAVE);
+    v += __shfl_xor(v, 32, DFL_WAVE);
+    return v;
+}
+__device__ __forceinline__ float group4_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16, DFL_WAVE));
+    v = fmaxf(v, __shfl_xor(v, 32, DFL_WAVE));
+    return v;
+}
+
+// streaming (non-temporal) 16-byte load for weights that are read once
+__device__ __forceinline__ u32x4 ld_stream16(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ float4 ld_f4(const float *p) { return *reinterpret_cast<const float4 *>(p); }

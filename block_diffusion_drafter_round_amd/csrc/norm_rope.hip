@@ -1,0 +1,118 @@
+// Row RMSNorm, and the q/k head norm + NeoX rope + KV stores.
+//
+// RMSNorm ([DflashDraft] "ctx_features": hidden_norm; the layer norms and the
+// final norm): y = g * x / sqrt(mean(x^2) + eps).  One workgroup per row.
+//
+// Head norm + rope ([memra dflash module] "DflashKv": cached K is
+// normed+roped, V raw; [DflashDraft] "rope_yarn": rope_neox_ff with
+// per-dimension inverse frequencies, then the q/k scale mscale).
+// * One workgroup per row.  It first builds the row's cos/sin table.  The
+//   angle pos * inv_freq[j] and its sin/cos are evaluated in f64, so long
+//   positions keep full accuracy.
+// * Each wave then takes heads in turn.  Lane j < d/2 holds the rope pair
+//   (j, j + d/2) of one head: one wave-wide sum of squares gives the head's
+//   RMS, and the rotation is lane-local.
+// * q goes to a f32 buffer.  k and v go to the layer's cache at rows
+//   row0 + r: K [nkv][cap][d], V transposed [nkv][d][cap].
+#include "common.h"
+#include "kernels.h"
+
+namespace dfl {
+
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ x, int ldx,
+                                                      const float *__restrict__ g, float *y, int ldy,
+                                                      float *xcopy, int H, float eps) {
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const float *xr = x + (size_t)r * ldx;
+    float ss = 0.f;
+    for (int c = tid * 4; c < H; c += 256 * 4) {
+        float4 v = ld_f4(xr + c);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    __shared__ float part[4];
+    if ((tid & 63) == 0) part[tid >> 6] = ss;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float inv = 1.f / sqrtf(tot / (float)H + eps);
+    float *yr = y + (size_t)r * ldy;
+    for (int c = tid * 4; c < H; c += 256 * 4) {
+        float4 v = ld_f4(xr + c), gg = ld_f4(g + c);
+        if (xcopy) *reinterpret_cast<float4 *>(xcopy + (size_t)r * H + c) = v;
+        float4 o = make_float4(gg.x * (v.x * inv), gg.y * (v.y * inv), gg.z * (v.z * inv), gg.w * (v.w * inv));
+        *reinterpret_cast<float4 *>(yr + c) = o;
+    }
+}
+
+hipError_t rmsnorm(const float *x, int ldx, const float *g, float *y, int ldy, float *xcopy, int rows, int H,
+                   float eps, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, x, ldx, g, y, ldy, xcopy, H, eps);
+    return hipGetLastError();
+}
+
+__device__ __forceinline__ void store_kv(void *base, size_t idx, float v, int kv_f32) {
+    if (kv_f32) reinterpret_cast<float *>(base)[idx] = v;
+    else reinterpret_cast<uint16_t *>(base)[idx] = (uint16_t)f32_to_bf16_bits(v);
+}
+
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(RopeArgs a) {
+    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int half = a.d >> 1;
+    __shared__ float cs[MAX_HALF_DIM], sn[MAX_HALF_DIM];
+    if (tid < half) {
+        double th = (double)a.pos[r] * a.inv_freq[tid];
+        double sv, cv;
+        sincos(th, &sv, &cv);
+        cs[tid] = (float)cv;
+        sn[tid] = (float)sv;
+    }
+    __syncthreads();
+
+    const float *row = a.src + (size_t)r * a.ld;
+    const int nqh = a.q_off >= 0 ? a.nq : 0;
+    const int nnorm = nqh + a.nkv;          // heads that get norm + rope
+    const int nheads = nnorm + a.nkv;       // + raw v heads
+    const bool act = lane < half;
+    const float c = act ? cs[lane] : 0.f, s = act ? sn[lane] : 0.f;
+    const size_t crow = (size_t)(a.row0 + r);
+
+    for (int h = wave; h < nheads; h += 4) {
+        if (h < nnorm) {
+            const bool isq = h < nqh;
+            const int hh = isq ? h : h - nqh;
+            const float *src = row + (isq ? a.q_off : a.k_off) + hh * a.d;
+            const float *gain = isq ? a.g_q : a.g_k;
+            const float x0 = act ? src[lane] : 0.f, x1 = act ? src[lane + half] : 0.f;
+            const float ss = wave_sum(x0 * x0 + x1 * x1);
+            const float inv = 1.f / sqrtf(ss / (float)a.d + a.eps);
+            if (act) {
+                const float y0 = gain[lane] * (x0 * inv), y1 = gain[lane + half] * (x1 * inv);
+                const float o0 = (y0 * c - y1 * s) * a.mscale;
+                const float o1 = (y1 * c + y0 * s) * a.mscale;
+                if (isq) {
+                    float *q = a.q_out + ((size_t)r * a.nq + hh) * a.d;
+                    q[lane] = o0;
+                    q[lane + half] = o1;
+                } else {
+                    const size_t base = ((size_t)hh * a.cap + crow) * a.d;
+                    store_kv(a.kc, base + lane, o0, a.kv_f32);
+                    store_kv(a.kc, base + lane + half, o1, a.kv_f32);
+                }
+            }
+        } else if (act) {
+            const int hh = h - nnorm;
+            const float *src = row + a.v_off + hh * a.d;
+            store_kv(a.vc, ((size_t)hh * a.d + lane) * a.cap + crow, src[lane], a.kv_f32);
+            store_kv(a.vc, ((size_t)hh * a.d + lane + half) * a.cap + crow, src[lane + half], a.kv_f32);
+        }
+    }
+}
+
+hipError_t qk_norm_rope(const RopeArgs &a, hipStream_t s) {
+    if (a.rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(qk_norm_rope_kernel, dim3(a.rows), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace dfl

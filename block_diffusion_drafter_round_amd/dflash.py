@@ -1,0 +1,313 @@
+"""ctypes binding of libdflash (include/dflash.h).
+
+The functions keep the C names and only marshal arguments: torch tensors
+become device pointers, and the current torch stream becomes the hipStream_t.
+Every step of the drafter runs in libdflash's HIP kernels.  If the library is
+missing, loading fails with an error; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdflash.so")
+
+DFLASH_OK, DFLASH_E_INVAL, DFLASH_E_CAPACITY, DFLASH_E_UNSUPPORTED, DFLASH_E_HIP = range(5)
+DFLASH_F32, DFLASH_BF16, DFLASH_FP8_E4M3 = 0, 1, 2
+DFLASH_ROPE_PLAIN, DFLASH_ROPE_YARN = 0, 1
+DTYPE_CODES = {"f32": DFLASH_F32, "bf16": DFLASH_BF16, "fp8": DFLASH_FP8_E4M3}
+ROPE_CODES = {"plain": DFLASH_ROPE_PLAIN, "yarn": DFLASH_ROPE_YARN}
+
+
+class DflashError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dflash error {code}: {msg}")
+        self.code = code
+
+
+class dflash_cfg(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("intermediate", C.c_int32),
+                ("n_taps", C.c_int32), ("rms_eps", C.c_float), ("rope_base", C.c_double),
+                ("rope_type", C.c_int32), ("yarn_factor", C.c_double), ("yarn_orig_ctx", C.c_int32),
+                ("yarn_beta_fast", C.c_double), ("yarn_beta_slow", C.c_double),
+                ("weight_dtype", C.c_int32), ("kv_dtype", C.c_int32), ("d2_groups", C.c_int32)]
+
+
+class dflash_matrix(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("scale", C.c_void_p)]
+
+
+class dflash_layer_weights(C.Structure):
+    _fields_ = [(n, dflash_matrix) for n in ("wq", "wk", "wv", "wo", "wg", "wu", "wd")] + \
+               [(n, C.c_void_p) for n in ("g_in", "g_post", "g_q", "g_k")] + \
+               [("attn_w_dyn", dflash_matrix), ("attn_base", C.c_void_p),
+                ("mlp_w_dyn", dflash_matrix), ("mlp_base", C.c_void_p)]
+
+
+class dflash_weights(C.Structure):
+    _fields_ = [("fc", dflash_matrix), ("g_hidden_norm", C.c_void_p), ("g_norm", C.c_void_p),
+                ("layers", C.POINTER(dflash_layer_weights))]
+
+
+class dflash_kv(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("capacity", C.c_int32), ("len", C.c_int32)]
+
+
+_lib = None
+EXPORTS = ("dflash_load_weights", "dflash_free", "dflash_workspace_bytes", "dflash_ctx_features",
+           "dflash_ingest_ctx", "dflash_forward_round", "dflash_forward_full", "dflash_last_error",
+           "dflash_rope_table")
+
+
+def lib():
+    """Load libdflash.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    L = C.CDLL(LIB_PATH)
+    vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+    L.dflash_load_weights.argtypes = [C.POINTER(dflash_cfg), C.POINTER(dflash_weights), C.POINTER(vp)]
+    L.dflash_free.argtypes = [vp]
+    L.dflash_free.restype = None
+    L.dflash_workspace_bytes.argtypes = [vp, i32]
+    L.dflash_workspace_bytes.restype = sz
+    L.dflash_ctx_features.argtypes = [vp, vp, i32, vp, vp, sz, vp]
+    L.dflash_ingest_ctx.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, i32, vp, sz, vp]
+    L.dflash_forward_round.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, i32, vp, vp, sz, vp]
+    L.dflash_forward_full.argtypes = [vp, vp, vp, vp, i32, i32, vp, C.POINTER(dflash_kv), vp, sz, vp]
+    L.dflash_last_error.restype = C.c_char_p
+    L.dflash_rope_table.argtypes = [vp, C.POINTER(C.c_double), i32, C.POINTER(C.c_double)]
+    for name in EXPORTS:
+        if name not in ("dflash_free", "dflash_workspace_bytes", "dflash_last_error"):
+            getattr(L, name).restype = C.c_int
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != DFLASH_OK:
+        raise DflashError(rc, lib().dflash_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# --------------------------------------------------------------------------
+# C calls, same names
+# --------------------------------------------------------------------------
+
+def dflash_load_weights(cfg: dflash_cfg, weights: dflash_weights) -> int:
+    h = C.c_void_p()
+    _check(lib().dflash_load_weights(C.byref(cfg), C.byref(weights), C.byref(h)))
+    return h.value
+
+
+def dflash_free(model: int) -> None:
+    lib().dflash_free(model)
+
+
+def dflash_workspace_bytes(model: int, max_rows: int) -> int:
+    return int(lib().dflash_workspace_bytes(model, max_rows))
+
+
+def dflash_ctx_features(model, taps, t, feats, ws, ws_bytes, stream=None) -> None:
+    _check(lib().dflash_ctx_features(model, _ptr(taps), t, _ptr(feats), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dflash_ingest_ctx(model, kv: dflash_kv, feats, pos_new, t, ws, ws_bytes, stream=None) -> None:
+    _check(lib().dflash_ingest_ctx(model, C.byref(kv), _ptr(feats), _ptr(pos_new), t, _ptr(ws), ws_bytes,
+                                   _stream(stream)))
+
+
+def dflash_forward_round(model, kv: dflash_kv, noise_emb, pos_block, b, out, ws, ws_bytes, stream=None) -> None:
+    _check(lib().dflash_forward_round(model, C.byref(kv), _ptr(noise_emb), _ptr(pos_block), b, _ptr(out),
+                                      _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dflash_forward_full(model, taps, noise_emb, pos, n, b, out, scratch: dflash_kv, ws, ws_bytes,
+                        stream=None) -> None:
+    _check(lib().dflash_forward_full(model, _ptr(taps), _ptr(noise_emb), _ptr(pos), n, b, _ptr(out),
+                                     C.byref(scratch), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dflash_last_error() -> str:
+    return lib().dflash_last_error().decode()
+
+
+def dflash_rope_table(model, half: int):
+    buf = (C.c_double * half)()
+    ms = C.c_double()
+    _check(lib().dflash_rope_table(model, buf, half, C.byref(ms)))
+    return list(buf), ms.value
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers: configs, device weights, KV storage, workspace
+# --------------------------------------------------------------------------
+
+def make_cfg(c) -> dflash_cfg:
+    """A dflash_cfg from any object with the drafter config attribute names."""
+    return dflash_cfg(
+        n_layers=c.n_layers, hidden=c.hidden, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads,
+        head_dim=c.head_dim, intermediate=c.intermediate, n_taps=c.n_taps, rms_eps=c.rms_eps,
+        rope_base=c.rope_base, rope_type=ROPE_CODES[c.rope_type], yarn_factor=c.yarn_factor,
+        yarn_orig_ctx=c.yarn_orig_ctx, yarn_beta_fast=c.yarn_beta_fast, yarn_beta_slow=c.yarn_beta_slow,
+        weight_dtype=DTYPE_CODES[c.weight_dtype], kv_dtype=DTYPE_CODES[c.kv_dtype], d2_groups=c.d2_groups)
+
+
+def _to_device(arr, device):
+    t = torch.from_numpy(arr)
+    if t.dtype == torch.uint16:
+        t = t.view(torch.int16)
+    return t.to(device).contiguous()
+
+
+class DeviceWeights:
+    """Uploads stored weights (objects with ``.dtype``, ``.data`` and ``.scale``
+    per matrix) to the GPU and builds the dflash_weights struct over them.
+    The tensors live as long as this object does."""
+
+    MATS = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
+
+    def __init__(self, stored, device="cuda"):
+        self.tensors = []
+        self.cfg = stored.cfg
+
+        def mat(sm):
+            d = _to_device(sm.data, device)
+            s = _to_device(sm.scale, device) if sm.scale is not None else None
+            self.tensors += [d, s]
+            return dflash_matrix(d.data_ptr(), s.data_ptr() if s is not None else None)
+
+        def vec(a):
+            t = _to_device(a, device)
+            self.tensors.append(t)
+            return t.data_ptr()
+
+        L = len(stored.layers)
+        self.layer_arr = (dflash_layer_weights * max(L, 1))()
+        for l, ls in enumerate(stored.layers):
+            lw = self.layer_arr[l]
+            for n in self.MATS:
+                setattr(lw, n, mat(ls[n]))
+            for n in ("g_in", "g_post", "g_q", "g_k"):
+                setattr(lw, n, vec(ls[n]))
+            if "attn.w_dyn" in ls:
+                lw.attn_w_dyn = mat(ls["attn.w_dyn"])
+                lw.attn_base = vec(ls["attn.base"])
+                lw.mlp_w_dyn = mat(ls["mlp.w_dyn"])
+                lw.mlp_base = vec(ls["mlp.base"])
+        self.struct = dflash_weights(fc=mat(stored.fc), g_hidden_norm=vec(stored.g_hidden_norm),
+                                     g_norm=vec(stored.g_norm), layers=self.layer_arr)
+
+
+class KVCache:
+    """Device storage for one dflash_kv: K [L][nkv][cap][d], V [L][nkv][d][cap]."""
+
+    def __init__(self, cfg, capacity: int, device="cuda"):
+        dt = torch.float32 if cfg.kv_dtype == "f32" else torch.bfloat16
+        L, h, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+        self.k = torch.zeros((max(L, 1), h, capacity, d), dtype=dt, device=device)
+        self.v = torch.zeros((max(L, 1), h, d, capacity), dtype=dt, device=device)
+        self.c = dflash_kv(self.k.data_ptr(), self.v.data_ptr(), capacity, 0)
+
+    @property
+    def len(self) -> int:
+        return self.c.len
+
+    @len.setter
+    def len(self, n: int):
+        self.c.len = n
+
+    def prefill(self, k_stored, v_stored) -> None:
+        """Write stored rows [L][nkv][rows][d] (f32, or bf16 bits as uint16)
+        into rows [0, rows) and set len = rows."""
+        rows = k_stored.shape[2]
+        k = _to_device(k_stored, self.k.device).view(self.k.dtype)
+        v = _to_device(v_stored, self.k.device).view(self.v.dtype)
+        self.k[:, :, :rows] = k
+        self.v[:, :, :, :rows] = v.transpose(-1, -2)
+        self.c.len = rows
+
+    def rows(self, layer: int, start: int, stop: int):
+        """(K, V) of rows [start, stop) of one layer as [rows, nkv, d] tensors."""
+        return (self.k[layer, :, start:stop].transpose(0, 1),
+                self.v[layer, :, :, start:stop].permute(2, 0, 1))
+
+
+class Drafter:
+    """A loaded model plus one workspace; wraps the five calls with torch
+    tensors.  The caller supplies KV storage (:class:`KVCache`)."""
+
+    def __init__(self, stored, device="cuda", max_rows: int = 16):
+        self.cfg = stored.cfg
+        self.device = torch.device(device)
+        self.weights = DeviceWeights(stored, device)
+        self.ccfg = make_cfg(self.cfg)
+        self.model = dflash_load_weights(self.ccfg, self.weights.struct)
+        self.max_rows = 0
+        self.ws = None
+        self.ensure_rows(max_rows)
+
+    def ensure_rows(self, rows: int):
+        if rows > self.max_rows or self.ws is None:
+            self.ws_bytes = dflash_workspace_bytes(self.model, rows)
+            self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=self.device)
+            self.max_rows = rows
+
+    def __del__(self):
+        try:
+            if getattr(self, "model", None):
+                dflash_free(self.model)
+                self.model = None
+        except Exception:
+            pass
+
+    def ctx_features(self, taps: torch.Tensor) -> torch.Tensor:
+        t = taps.shape[0]
+        self.ensure_rows(t)
+        feats = torch.empty((t, self.cfg.hidden), dtype=torch.float32, device=self.device)
+        dflash_ctx_features(self.model, taps, t, feats, self.ws, self.ws_bytes)
+        return feats
+
+    def ingest_ctx(self, kv: KVCache, feats: torch.Tensor, pos_new: torch.Tensor) -> None:
+        t = feats.shape[0]
+        self.ensure_rows(t)
+        dflash_ingest_ctx(self.model, kv.c, feats, pos_new, t, self.ws, self.ws_bytes)
+
+    def forward_round(self, kv: KVCache, noise_emb: torch.Tensor, pos_block: torch.Tensor,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+        b = noise_emb.shape[0]
+        if out is None:
+            out = torch.empty((b, self.cfg.hidden), dtype=torch.float32, device=self.device)
+        dflash_forward_round(self.model, kv.c, noise_emb, pos_block, b, out, self.ws, self.ws_bytes)
+        return out
+
+    def forward_full(self, taps: torch.Tensor, noise_emb: torch.Tensor, pos: torch.Tensor,
+                     scratch: KVCache | None = None) -> torch.Tensor:
+        n, b = taps.shape[0], noise_emb.shape[0]
+        self.ensure_rows(n)
+        if scratch is None:
+            scratch = KVCache(self.cfg, max(64, (n + b + 63) // 64 * 64), self.device)
+        out = torch.empty((b, self.cfg.hidden), dtype=torch.float32, device=self.device)
+        dflash_forward_full(self.model, taps, noise_emb, pos, n, b, out, scratch.c, self.ws, self.ws_bytes)
+        return out

@@ -1,0 +1,222 @@
+/*
+ * dflash.h — C ABI of the MI355X (gfx950) DFlash block-diffusion drafter
+ * forward.
+ *
+ * The drafter is a small Qwen3-class transformer that drafts a whole block of
+ * b <= 16 tokens in one non-causal forward.  It is conditioned on context
+ * features hidden_norm(fc(concat of the target's tapped hidden states)),
+ * which are served from an append-only draft KV cache.
+ *
+ * Sources (the pages these calls implement):
+ *  [memra dflash module]  docs.rs memra_engine::dflash, module index
+ *                         (overview, "DflashKv", "Dflash2Conv").
+ *  [DflashDraft]          docs.rs memra_engine::dflash::DflashDraft, struct page
+ *                         (fields, "ctx_features", "forward", "forward_block",
+ *                          "ingest_ctx", "forward_round", "d2_conv_prepare",
+ *                          "d2_conv_finish", "rope_yarn").
+ *  [atlas dflash_head]    spark_model::layers::dflash_head, module page
+ *                         (overview, "DflashLayer", "DflashQuantization",
+ *                          "DflashScratch", "DflashProposerState").
+ *
+ * Conventions for every call
+ *  - Pointers named "device" point into GPU memory of the current HIP device.
+ *    Pointers named "host" point into host memory.  The caller owns all
+ *    memory.  The library allocates no device memory, and it copies nothing
+ *    between host and device.
+ *  - Compute calls are asynchronous on `stream` (a hipStream_t; NULL means the
+ *    default stream).  They never synchronise the host.  Inputs must stay
+ *    alive and unchanged until the stream has passed the call.
+ *  - Return value: DFLASH_OK (0) or an error code.  dflash_last_error()
+ *    returns a message for the calling thread's last error.  All argument
+ *    checks run before any HIP call.  On an error nothing has been enqueued,
+ *    and kv->len is unchanged.  A HIP launch failure is DFLASH_E_HIP.
+ *  - A model may serve several streams at once, each with its own workspace.
+ *    One dflash_kv and one workspace must not be used by two calls in flight
+ *    at the same time.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- error codes ------------------------------------------------------- */
+#define DFLASH_OK            0
+#define DFLASH_E_INVAL       1  /* null/misaligned pointer, bad size or count */
+#define DFLASH_E_CAPACITY    2  /* kv->len + rows would exceed kv->capacity */
+#define DFLASH_E_UNSUPPORTED 3  /* a dtype / shape combination not built */
+#define DFLASH_E_HIP         4  /* HIP runtime or launch error */
+
+/* ---- storage types ----------------------------------------------------- */
+#define DFLASH_F32       0
+#define DFLASH_BF16      1
+#define DFLASH_FP8_E4M3  2   /* OCP e4m3fn codes + one f32 scale per row */
+
+#define DFLASH_ROPE_PLAIN 0
+#define DFLASH_ROPE_YARN  1
+
+/* Model dimensions and options ([DflashDraft] field "cfg"; [atlas
+ * dflash_head] overview).  Supported: hidden, intermediate, n_q_heads*head_dim
+ * and n_taps*hidden are multiples of 256.  head_dim is 64 or 128.  n_q_heads is
+ * a multiple of n_kv_heads, with n_q_heads/n_kv_heads <= 16.  For DFLASH_F32
+ * weights the KV dtype must be DFLASH_F32; otherwise it must be DFLASH_BF16.
+ * d2_groups divides hidden; 0 disables the DFlash2 conv wrap. */
+typedef struct dflash_cfg {
+    int32_t n_layers;
+    int32_t hidden;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t intermediate;
+    int32_t n_taps;           /* tapped target layers; fc input = n_taps*hidden */
+    float   rms_eps;          /* every RMSNorm (hidden_norm, layer norms, q/k head norms, final norm) */
+    double  rope_base;
+    int32_t rope_type;        /* DFLASH_ROPE_PLAIN | DFLASH_ROPE_YARN */
+    double  yarn_factor;      /* YaRN only ([DflashDraft] "rope_yarn") */
+    int32_t yarn_orig_ctx;
+    double  yarn_beta_fast;
+    double  yarn_beta_slow;
+    int32_t weight_dtype;     /* DFLASH_F32 | DFLASH_BF16 | DFLASH_FP8_E4M3 */
+    int32_t kv_dtype;         /* DFLASH_F32 | DFLASH_BF16 */
+    int32_t d2_groups;        /* DFlash2 conv groups G; 0 = no conv wrap */
+} dflash_cfg;
+
+/* One projection matrix, [N_out, K_in] row-major (torch Linear layout), in
+ * cfg.weight_dtype.  For DFLASH_FP8_E4M3, `scale` holds N_out f32 row scales
+ * and W[n,k] = scale[n] * e4m3fn(data[n,k]).  Otherwise `scale` is NULL.
+ * Device pointers, 16-byte aligned. */
+typedef struct dflash_matrix {
+    const void  *data;
+    const float *scale;
+} dflash_matrix;
+
+/* One drafter layer ([atlas dflash_head] "DflashLayer": Qwen3-style weights,
+ * no biases).  Gains are f32 device vectors. */
+typedef struct dflash_layer_weights {
+    dflash_matrix wq;         /* [n_q_heads*head_dim, hidden] */
+    dflash_matrix wk;         /* [n_kv_heads*head_dim, hidden] */
+    dflash_matrix wv;         /* [n_kv_heads*head_dim, hidden] */
+    dflash_matrix wo;         /* [hidden, n_q_heads*head_dim] */
+    dflash_matrix wg;         /* [intermediate, hidden]  SwiGLU gate */
+    dflash_matrix wu;         /* [intermediate, hidden]  SwiGLU up */
+    dflash_matrix wd;         /* [hidden, intermediate]  down */
+    const float  *g_in;       /* [hidden]   input RMSNorm */
+    const float  *g_post;     /* [hidden]   post-attention RMSNorm */
+    const float  *g_q;        /* [head_dim] q head RMSNorm */
+    const float  *g_k;        /* [head_dim] k head RMSNorm */
+    /* DFlash2 conv wrap ([memra dflash module] "Dflash2Conv"); used iff
+     * cfg.d2_groups > 0.  w_dyn: [2*G*2, hidden] in cfg.weight_dtype, output
+     * laid out [half][group][tap].  base: f32 [2][hidden][2] = [half][channel][tap]. */
+    dflash_matrix attn_w_dyn;
+    const float  *attn_base;
+    dflash_matrix mlp_w_dyn;
+    const float  *mlp_base;
+} dflash_layer_weights;
+
+/* All drafter weights ([DflashDraft] fields "fc", "hidden_norm", "norm",
+ * "layers"). */
+typedef struct dflash_weights {
+    dflash_matrix fc;                     /* [hidden, n_taps*hidden] */
+    const float  *g_hidden_norm;          /* [hidden] */
+    const float  *g_norm;                 /* [hidden] final norm */
+    const dflash_layer_weights *layers;   /* host array of cfg.n_layers entries */
+} dflash_weights;
+
+/* Draft KV cache ([memra dflash module] "DflashKv"; one per sequence, as
+ * [atlas dflash_head] "DflashProposerState").  It holds, per layer, the
+ * normed+roped ctx K and the raw ctx V, append-only in committed order.
+ *   k: device, [n_layers][n_kv_heads][capacity][head_dim]   (row-major rows)
+ *   v: device, [n_layers][n_kv_heads][head_dim][capacity]   (transposed: one
+ *      row per head dimension, so that the attention's P.V product streams
+ *      contiguous keys)
+ * Both are in cfg.kv_dtype.  capacity is a positive multiple of 64.  Rows
+ * [0, len) are committed.  forward_round overwrites rows [len, len+b) with
+ * the block's K/V while it runs, and never commits them. */
+typedef struct dflash_kv {
+    void   *k;
+    void   *v;
+    int32_t capacity;
+    int32_t len;
+} dflash_kv;
+
+typedef struct dflash_model dflash_model;   /* opaque host handle */
+
+/* Validate cfg and weights, precompute the rope tables on the host (plain:
+ * inv_freq[j] = base^(-2j/d); YaRN: divided by the per-dimension YaRN ramp
+ * factor, and mscale = 0.1*ln(factor)+1, as [DflashDraft] "rope_yarn"
+ * describes), and return a host handle in *out.  The weight pointers are
+ * borrowed: the caller keeps them alive and unchanged while the model is
+ * used.  Makes no HIP call. */
+int dflash_load_weights(const dflash_cfg *cfg, const dflash_weights *w, dflash_model **out);
+
+/* Release a handle from dflash_load_weights (NULL is allowed). */
+void dflash_free(dflash_model *m);
+
+/* Bytes of device workspace (the per-step scratch of [atlas dflash_head]
+ * "DflashScratch") needed by calls that process up to `max_rows` ctx rows at
+ * once: ctx_features t, ingest_ctx t, or forward_full n.  The workspace must
+ * be 256-byte aligned and zero-filled once before its first use.  The library
+ * leaves its counters at zero after every call.  Returns 0 if max_rows < 0. */
+size_t dflash_workspace_bytes(const dflash_model *m, int32_t max_rows);
+
+/* Context features ([DflashDraft] "ctx_features"): feats = hidden_norm(fc(taps)).
+ *   taps : device f32 [t, n_taps*hidden], the raw tapped target states, taps
+ *          concatenated in order along each row.
+ *   feats: device f32 [t, hidden] (written).
+ * t = 0 is a no-op.  Needs t <= the workspace's max_rows. */
+int dflash_ctx_features(const dflash_model *m, const float *taps, int32_t t,
+                        float *feats, void *ws, size_t ws_bytes, void *stream);
+
+/* Append t committed ctx rows to the draft KV cache ([DflashDraft]
+ * "ingest_ctx").  Per layer: k/v projections of the features, k head-norm,
+ * rope (times the YaRN mscale), and the rows stored at kv->len.  Then
+ * kv->len += t on the host, at enqueue time.
+ *   feats  : device f32 [t, hidden] (from dflash_ctx_features).
+ *   pos_new: device int32 [t], the rows' absolute positions.
+ * DFLASH_E_CAPACITY if kv->len + t > kv->capacity. */
+int dflash_ingest_ctx(const dflash_model *m, dflash_kv *kv, const float *feats,
+                      const int32_t *pos_new, int32_t t, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/* One drafting round over the cached ctx K/V ([DflashDraft] "forward_round").
+ * Only the b block rows are projected per layer.  Their K/V land transiently
+ * at rows [kv->len, kv->len + b), and attention over all kv->len + b keys is
+ * full and non-causal.  kv->len is unchanged.
+ *   noise_emb: device f32 [b, hidden], the block's input embeddings.
+ *   pos_block: device int32 [b], the block rows' absolute positions.
+ *   out      : device f32 [b, hidden], the final normed hidden states (fed to
+ *              the target's lm_head by the caller).
+ * 1 <= b <= 16.  DFLASH_E_CAPACITY if kv->len + b > kv->capacity. */
+int dflash_forward_round(const dflash_model *m, dflash_kv *kv, const float *noise_emb,
+                         const int32_t *pos_block, int32_t b, float *out,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* First-light forward ([DflashDraft] "forward"): full non-causal attention
+ * over [ctx features ; block], with no persistent cache.  It runs
+ * ctx_features over all n ctx rows, resets `scratch` to len 0, ingests the n
+ * rows, and runs one round.  `scratch` is caller KV storage with
+ * capacity >= n + b; afterwards its len is n.
+ *   taps: device f32 [n, n_taps*hidden]; noise_emb: device f32 [b, hidden]
+ *   pos : device int32 [n + b], the ctx positions, then the block positions.
+ *   out : device f32 [b, hidden].
+ * n >= 0, 1 <= b <= 16, and n <= the workspace's max_rows. */
+int dflash_forward_full(const dflash_model *m, const float *taps, const float *noise_emb,
+                        const int32_t *pos, int32_t n, int32_t b, float *out,
+                        dflash_kv *scratch, void *ws, size_t ws_bytes, void *stream);
+
+/* Message for the calling thread's last error ("" if none). */
+const char *dflash_last_error(void);
+
+/* Host-side copy of the rope tables of a loaded model: inv_freq[head_dim/2]
+ * (f64) and the q/k scale.  Lets a caller check them against their own.
+ * Makes no HIP call. */
+int dflash_rope_table(const dflash_model *m, double *inv_freq, int32_t n, double *mscale);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

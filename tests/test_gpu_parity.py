@@ -1,0 +1,150 @@
+"""GPU parity: libdflash (HIP, gfx950) against the fp64 CPU oracle.
+
+Every call goes through the C ABI via the ctypes binding.  Tolerances
+(per-row infinity-norm relative error): 1e-4 for the f32 arm, 2e-2 for bf16
+weights with f32 accumulation.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import dflash_oracle as O
+from tests.gpu_util import check, dev, host, kv_rows_f64, rel_rows, tol_for
+
+pytestmark = pytest.mark.gpu
+
+# A small bf16 drafter with GQA 8:2, head_dim 64 and ragged ctx sizes.
+SMALL_BF16 = synth.DraftConfig(
+    name="small_bf16", n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64,
+    intermediate=768, n_taps=2, weight_dtype="bf16", kv_dtype="bf16", path="round",
+    ctx=100, block=16, seed=21)
+SMALL_BF16_D128 = SMALL_BF16.replace(name="small_bf16_d128", hidden=1024, n_q_heads=8, n_kv_heads=2,
+                                     head_dim=128, seed=22)
+
+
+def _setup(cfg, max_rows=16):
+    from block_diffusion_drafter_round_amd import dflash as D
+    sw = synth.make_weights(cfg)
+    return sw, O.OracleModel(sw), D.Drafter(sw, max_rows=max_rows), D
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    torch.cuda.init()
+
+
+def test_zero_layers_final_norm():
+    cfg = synth.TINY_F32.replace(n_layers=0)
+    sw, m, dr, D = _setup(cfg)
+    noise = synth.make_noise(cfg)
+    kv = D.KVCache(cfg, 64)
+    out = host(dr.forward_round(kv, dev(noise), dev(synth.positions(0, 16))))
+    ref = O.forward_round(m, O.OracleKV(cfg), noise, synth.positions(0, 16))
+    check("L=0 final norm", out, ref, 1e-6)
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_BF16_D128], ids=lambda c: c.name)
+@pytest.mark.parametrize("t", [1, 5, 64])
+def test_ctx_features(cfg, t):
+    sw, m, dr, D = _setup(cfg, max_rows=t)
+    taps = synth.make_taps(cfg, t, stream=t)
+    out = host(dr.ctx_features(dev(taps)))
+    check(f"{cfg.name} ctx_features t={t}", out, O.ctx_features(m, taps), tol_for(cfg) / 10)
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_BF16_D128], ids=lambda c: c.name)
+def test_ingest_cache_rows(cfg):
+    """Cache rows after ingesting in uneven chunks: K normed+roped, V raw, at
+    the right rows and positions.  len advances by t per call."""
+    sw, m, dr, D = _setup(cfg, max_rows=64)
+    n = 37
+    taps = synth.make_taps(cfg, n)
+    pos = synth.positions(1000, n)
+    kv = D.KVCache(cfg, 128)
+    feats = dr.ctx_features(dev(taps))
+    for lo, hi in ((0, 1), (1, 17), (17, 37)):
+        dr.ingest_ctx(kv, feats[lo:hi].contiguous(), dev(pos[lo:hi]))
+        assert kv.len == hi
+    okv = O.OracleKV(cfg)
+    O.ingest_ctx(m, okv, O.ctx_features(m, taps), pos)
+    tol = 1e-5 if cfg.kv_dtype == "f32" else 1e-2
+    for l in range(cfg.n_layers):
+        k, v = kv_rows_f64(kv, l, 0, n)
+        check(f"{cfg.name} layer {l} cached K", k, okv.k[l], tol)
+        check(f"{cfg.name} layer {l} cached V", v, okv.v[l], tol)
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_BF16_D128], ids=lambda c: c.name)
+@pytest.mark.parametrize("b", [16, 5, 1])
+def test_forward_full_vs_oracle(cfg, b):
+    sw, m, dr, D = _setup(cfg, max_rows=cfg.ctx)
+    n = cfg.ctx
+    taps = synth.make_taps(cfg, n)
+    noise = synth.make_noise(cfg, rows=b)
+    pos = synth.positions(0, n + b)
+    out = host(dr.forward_full(dev(taps), dev(noise), dev(pos)))
+    ref = O.forward_full(m, taps, noise, pos, n)
+    check(f"{cfg.name} forward_full n={n} b={b}", out, ref, tol_for(cfg))
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16], ids=lambda c: c.name)
+def test_round_equals_full_bitwise(cfg):
+    """[DflashDraft] forward_round: bit-class-identical to the fresh forward.
+    On the GPU the two run the same kernels, so they must agree bit for bit,
+    also when the cache was filled in several chunks of the same total."""
+    sw, m, dr, D = _setup(cfg, max_rows=cfg.ctx)
+    n, b = cfg.ctx, cfg.block
+    taps = synth.make_taps(cfg, n)
+    noise = dev(synth.make_noise(cfg))
+    pos = dev(synth.positions(0, n + b))
+    full = dr.forward_full(dev(taps), noise, pos)
+    kv = D.KVCache(cfg, (n + b + 63) // 64 * 64)
+    feats = dr.ctx_features(dev(taps))
+    dr.ingest_ctx(kv, feats, pos[:n])
+    r1 = dr.forward_round(kv, noise, pos[n:])
+    r2 = dr.forward_round(kv, noise, pos[n:])
+    assert kv.len == n
+    torch.cuda.synchronize()
+    assert torch.equal(full, r1), "forward_round != forward_full"
+    assert torch.equal(r1, r2), "forward_round is not deterministic"
+
+
+@pytest.mark.parametrize("cfg", [SMALL_BF16], ids=lambda c: c.name)
+def test_multi_round_append_then_round(cfg):
+    """Several rounds: each ingests 16 committed rows, then drafts; every
+    round matches the oracle's cached path."""
+    sw, m, dr, D = _setup(cfg, max_rows=64)
+    kv = D.KVCache(cfg, 256)
+    okv = O.OracleKV(cfg)
+    p = 0
+    for rnd, t in enumerate((40, 16, 16, 3)):
+        taps = synth.make_taps(cfg, t, stream=100 + rnd)
+        pos = synth.positions(p, t)
+        dr.ingest_ctx(kv, dr.ctx_features(dev(taps)), dev(pos))
+        O.ingest_ctx(m, okv, O.ctx_features(m, taps), pos)
+        p += t
+        noise = synth.make_noise(cfg, stream=rnd)
+        bpos = synth.positions(p, cfg.block)
+        out = host(dr.forward_round(kv, dev(noise), dev(bpos)))
+        check(f"{cfg.name} round {rnd} len={p}", out, O.forward_round(m, okv, noise, bpos), tol_for(cfg))
+
+
+def test_errors_leave_state_unchanged():
+    cfg = SMALL_BF16
+    sw, m, dr, D = _setup(cfg, max_rows=64)
+    kv = D.KVCache(cfg, 64)
+    feats = dr.ctx_features(dev(synth.make_taps(cfg, 60)))
+    dr.ingest_ctx(kv, feats, dev(synth.positions(0, 60)))
+    assert kv.len == 60
+    with pytest.raises(D.DflashError) as ei:
+        dr.forward_round(kv, dev(synth.make_noise(cfg)), dev(synth.positions(60, 16)))
+    assert ei.value.code == D.DFLASH_E_CAPACITY
+    with pytest.raises(D.DflashError) as ei:
+        dr.ingest_ctx(kv, feats[:5].contiguous(), dev(synth.positions(60, 5)))
+    assert ei.value.code == D.DFLASH_E_CAPACITY
+    assert kv.len == 60
+    out = dr.forward_round(kv, dev(synth.make_noise(cfg, rows=4)), dev(synth.positions(60, 4)))
+    assert torch.isfinite(out).all()
