@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark: DFlash drafter rounds per second at ctx 4096 on one MI355X.
+
+Workload: the 8-layer drafter (hidden 2048, GQA 32:4, head_dim 128, SwiGLU
+6144, 5 taps, bf16 weights, bf16 KV), random-initialised, on the cached round
+path.  One step (one round) is:
+  1. ctx_features of 16 new tapped rows;
+  2. ingest_ctx of those 16 rows at positions 4080..4095 (len 4080 -> 4096);
+  3. forward_round of a 16-token block at positions 4096..4111, which
+     attends 4112 keys;
+  4. a rewind of len to 4080 on the host (no GPU work).
+
+The KV cache is prefilled once, untimed, through the same calls.  All inputs
+are resident in HBM before the timed region starts.
+
+Printed as one JSON line:
+* value: rounds per second;
+* roofline: the gate|up + SwiGLU GEMM's algorithmic bytes per launch over its
+  average launch time, timed live with HIP events on its stream;
+* cpu_baseline: the fp64 CPU oracle running the same round on a bounded
+  sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "drafter 16-token rounds/sec at ctx 4096 + achieved HBM GB/s fraction"
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, vendor figure
+
+
+def round_bytes(cfg, ctx: int, t: int = 16, b: int = 16) -> dict:
+    """Algorithmic HBM bytes of one round: every weight read once, the
+    attended K/V read once per layer, the new K/V rows written, the taps read.
+    Activations that stay in L2 (<1 MB) are not counted."""
+    wb = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight_dtype]
+    kvb = 4 if cfg.kv_dtype == "f32" else 2
+    H, I, qd, kvd, L = cfg.hidden, cfg.intermediate, cfg.q_dim, cfg.kv_dim, cfg.n_layers
+    layer_w = ((qd + 2 * kvd) * H + H * qd + 3 * I * H) * wb * L
+    fc_w = H * cfg.n_taps * H * wb
+    ingest_w = 2 * kvd * H * wb * L
+    kv_read = (ctx + b) * kvd * 2 * kvb * L
+    kv_write = (t + b) * kvd * 2 * kvb * L
+    taps = t * cfg.n_taps * H * 4
+    scales = 0
+    if cfg.weight_dtype == "fp8":
+        scales = ((qd + 2 * kvd) + H + 3 * I + 2 * kvd) * 4 * L + H * 4
+    tot = layer_w + fc_w + ingest_w + kv_read + kv_write + taps + scales
+    return dict(layer_weights=layer_w, fc_weights=fc_w, ingest_weights=ingest_w, kv_read=kv_read,
+                kv_write=kv_write, taps=taps, scales=scales, total=tot)
+
+
+def gateup_bytes(cfg, b: int = 16) -> int:
+    """gate|up + SwiGLU launch: both weight matrices, the normed input rows
+    and the SwiGLU output rows."""
+    wb = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight_dtype]
+    return 2 * cfg.intermediate * cfg.hidden * wb + b * cfg.hidden * 4 + b * cfg.intermediate * 4
+
+
+def cpu_baseline(cfg, ctx: int, seconds: float) -> dict:
+    """The fp64 CPU oracle on the same round: ctx_features(16) + ingest(16)
+    + forward_round(16) over a cache of ctx - 16 committed rows.  The cache is
+    prefilled directly with seeded bf16 K/V, untimed.  Rounds repeat until
+    `seconds` of CPU time have passed."""
+    from oracle import dflash_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    m = O.OracleModel(synth.make_weights(cfg))
+    base = ctx - 16
+    kv = O.OracleKV(cfg)
+    kst, vst = synth.make_prefill_kv(cfg, base)
+    kv.prefill(kst, vst)
+    taps = synth.make_taps(cfg, 16, stream=1)
+    noise = synth.make_noise(cfg)
+    pos_new = synth.positions(base, 16)
+    pos_blk = synth.positions(ctx, 16)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        feats = O.ctx_features(m, taps)
+        O.ingest_ctx(m, kv, feats, pos_new)
+        O.forward_round(m, kv, noise, pos_blk)
+        kv.truncate(base)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n / el, "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} full rounds (ctx_features 16 + ingest 16 + forward_round b=16 at ctx {ctx}, "
+                      f"cache prefilled directly to {base} rows), {el:.1f} s, numpy fp64"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-prof", action="store_true", help="skip the live per-kernel timing")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the drafter path has no "
+              f"cross-GPU work; sequences shard by data parallelism).", file=sys.stderr)
+        return 2
+
+    import torch
+    from block_diffusion_drafter_round_amd import dflash as D
+
+    cfg = synth.ROUND8_BF16
+    ctx, t, b = cfg.ctx, cfg.new_rows, cfg.block
+    base = ctx - t
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    print(f"[bench] loading {cfg.name}", file=sys.stderr, flush=True)
+    sw = synth.make_weights(cfg)
+    dr = D.Drafter(sw, device=dev, max_rows=1024)
+    cap = (ctx + b + 63) // 64 * 64
+    kv = D.KVCache(cfg, cap, dev)
+    # untimed prefill of `base` committed rows through the library itself
+    for lo in range(0, base, 1020):
+        hi = min(base, lo + 1020)
+        taps = torch.from_numpy(synth.make_taps(cfg, hi - lo, stream=1000 + lo)).to(dev)
+        dr.ingest_ctx(kv, dr.ctx_features(taps), torch.from_numpy(synth.positions(lo, hi - lo)).to(dev))
+    assert kv.len == base
+    taps = torch.from_numpy(synth.make_taps(cfg, t, stream=1)).to(dev)
+    noise = torch.from_numpy(synth.make_noise(cfg)).to(dev)
+    pos_new = torch.from_numpy(synth.positions(base, t)).to(dev)
+    pos_blk = torch.from_numpy(synth.positions(ctx, b)).to(dev)
+    feats = torch.empty((t, cfg.hidden), dtype=torch.float32, device=dev)
+    out = torch.empty((b, cfg.hidden), dtype=torch.float32, device=dev)
+    model, ws, wsb = dr.model, dr.ws, dr.ws_bytes
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        D.dflash_ctx_features(model, taps, t, feats, ws, wsb, stream)
+        D.dflash_ingest_ctx(model, kv.c, feats, pos_new, t, ws, wsb, stream)
+        D.dflash_forward_round(model, kv.c, noise, pos_blk, b, out, ws, wsb, stream)
+        kv.c.len = base
+
+    def timed(k: int) -> float:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(k):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return max(e0.elapsed_time(e1) / 1e3, 0.0), wall
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} rounds", file=sys.stderr, flush=True)
+    gpu_s, wall_s = timed(args.steps)
+    sec = max(gpu_s, wall_s)
+    ms_per_step = sec * 1e3 / args.steps
+    rounds_per_s = args.steps / sec
+    rb = round_bytes(cfg, ctx, t, b)
+    hbm_gbs = rb["total"] / (sec / args.steps) / 1e9
+
+    roofline = None
+    if not args.no_prof:
+        # live timing of the dominant kernel (gate|up + SwiGLU GEMM, 8 launches per round)
+        D.dflash_prof_start(D.K_GEMM_GATEUP, args.steps * cfg.n_layers)
+        gpu_p, wall_p = timed(args.steps)
+        tot_ms, nl = D.dflash_prof_stop()
+        avg_s = tot_ms / 1e3 / max(nl, 1)
+        gb = gateup_bytes(cfg, b)
+        ach = gb / avg_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "gemm gate|up + SwiGLU (M=16, N=2x6144, K=2048, bf16)",
+                    "bytes_per_launch": gb, "avg_launch_us": round(avg_s * 1e6, 2), "launches": nl,
+                    "ms_per_step_while_timed": round(max(gpu_p, wall_p) * 1e3 / args.steps, 4)}
+
+    cpu = None
+    if not args.no_cpu:
+        print(f"[bench] cpu oracle baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, ctx, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC, "value": round(rounds_per_s, 2), "unit": "rounds/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) taps/noise, random init)",
+        "config": {"workload": "8-layer drafter cached round: ctx_features 16 + ingest_ctx 16 + forward_round "
+                               "b=16 over a ctx-4096 bf16 KV cache (4112 keys)",
+                   "layers": cfg.n_layers, "hidden": cfg.hidden, "heads": f"{cfg.n_q_heads}:{cfg.n_kv_heads}",
+                   "head_dim": cfg.head_dim, "intermediate": cfg.intermediate, "taps": cfg.n_taps,
+                   "ctx": ctx, "block": b, "weights": "bf16", "kv": "bf16"},
+        "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "round_bytes": rb["total"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -4,14 +4,17 @@
 // Pages: [DflashDraft] (docs.rs memra_engine::dflash::DflashDraft) sections
 // "ctx_features", "forward", "ingest_ctx", "forward_round", "rope_yarn";
 // [memra dflash module] "DflashKv"; [atlas dflash_head] "DflashScratch".
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <mutex>
 #include <vector>
 
 #include "dflash.h"
+#include "dflash_prof.h"
 #include "kernels.h"
 
 struct dflash_model {
@@ -39,6 +42,29 @@ int fail(int code, const char *fmt, ...) {
 int hip_fail(hipError_t e, const char *where) {
     return fail(DFLASH_E_HIP, "%s: %s", where, hipGetErrorString(e));
 }
+
+// ---- measurement hook: HIP events around the launches of one kernel class ----
+struct Prof {
+    std::mutex mu;
+    std::atomic<int> cls{0};
+    std::vector<hipEvent_t> ev;   // start, stop pairs
+    int used = 0, cap = 0;
+} g_prof;
+
+struct ProfScope {
+    int idx = -1;
+    hipStream_t s;
+    ProfScope(int cls, hipStream_t st) : s(st) {
+        if (g_prof.cls.load(std::memory_order_relaxed) != cls) return;
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        if (g_prof.cls.load() != cls || g_prof.used >= g_prof.cap) return;
+        idx = g_prof.used++;
+        hipEventRecord(g_prof.ev[2 * idx], s);
+    }
+    ~ProfScope() {
+        if (idx >= 0) hipEventRecord(g_prof.ev[2 * idx + 1], s);
+    }
+};
 
 bool aligned(const void *p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -183,8 +209,13 @@ hipError_t run_ctx_features(const dflash_model *m, const float *taps, int t, flo
     g.A = taps; g.lda = c.n_taps * c.hidden; g.M = t; g.K = c.n_taps * c.hidden;
     g.seg[0] = seg(m->w.fc, c.hidden); g.nseg = 1;
     g.Y = feats; g.ldy = c.hidden; g.epi = dfl::EPI_STORE; g.wtype = wtype(c);
-    hipError_t e = dfl::gemm(g, at<float>(ws, L.gpart), at<unsigned>(ws, L.gcnt), s);
+    hipError_t e;
+    {
+        ProfScope p(DFLASH_K_GEMM_FC, s);
+        e = dfl::gemm(g, at<float>(ws, L.gpart), at<unsigned>(ws, L.gcnt), s);
+    }
     if (e != hipSuccess) return e;
+    ProfScope p(DFLASH_K_NORM, s);
     return dfl::rmsnorm(feats, c.hidden, m->w.g_hidden_norm, feats, c.hidden, nullptr, t, c.hidden, c.rms_eps, s);
 }
 
@@ -199,7 +230,11 @@ hipError_t run_ingest(const dflash_model *m, dflash_kv *kv, const float *feats, 
         g.A = feats; g.lda = c.hidden; g.M = t; g.K = c.hidden;
         g.seg[0] = seg(W.wk, kvd); g.seg[1] = seg(W.wv, kvd); g.nseg = 2;
         g.Y = kvbuf; g.ldy = 2 * kvd; g.epi = dfl::EPI_STORE; g.wtype = wtype(c);
-        hipError_t e = dfl::gemm(g, at<float>(ws, L.gpart), at<unsigned>(ws, L.gcnt), s);
+        hipError_t e;
+        {
+            ProfScope p(DFLASH_K_GEMM_KV, s);
+            e = dfl::gemm(g, at<float>(ws, L.gpart), at<unsigned>(ws, L.gcnt), s);
+        }
         if (e != hipSuccess) return e;
         dfl::RopeArgs r{};
         r.src = kvbuf; r.ld = 2 * kvd; r.q_off = -1; r.k_off = 0; r.v_off = kvd;
@@ -208,7 +243,10 @@ hipError_t run_ingest(const dflash_model *m, dflash_kv *kv, const float *feats, 
         r.q_out = nullptr; r.kc = layer_ptr(kv->k, c, kv->capacity, l); r.vc = layer_ptr(kv->v, c, kv->capacity, l);
         r.cap = kv->capacity; r.row0 = kv->len; r.kv_f32 = c.kv_dtype == DFLASH_F32;
         memcpy(r.inv_freq, m->inv_freq, sizeof r.inv_freq);
-        e = dfl::qk_norm_rope(r, s);
+        {
+            ProfScope p(DFLASH_K_ROPE, s);
+            e = dfl::qk_norm_rope(r, s);
+        }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -224,20 +262,30 @@ hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *no
     unsigned *gc = at<unsigned>(ws, L.gcnt);
     const int wt = wtype(c);
     hipError_t e;
-    if (c.n_layers == 0) return dfl::rmsnorm(noise, H, m->w.g_norm, out, H, nullptr, b, H, c.rms_eps, s);
+    if (c.n_layers == 0) {
+        ProfScope p(DFLASH_K_NORM, s);
+        return dfl::rmsnorm(noise, H, m->w.g_norm, out, H, nullptr, b, H, c.rms_eps, s);
+    }
 
     for (int l = 0; l < c.n_layers; ++l) {
         const dflash_layer_weights &W = m->layers[l];
         // input norm (layer 0 also copies the block embeddings into the residual stream)
-        e = l == 0 ? dfl::rmsnorm(noise, H, W.g_in, XN, H, X, b, H, c.rms_eps, s)
-                   : dfl::rmsnorm(X, H, W.g_in, XN, H, nullptr, b, H, c.rms_eps, s);
+        {
+            ProfScope p(DFLASH_K_NORM, s);
+            e = l == 0 ? dfl::rmsnorm(noise, H, W.g_in, XN, H, X, b, H, c.rms_eps, s)
+                       : dfl::rmsnorm(X, H, W.g_in, XN, H, nullptr, b, H, c.rms_eps, s);
+        }
         if (e != hipSuccess) return e;
         // q | k | v projections of the block rows
         dfl::GemmArgs g{};
         g.A = XN; g.lda = H; g.M = b; g.K = H;
         g.seg[0] = seg(W.wq, qd); g.seg[1] = seg(W.wk, kvd); g.seg[2] = seg(W.wv, kvd); g.nseg = 3;
         g.Y = QKV; g.ldy = qd + 2 * kvd; g.epi = dfl::EPI_STORE; g.wtype = wt;
-        if ((e = dfl::gemm(g, gp, gc, s)) != hipSuccess) return e;
+        {
+            ProfScope p(DFLASH_K_GEMM_QKV, s);
+            e = dfl::gemm(g, gp, gc, s);
+        }
+        if (e != hipSuccess) return e;
         // q/k head norm + rope; block K/V into cache rows [len, len + b)
         dfl::RopeArgs r{};
         r.src = QKV; r.ld = qd + 2 * kvd; r.q_off = 0; r.k_off = qd; r.v_off = qd + kvd;
@@ -246,7 +294,11 @@ hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *no
         r.q_out = Q; r.kc = layer_ptr(kv->k, c, kv->capacity, l); r.vc = layer_ptr(kv->v, c, kv->capacity, l);
         r.cap = kv->capacity; r.row0 = kv->len; r.kv_f32 = c.kv_dtype == DFLASH_F32;
         memcpy(r.inv_freq, m->inv_freq, sizeof r.inv_freq);
-        if ((e = dfl::qk_norm_rope(r, s)) != hipSuccess) return e;
+        {
+            ProfScope p(DFLASH_K_ROPE, s);
+            e = dfl::qk_norm_rope(r, s);
+        }
+        if (e != hipSuccess) return e;
         // attention over all len + b keys
         dfl::AttnArgs a{};
         a.q = Q; a.kc = r.kc; a.vc = r.vc; a.cap = kv->capacity; a.n_keys = kv->len + b;
@@ -254,23 +306,44 @@ hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *no
         a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
         dfl::attn_plan(a, MAX_ATTN_SPLITS);
         a.part_o = at<float>(ws, L.part_o); a.part_ml = at<float>(ws, L.part_ml); a.out = O;
-        if ((e = dfl::attention(a, s)) != hipSuccess) return e;
+        {
+            ProfScope p(DFLASH_K_ATTN, s);
+            e = dfl::attention(a, s);
+        }
+        if (e != hipSuccess) return e;
         // o_proj + residual
         g = dfl::GemmArgs{};
         g.A = O; g.lda = qd; g.M = b; g.K = qd; g.seg[0] = seg(W.wo, H); g.nseg = 1;
         g.Y = X; g.ldy = H; g.epi = dfl::EPI_ADD; g.wtype = wt;
-        if ((e = dfl::gemm(g, gp, gc, s)) != hipSuccess) return e;
+        {
+            ProfScope p(DFLASH_K_GEMM_O, s);
+            e = dfl::gemm(g, gp, gc, s);
+        }
+        if (e != hipSuccess) return e;
         // post-attention norm, gate|up + SwiGLU, down + residual
-        if ((e = dfl::rmsnorm(X, H, W.g_post, XN, H, nullptr, b, H, c.rms_eps, s)) != hipSuccess) return e;
+        {
+            ProfScope p(DFLASH_K_NORM, s);
+            e = dfl::rmsnorm(X, H, W.g_post, XN, H, nullptr, b, H, c.rms_eps, s);
+        }
+        if (e != hipSuccess) return e;
         g = dfl::GemmArgs{};
         g.A = XN; g.lda = H; g.M = b; g.K = H; g.seg[0] = seg(W.wg, I); g.seg[1] = seg(W.wu, I); g.nseg = 2;
         g.Y = Z; g.ldy = I; g.epi = dfl::EPI_SWIGLU; g.wtype = wt;
-        if ((e = dfl::gemm(g, gp, gc, s)) != hipSuccess) return e;
+        {
+            ProfScope p(DFLASH_K_GEMM_GATEUP, s);
+            e = dfl::gemm(g, gp, gc, s);
+        }
+        if (e != hipSuccess) return e;
         g = dfl::GemmArgs{};
         g.A = Z; g.lda = I; g.M = b; g.K = I; g.seg[0] = seg(W.wd, H); g.nseg = 1;
         g.Y = X; g.ldy = H; g.epi = dfl::EPI_ADD; g.wtype = wt;
-        if ((e = dfl::gemm(g, gp, gc, s)) != hipSuccess) return e;
+        {
+            ProfScope p(DFLASH_K_GEMM_DOWN, s);
+            e = dfl::gemm(g, gp, gc, s);
+        }
+        if (e != hipSuccess) return e;
     }
+    ProfScope p(DFLASH_K_NORM, s);
     return dfl::rmsnorm(X, H, m->w.g_norm, out, H, nullptr, b, H, c.rms_eps, s);
 }
 
@@ -400,6 +473,43 @@ int dflash_forward_full(const dflash_model *m, const float *taps, const float *n
     if (e == hipSuccess) e = run_round(m, &kv, noise_emb, pos + n, b, out, ws, L, s);
     if (e != hipSuccess) return hip_fail(e, "forward_full");
     scratch->len = n;
+    return DFLASH_OK;
+}
+
+int dflash_prof_start(int32_t kernel_class, int32_t max_launches) {
+    g_err.clear();
+    if (kernel_class < DFLASH_K_GEMM_FC || kernel_class > DFLASH_K_NORM || max_launches <= 0 || max_launches > (1 << 20))
+        return fail(DFLASH_E_INVAL, "bad kernel class %d or launch count %d", kernel_class, max_launches);
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    while ((int)g_prof.ev.size() < 2 * max_launches) {
+        hipEvent_t e;
+        hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) return hip_fail(r, "prof_start");
+        g_prof.ev.push_back(e);
+    }
+    g_prof.cap = max_launches;
+    g_prof.used = 0;
+    g_prof.cls.store(kernel_class);
+    return DFLASH_OK;
+}
+
+int dflash_prof_stop(double *total_ms, int32_t *launches) {
+    g_err.clear();
+    if (!total_ms || !launches) return fail(DFLASH_E_INVAL, "null argument");
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    g_prof.cls.store(0);
+    double tot = 0.0;
+    for (int i = 0; i < g_prof.used; ++i) {
+        hipError_t r = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+        if (r != hipSuccess) return hip_fail(r, "prof_stop");
+        float ms = 0.f;
+        r = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+        if (r != hipSuccess) return hip_fail(r, "prof_stop");
+        tot += ms;
+    }
+    *total_ms = tot;
+    *launches = g_prof.used;
+    g_prof.used = 0;
     return DFLASH_OK;
 }
 

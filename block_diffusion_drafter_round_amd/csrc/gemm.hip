@@ -5,118 +5,134 @@
 // W: f32, bf16 or fp8 e4m3fn weights in torch Linear layout [N, K], streamed
 //    from HBM once per call.  This stream is the dominant cost of a round.
 //
-// Work item = (group of MT 16-row tiles, one 16-column tile, one K split).
-// A workgroup of 4 waves takes one item.  The waves interleave over K chunks,
-// so at any moment the workgroup reads 16 weight rows x 4 adjacent chunks.
-// Each lane issues one 16-byte load per chunk and weight row:
-//   bf16: 8 values (K chunk 32), one MFMA 16x16x32 each on the hi and lo
-//         bf16 halves of the activations;
-//   fp8 : 16 codes (K chunk 64), decoded exactly to bf16, 4 MFMAs;
-//   f32 : 4 values (K chunk 16), 4 MFMAs 16x16x4 f32.
-// The 4 wave accumulators are summed in LDS in a fixed order.  With a K
-// split, each workgroup writes its partial tile.  The last workgroup of a
-// tile to finish (an atomic counter) sums the partials in split order and
-// applies the epilogue, so results do not depend on scheduling.
+// Work item = (MT 16-row tiles) x (64 output columns) x (one K split).
+// * A workgroup of 4 waves takes one item.  Wave w owns the 16 columns
+//   [16w, 16w + 16) of the group (with SwiGLU, also the matching 16 up
+//   columns).
+// * Per K chunk, every wave first issues all of its weight loads.  Each lane
+//   loads one 16-byte piece per step and weight row: bf16 8 values (K step
+//   32), fp8 16 codes (K step 64), f32 4 values (K step 16).
+// * Meanwhile the workgroup stages the activation chunk in LDS once, in MFMA
+//   fragment order.  bf16/fp8 weights use the activations split into bf16
+//   hi + lo parts (two MFMAs 16x16x32 per step, ~16-bit activation
+//   precision).  f32 weights use MFMA 16x16x4 f32 on the f32 values.
+// * The MFMAs then read A from LDS (one 16-byte read per fragment) and W
+//   from registers.
+// * Split-K: each workgroup stores its partial tiles with device-coherent
+//   stores, then bumps a per-column-group counter.  The last workgroup to
+//   arrive sums the partials in split order and applies the epilogue.  The
+//   result is therefore independent of scheduling.  Only workgroup-scope
+//   fences are used (no L2 writeback / invalidate).
 #include "common.h"
 #include "kernels.h"
 
 namespace dfl {
 
 template <int WT> struct WCfg;
-template <> struct WCfg<WT_BF16> { static constexpr int KC = 32, E = 8,  ES = 2; };
-template <> struct WCfg<WT_FP8>  { static constexpr int KC = 64, E = 16, ES = 1; };
-template <> struct WCfg<WT_F32>  { static constexpr int KC = 16, E = 4,  ES = 4; };
+// KS: K per 16-byte weight load; FR: 16-byte A fragments per step and m-tile
+template <> struct WCfg<WT_BF16> { static constexpr int KS = 32, ES = 2, FR = 2; };
+template <> struct WCfg<WT_FP8>  { static constexpr int KS = 64, ES = 1, FR = 4; };
+template <> struct WCfg<WT_F32>  { static constexpr int KS = 16, ES = 4, FR = 1; };
 
-// One K chunk of one 16x16 tile: acc += A_frag . W_frag.
-template <int WT>
-__device__ __forceinline__ void mac_chunk(f32x4 &acc, const u32x4 &wv, const float *a, bool valid) {
-    if constexpr (WT == WT_BF16) {
+__device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
+
+__device__ __forceinline__ void st_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Stage A[m0 .. m0+16*MT)[k0 .. k0 + NSTEP*KS) into LDS fragments.
+// Layout: lds[((mt * NSTEP + s) * FR + f) * 64 + lane] (16 bytes each).
+template <int WT, int MT, int NSTEP>
+__device__ __forceinline__ void stage_a(u32x4 *lds, const GemmArgs &p, int m0, int k0, int kvalid) {
+    constexpr int KS = WCfg<WT>::KS;
+    constexpr int GROUPS = NSTEP * KS / 8;          // 8-float groups per row
+    constexpr int TOTAL = MT * 16 * GROUPS;
+    for (int idx = threadIdx.x; idx < TOTAL; idx += 256) {
+        const int rowl = idx / GROUPS, j = idx - rowl * GROUPS;   // row in item, 8-float group
+        const int row = m0 + rowl;
         float x[8];
-        if (valid) {
-            float4 p = ld_f4(a), q = ld_f4(a + 4);
-            x[0] = p.x; x[1] = p.y; x[2] = p.z; x[3] = p.w; x[4] = q.x; x[5] = q.y; x[6] = q.z; x[7] = q.w;
+        if (row < p.M && 8 * j < kvalid) {
+            const float *src = p.A + (size_t)row * p.lda + k0 + 8 * j;
+            float4 a = ld_f4(src), b = ld_f4(src + 4);
+            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = 0.f;
         }
-        bf16x8 hi, lo;
-        split_bf16x8(x, hi, lo);
-        bf16x8 b = __builtin_bit_cast(bf16x8, wv);
-        acc = mfma_bf16(hi, b, acc);
-        acc = mfma_bf16(lo, b, acc);
-    } else if constexpr (WT == WT_FP8) {
-        bf16x8 b0 = fp8x8_to_bf16x8(wv.x, wv.y);
-        bf16x8 b1 = fp8x8_to_bf16x8(wv.z, wv.w);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float x[8];
-            if (valid) {
-                float4 p = ld_f4(a + 8 * h), q = ld_f4(a + 8 * h + 4);
-                x[0] = p.x; x[1] = p.y; x[2] = p.z; x[3] = p.w; x[4] = q.x; x[5] = q.y; x[6] = q.z; x[7] = q.w;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) x[i] = 0.f;
-            }
+        const int mt = rowl >> 4, r16 = rowl & 15;
+        if constexpr (WT == WT_F32) {
+            // step s covers 16 K: lane group g holds K 4g..4g+3 -> two fragments per 8 floats
+            const int s = j >> 1, g0 = (j & 1) * 2;
+            u32x4 f0 = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+            u32x4 f1 = {__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])};
+            lds[(mt * NSTEP + s) * 64 + g0 * 16 + r16] = f0;
+            lds[(mt * NSTEP + s) * 64 + (g0 + 1) * 16 + r16] = f1;
+        } else {
             bf16x8 hi, lo;
             split_bf16x8(x, hi, lo);
-            acc = mfma_bf16(hi, h ? b1 : b0, acc);
-            acc = mfma_bf16(lo, h ? b1 : b0, acc);
+            int s, f, g;
+            if constexpr (WT == WT_BF16) { s = j >> 2; g = j & 3; f = 0; }
+            else { s = j >> 3; const int jj = j & 7; g = jj >> 1; f = (jj & 1) * 2; }  // fp8: lane group g holds 16 K
+            const int lane = g * 16 + r16;
+            lds[((mt * NSTEP + s) * WCfg<WT>::FR + f) * 64 + lane] = __builtin_bit_cast(u32x4, hi);
+            lds[((mt * NSTEP + s) * WCfg<WT>::FR + f + 1) * 64 + lane] = __builtin_bit_cast(u32x4, lo);
         }
-    } else {
-        float4 p = valid ? ld_f4(a) : make_float4(0.f, 0.f, 0.f, 0.f);
-        float4 w = __builtin_bit_cast(float4, wv);
-        acc = mfma_f32(p.x, w.x, acc);
-        acc = mfma_f32(p.y, w.y, acc);
-        acc = mfma_f32(p.z, w.z, acc);
-        acc = mfma_f32(p.w, w.w, acc);
     }
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
+template <int WT>
+__device__ __forceinline__ void mac_step(f32x4 &acc, const u32x4 &wv, const u32x4 *af) {
+    if constexpr (WT == WT_BF16) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, wv);
+        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[0]), b, acc);
+        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[64]), b, acc);
+    } else if constexpr (WT == WT_FP8) {
+        const bf16x8 b0 = fp8x8_to_bf16x8(wv.x, wv.y), b1 = fp8x8_to_bf16x8(wv.z, wv.w);
+        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[0]), b0, acc);
+        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[64]), b0, acc);
+        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[128]), b1, acc);
+        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[192]), b1, acc);
+    } else {
+        const u32x4 a = af[0];
+        acc = mfma_f32(__uint_as_float(a.x), __uint_as_float(wv.x), acc);
+        acc = mfma_f32(__uint_as_float(a.y), __uint_as_float(wv.y), acc);
+        acc = mfma_f32(__uint_as_float(a.z), __uint_as_float(wv.z), acc);
+        acc = mfma_f32(__uint_as_float(a.w), __uint_as_float(wv.w), acc);
+    }
+}
 
-template <int WT, int MT, int EPI, int U>
+template <int WT, int MT, int EPI, int NSTEP>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
-    constexpr int KC = WCfg<WT>::KC, E = WCfg<WT>::E, ES = WCfg<WT>::ES;
+    constexpr int KS = WCfg<WT>::KS, ES = WCfg<WT>::ES, FR = WCfg<WT>::FR;
     constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
-    constexpr int NT = MT * NACC;  // 16x16 tiles per workgroup
+    constexpr int KCH = NSTEP * KS;                      // K per staged chunk
+    __shared__ u32x4 lds[MT * NSTEP * FR * 64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r16 = lane & 15;
-    const int ntile = blockIdx.x / p.ksplit, split = blockIdx.x - ntile * p.ksplit;
+    const int group = blockIdx.x / p.ksplit, split = blockIdx.x - group * p.ksplit;
     const int mgroup = blockIdx.y;
-    const int n0 = ntile * 16;
     const int m0 = mgroup * MT * 16;
+    const int n0 = group * 64 + wave * 16;               // this wave's first output column
 
-    // weight segment(s) of this column tile
+    // weight segment of this column group (groups never straddle segments)
     const char *wbase[NACC];
     const float *wscale[NACC];
-    int ncol0 = n0;  // column within the segment
+    int ncol = n0;                                       // column inside the segment
     if constexpr (EPI == EPI_SWIGLU) {
         wbase[0] = (const char *)p.seg[0].w; wscale[0] = p.seg[0].scale;
         wbase[1] = (const char *)p.seg[1].w; wscale[1] = p.seg[1].scale;
     } else {
         int s = 0;
-        while (s + 1 < p.nseg && ncol0 >= p.seg[s].n) { ncol0 -= p.seg[s].n; ++s; }
+        while (s + 1 < p.nseg && ncol >= p.seg[s].n) { ncol -= p.seg[s].n; ++s; }
         wbase[0] = (const char *)p.seg[s].w; wscale[0] = p.seg[s].scale;
     }
-
-    const int K = p.K;
+    const size_t K = p.K;
     const int kbeg = split * p.kchunk;
-    const int klen = min(p.kchunk, K - kbeg);
-    const int nch = klen / KC;
-
-    const char *wrow[NACC];
-#pragma unroll
-    for (int a = 0; a < NACC; ++a)
-        wrow[a] = wbase[a] + ((size_t)(ncol0 + r16) * K + kbeg + g * E) * ES;
-    const float *arow[MT];
-    bool avalid[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        int row = m0 + mt * 16 + r16;
-        avalid[mt] = row < p.M;
-        arow[mt] = p.A + (size_t)(avalid[mt] ? row : 0) * p.lda + kbeg + g * E;
-    }
+    const int kend = min(kbeg + p.kchunk, p.K);
 
     f32x4 acc[MT][NACC];
 #pragma unroll
@@ -124,142 +140,152 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int a = 0; a < NACC; ++a) acc[mt][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int c0 = wave; c0 < nch; c0 += 4 * U) {
-        u32x4 wv[U][NACC];
+    const int lane_koff = g * (KS / 4);                  // this lane's K offset inside a step
+    for (int k0 = kbeg; k0 < kend; k0 += KCH) {
+        const int kvalid = min(KCH, kend - k0);          // a multiple of KS
+        const int nst = kvalid / KS;
+        // 1. all weight loads of this chunk
+        u32x4 wv[NSTEP][NACC];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = c0 + 4 * u;
-            if (c < nch) {
+        for (int a = 0; a < NACC; ++a) {
+            const char *wr = wbase[a] + ((size_t)(ncol + r16) * K + k0 + lane_koff) * ES;
 #pragma unroll
-                for (int a = 0; a < NACC; ++a) wv[u][a] = ld_stream16(wrow[a] + (size_t)c * KC * ES);
-            }
+            for (int s = 0; s < NSTEP; ++s)
+                if (s < nst) wv[s][a] = ld_stream16(wr + (size_t)s * KS * ES);
         }
+        // 2. activations -> LDS fragments
+        if (k0 != kbeg) __syncthreads();
+        stage_a<WT, MT, NSTEP>(lds, p, m0, k0, kvalid);
+        __syncthreads();
+        // 3. MFMAs
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = c0 + 4 * u;
-            if (c < nch) {
+        for (int s = 0; s < NSTEP; ++s)
+            if (s < nst)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt) {
+                const u32x4 *af = lds + ((mt * NSTEP + s) * FR) * 64 + lane;
 #pragma unroll
-                    for (int a = 0; a < NACC; ++a)
-                        mac_chunk<WT>(acc[mt][a], wv[u][a], arow[mt] + (size_t)c * KC, avalid[mt]);
+                for (int a = 0; a < NACC; ++a) mac_step<WT>(acc[mt][a], wv[s][a], af);
             }
-        }
     }
 
-    // ---- sum the 4 waves' tiles in LDS (fixed order) ----
-    __shared__ float red[4][NT][256];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int a = 0; a < NACC; ++a)
-            *reinterpret_cast<f32x4 *>(&red[wave][mt * NACC + a][lane * 4]) = acc[mt][a];
-    __syncthreads();
-    float v[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) v[t] = ((red[0][t][tid] + red[1][t][tid]) + red[2][t][tid]) + red[3][t][tid];
-
-    // ---- split-K: the last workgroup of the tile reduces in split order ----
+    // ---- split-K: the last workgroup of the column group reduces in split order ----
+    // partial layout per (item, split): [mt][a][wave][256]
+    constexpr int PER = MT * NACC * 4 * 256;
     if (p.ksplit > 1) {
-        const int tile_id = mgroup * p.ntiles + ntile;
-        float *part = p.part + (size_t)tile_id * p.ksplit * (NT * 256);
+        const int item = mgroup * p.ngroups + group;
+        float *part = p.part + (size_t)item * p.ksplit * PER;
+        float *mine = part + (size_t)split * PER;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            __hip_atomic_store(part + (size_t)split * (NT * 256) + t * 256 + tid, v[t], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        __threadfence();
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int a = 0; a < NACC; ++a)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    st_coherent(mine + ((mt * NACC + a) * 4 + wave) * 256 + lane * 4 + j, acc[mt][a][j]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // wait for the stores
         __syncthreads();
         __shared__ int is_last;
         if (tid == 0) {
-            unsigned prev = __hip_atomic_fetch_add(p.cnt + tile_id, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            unsigned prev = __hip_atomic_fetch_add(p.cnt + item, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             is_last = (prev == (unsigned)(p.ksplit - 1));
         }
         __syncthreads();
         if (!is_last) return;
-        __threadfence();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 #pragma unroll
-        for (int t = 0; t < NT; ++t) v[t] = 0.f;
-        for (int s = 0; s < p.ksplit; ++s)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                v[t] += __hip_atomic_load(part + (size_t)s * (NT * 256) + t * 256 + tid, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-        if (tid == 0) __hip_atomic_store(p.cnt + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int a = 0; a < NACC; ++a) {
+                f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s < p.ksplit; ++s) {
+                    const float *q = part + (size_t)s * PER + ((mt * NACC + a) * 4 + wave) * 256 + lane * 4;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] += ld_coherent(q + j);
+                }
+                acc[mt][a] = v;
+            }
+        if (tid == 0) __hip_atomic_store(p.cnt + item, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // ---- epilogue: element tid of each 16x16 tile ----
-    const int el = tid >> 2, j = tid & 3;
-    const int row_in = 4 * (el >> 4) + j, col = el & 15;
-    const int ccol = ncol0 + col;  // column inside the segment (for scales)
+    // ---- epilogue: lane holds rows 4g + j, column r16 of each 16x16 tile ----
+    const int col = n0 + r16, ccol = ncol + r16;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int row = m0 + mt * 16 + row_in;
-        if (row >= p.M) continue;
-        float *y = p.Y + (size_t)row * p.ldy + n0 + col;
-        if constexpr (EPI == EPI_SWIGLU) {
-            float gv = v[mt * 2 + 0], uv = v[mt * 2 + 1];
-            if constexpr (WT == WT_FP8) { gv *= wscale[0][ccol]; uv *= wscale[1][ccol]; }
-            *y = silu(gv) * uv;
-        } else {
-            float r = v[mt];
-            if constexpr (WT == WT_FP8) r *= wscale[0][ccol];
-            if constexpr (EPI == EPI_ADD) *y += r;
-            else *y = r;
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = m0 + mt * 16 + 4 * g + j;
+            if (row >= p.M) continue;
+            float *y = p.Y + (size_t)row * p.ldy + col;
+            if constexpr (EPI == EPI_SWIGLU) {
+                float gv = acc[mt][0][j], uv = acc[mt][1][j];
+                if constexpr (WT == WT_FP8) { gv *= wscale[0][ccol]; uv *= wscale[1][ccol]; }
+                *y = silu(gv) * uv;
+            } else {
+                float r = acc[mt][0][j];
+                if constexpr (WT == WT_FP8) r *= wscale[0][ccol];
+                if constexpr (EPI == EPI_ADD) *y += r;
+                else *y = r;
+            }
         }
-    }
 }
 
 // ---------------------------------------------------------------------------
-// host side: plan the split and launch
+// host side: plan and launch
 // ---------------------------------------------------------------------------
-static int kc_of(int wt) { return wt == WT_BF16 ? 32 : wt == WT_FP8 ? 64 : 16; }
+static int ks_of(int wt) { return wt == WT_BF16 ? 32 : wt == WT_FP8 ? 64 : 16; }
+
+// steps per staged chunk for a given instantiation
+static int nstep_of(int wt, int mt, int epi) {
+    if (mt > 1) return wt == WT_FP8 ? 2 : 4;
+    if (wt == WT_FP8) return epi == EPI_SWIGLU ? 4 : 8;
+    return epi == EPI_SWIGLU ? 8 : 16;
+}
 
 int gemm_plan(GemmArgs &a) {
     const int nacc = a.epi == EPI_SWIGLU ? 2 : 1;
     int ncols = 0;
     if (a.epi == EPI_SWIGLU) ncols = a.seg[0].n;
     else for (int s = 0; s < a.nseg; ++s) ncols += a.seg[s].n;
-    a.ntiles = ncols / 16;
+    a.ngroups = ncols / 64;
     a.mt = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 4;
     a.mgroups = (a.M + 16 * a.mt - 1) / (16 * a.mt);
-    const int kstep = 4 * kc_of(a.wtype);        // 4 waves x one chunk
-    const int base = a.ntiles * a.mgroups;
+    const int kch = nstep_of(a.wtype, a.mt, a.epi) * ks_of(a.wtype);
+    const int nchunks = (a.K + kch - 1) / kch;
+    const int base = a.ngroups * a.mgroups;
+    // split K until there are ~2 workgroups per CU, one or more chunks per split
     int ksplit = 1;
-    const int target = 1024;                     // ~4 workgroups per CU
+    const int target = 512;
     if (base < target) ksplit = (target + base - 1) / base;
-    int maxsplit = a.K / kstep;
-    if (ksplit > maxsplit) ksplit = maxsplit;
-    if (ksplit < 1) ksplit = 1;
-    // partial storage bound
-    const size_t per = (size_t)a.mt * nacc * 256;
+    if (ksplit > nchunks) ksplit = nchunks;
+    const size_t per = (size_t)a.mt * nacc * 4 * 256;
     while (ksplit > 1 && (size_t)base * ksplit * per > GEMM_PART_FLOATS) --ksplit;
     if (ksplit > 1 && base > GEMM_MAX_COUNTERS) ksplit = 1;
-    int kchunk = (a.K + ksplit - 1) / ksplit;
-    kchunk = (kchunk + kstep - 1) / kstep * kstep;
-    ksplit = (a.K + kchunk - 1) / kchunk;
-    a.ksplit = ksplit;
-    a.kchunk = kchunk;
-    return base * ksplit;
+    const int chunks_per = (nchunks + ksplit - 1) / ksplit;
+    a.kchunk = chunks_per * kch;
+    a.ksplit = (a.K + a.kchunk - 1) / a.kchunk;
+    return base * a.ksplit;
 }
 
 template <int WT, int EPI>
-static hipError_t launch_wt_epi(GemmArgs &a, hipStream_t s) {
-    dim3 grid(a.ntiles * a.ksplit, a.mgroups), block(256);
-    constexpr int U = WT == WT_F32 ? 4 : 8;
+static void launch_wt_epi(const GemmArgs &a, hipStream_t s) {
+    dim3 grid(a.ngroups * a.ksplit, a.mgroups), block(256);
+    constexpr bool SW = EPI == EPI_SWIGLU;
+    constexpr int N1 = WT == WT_FP8 ? (SW ? 4 : 8) : (SW ? 8 : 16);
+    constexpr int N4 = WT == WT_FP8 ? 2 : 4;
     switch (a.mt) {
-        case 1: hipLaunchKernelGGL((gemm_kernel<WT, 1, EPI, U>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((gemm_kernel<WT, 2, EPI, U>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((gemm_kernel<WT, 4, EPI, (U > 4 ? 4 : U)>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((gemm_kernel<WT, 1, EPI, N1>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((gemm_kernel<WT, 2, EPI, N4>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((gemm_kernel<WT, 4, EPI, N4>), grid, block, 0, s, a); break;
     }
-    return hipGetLastError();
 }
 
 template <int WT>
-static hipError_t launch_wt(GemmArgs &a, hipStream_t s) {
+static void launch_wt(const GemmArgs &a, hipStream_t s) {
     switch (a.epi) {
-        case EPI_STORE: return launch_wt_epi<WT, EPI_STORE>(a, s);
-        case EPI_ADD: return launch_wt_epi<WT, EPI_ADD>(a, s);
-        default: return launch_wt_epi<WT, EPI_SWIGLU>(a, s);
+        case EPI_STORE: launch_wt_epi<WT, EPI_STORE>(a, s); break;
+        case EPI_ADD: launch_wt_epi<WT, EPI_ADD>(a, s); break;
+        default: launch_wt_epi<WT, EPI_SWIGLU>(a, s); break;
     }
 }
 
@@ -269,10 +295,11 @@ hipError_t gemm(GemmArgs a, float *part, unsigned *cnt, hipStream_t s) {
     a.part = part;
     a.cnt = cnt;
     switch (a.wtype) {
-        case WT_BF16: return launch_wt<WT_BF16>(a, s);
-        case WT_FP8: return launch_wt<WT_FP8>(a, s);
-        default: return launch_wt<WT_F32>(a, s);
+        case WT_BF16: launch_wt<WT_BF16>(a, s); break;
+        case WT_FP8: launch_wt<WT_FP8>(a, s); break;
+        default: launch_wt<WT_F32>(a, s); break;
     }
+    return hipGetLastError();
 }
 
 }  // namespace dfl

@@ -23,7 +23,7 @@ struct GemmArgs {
     int epi;
     int wtype;
     // filled by the launcher
-    int ksplit, kchunk, mt, ntiles, mgroups;
+    int ksplit, kchunk, mt, ngroups, mgroups;   // ngroups: 64-column groups
     float *part; unsigned *cnt;
 };
 

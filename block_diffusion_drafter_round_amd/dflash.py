@@ -60,7 +60,10 @@ class dflash_kv(C.Structure):
 _lib = None
 EXPORTS = ("dflash_load_weights", "dflash_free", "dflash_workspace_bytes", "dflash_ctx_features",
            "dflash_ingest_ctx", "dflash_forward_round", "dflash_forward_full", "dflash_last_error",
-           "dflash_rope_table")
+           "dflash_rope_table", "dflash_prof_start", "dflash_prof_stop")
+
+# kernel classes of the measurement hook (include/dflash_prof.h)
+K_GEMM_FC, K_GEMM_KV, K_GEMM_QKV, K_GEMM_O, K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN, K_ROPE, K_NORM = range(1, 10)
 
 
 def lib():
@@ -83,6 +86,8 @@ def lib():
     L.dflash_forward_full.argtypes = [vp, vp, vp, vp, i32, i32, vp, C.POINTER(dflash_kv), vp, sz, vp]
     L.dflash_last_error.restype = C.c_char_p
     L.dflash_rope_table.argtypes = [vp, C.POINTER(C.c_double), i32, C.POINTER(C.c_double)]
+    L.dflash_prof_start.argtypes = [i32, i32]
+    L.dflash_prof_stop.argtypes = [C.POINTER(C.c_double), C.POINTER(i32)]
     for name in EXPORTS:
         if name not in ("dflash_free", "dflash_workspace_bytes", "dflash_last_error"):
             getattr(L, name).restype = C.c_int
@@ -158,6 +163,18 @@ def dflash_rope_table(model, half: int):
     ms = C.c_double()
     _check(lib().dflash_rope_table(model, buf, half, C.byref(ms)))
     return list(buf), ms.value
+
+
+def dflash_prof_start(kernel_class: int, max_launches: int) -> None:
+    _check(lib().dflash_prof_start(kernel_class, max_launches))
+
+
+def dflash_prof_stop():
+    """-> (total_ms, launches)"""
+    ms = C.c_double()
+    n = C.c_int32()
+    _check(lib().dflash_prof_stop(C.byref(ms), C.byref(n)))
+    return ms.value, n.value
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,45 @@
+/*
+ * dflash_prof.h — measurement hook of libdflash (not part of the drafter's
+ * arithmetic).
+ *
+ * While a timer is running, the library brackets every launch of one kernel
+ * class with a pair of HIP events.  The events are recorded on the stream the
+ * kernel is launched on.  A benchmark can thus measure one kernel's average
+ * duration inside a normal run of the public calls.  One timer exists per
+ * process, guarded by a mutex.  The events come from a pool created by
+ * dflash_prof_start, which may call hipEventCreate.  While the timer is off,
+ * nothing is recorded.
+ */
+#ifndef DFLASH_PROF_H
+#define DFLASH_PROF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* kernel classes */
+#define DFLASH_K_GEMM_FC      1   /* fc projection of the taps */
+#define DFLASH_K_GEMM_KV      2   /* ingest k|v projection */
+#define DFLASH_K_GEMM_QKV     3   /* block q|k|v projection */
+#define DFLASH_K_GEMM_O       4   /* o_proj + residual */
+#define DFLASH_K_GEMM_GATEUP  5   /* gate|up + SwiGLU */
+#define DFLASH_K_GEMM_DOWN    6   /* down + residual */
+#define DFLASH_K_ATTN         7   /* attention (splits + merge) */
+#define DFLASH_K_ROPE         8   /* head norm + rope + KV stores */
+#define DFLASH_K_NORM         9   /* row RMSNorm */
+
+/* Start timing launches of `kernel_class`, for up to `max_launches`
+ * launches.  Later launches are not timed.  DFLASH_E_INVAL for a bad class or
+ * count; DFLASH_E_HIP if the events cannot be created. */
+int dflash_prof_start(int32_t kernel_class, int32_t max_launches);
+
+/* Stop the timer.  Synchronises on the recorded events, then writes the
+ * summed duration (ms) and the number of timed launches. */
+int dflash_prof_stop(double *total_ms, int32_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_PROF_H */
