@@ -183,7 +183,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     st_coherent(mine + ((mt * NACC + a) * 4 + wave) * 256 + lane * 4 + j, acc[mt][a][j]);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // wait for the stores
+        // every partial store must have completed before this workgroup is counted
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         __shared__ int is_last;
         if (tid == 0) {
@@ -192,16 +193,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
         }
         __syncthreads();
         if (!is_last) return;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        // Sum the partials in split order.  All loads of a group of up to
+        // MAXS splits are issued before the first add.
+        constexpr int MAXS = 16;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int a = 0; a < NACC; ++a) {
                 f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-                for (int s = 0; s < p.ksplit; ++s) {
-                    const float *q = part + (size_t)s * PER + ((mt * NACC + a) * 4 + wave) * 256 + lane * 4;
+                const float *q0 = part + ((mt * NACC + a) * 4 + wave) * 256 + lane * 4;
+                for (int s0 = 0; s0 < p.ksplit; s0 += MAXS) {
+                    f32x4 pv[MAXS];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) v[j] += ld_coherent(q + j);
+                    for (int s = 0; s < MAXS; ++s)
+                        if (s0 + s < p.ksplit)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) pv[s][j] = ld_coherent(q0 + (size_t)(s0 + s) * PER + j);
+#pragma unroll
+                    for (int s = 0; s < MAXS; ++s)
+                        if (s0 + s < p.ksplit) v += pv[s];
                 }
                 acc[mt][a] = v;
             }
@@ -210,6 +220,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 
     // ---- epilogue: lane holds rows 4g + j, column r16 of each 16x16 tile ----
     const int col = n0 + r16, ccol = ncol + r16;
+    float sc[NACC];
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) sc[a] = (WT == WT_FP8) ? wscale[a][ccol] : 1.f;
+    float res[MT][4];
+    if constexpr (EPI == EPI_ADD) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = m0 + mt * 16 + 4 * g + j;
+                res[mt][j] = row < p.M ? p.Y[(size_t)row * p.ldy + col] : 0.f;
+            }
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -218,14 +241,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
             if (row >= p.M) continue;
             float *y = p.Y + (size_t)row * p.ldy + col;
             if constexpr (EPI == EPI_SWIGLU) {
-                float gv = acc[mt][0][j], uv = acc[mt][1][j];
-                if constexpr (WT == WT_FP8) { gv *= wscale[0][ccol]; uv *= wscale[1][ccol]; }
-                *y = silu(gv) * uv;
+                *y = silu(acc[mt][0][j] * sc[0]) * (acc[mt][1][j] * sc[1]);
+            } else if constexpr (EPI == EPI_ADD) {
+                *y = res[mt][j] + acc[mt][0][j] * sc[0];
             } else {
-                float r = acc[mt][0][j];
-                if constexpr (WT == WT_FP8) r *= wscale[0][ccol];
-                if constexpr (EPI == EPI_ADD) *y += r;
-                else *y = r;
+                *y = acc[mt][0][j] * sc[0];
             }
         }
 }
