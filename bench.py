@@ -15,8 +15,9 @@ are resident in HBM before the timed region starts.
 
 Printed as one JSON line:
 * value: rounds per second;
-* roofline: the gate|up + SwiGLU GEMM's algorithmic bytes per launch over its
-  average launch time, timed live with HIP events on its stream;
+* roofline: the persistent forward_round kernel's algorithmic bytes per
+  launch over its average launch time, timed live with HIP events on its
+  stream;
 * cpu_baseline: the fp64 CPU oracle running the same round on a bounded
   sample.
 """
@@ -60,11 +61,18 @@ def round_bytes(cfg, ctx: int, t: int = 16, b: int = 16) -> dict:
                 kv_write=kv_write, taps=taps, scales=scales, total=tot)
 
 
-def gateup_bytes(cfg, b: int = 16) -> int:
-    """gate|up + SwiGLU launch: both weight matrices, the normed input rows
-    and the SwiGLU output rows."""
+def round_kernel_bytes(cfg, ctx: int, b: int = 16) -> int:
+    """One launch of the persistent forward_round kernel: every layer's
+    weights once, each layer's K/V over all ctx + b keys once, the block K/V
+    rows written, the block embeddings read and the output written."""
     wb = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight_dtype]
-    return 2 * cfg.intermediate * cfg.hidden * wb + b * cfg.hidden * 4 + b * cfg.intermediate * 4
+    kvb = 4 if cfg.kv_dtype == "f32" else 2
+    H, I, qd, kvd, L = cfg.hidden, cfg.intermediate, cfg.q_dim, cfg.kv_dim, cfg.n_layers
+    layer_w = ((qd + 2 * kvd) * H + H * qd + 3 * I * H) * wb * L
+    kv_read = (ctx + b) * kvd * 2 * kvb * L
+    kv_write = b * kvd * 2 * kvb * L
+    io = 2 * b * H * 4
+    return layer_w + kv_read + kv_write + io
 
 
 def cpu_baseline(cfg, ctx: int, seconds: float) -> dict:
@@ -178,16 +186,16 @@ def main(argv=None) -> int:
 
     roofline = None
     if not args.no_prof:
-        # live timing of the dominant kernel (gate|up + SwiGLU GEMM, 8 launches per round)
-        D.dflash_prof_start(D.K_GEMM_GATEUP, args.steps * cfg.n_layers)
+        # live timing of the dominant kernel: the persistent forward_round kernel (1 launch per round)
+        D.dflash_prof_start(D.K_ROUND, args.steps)
         gpu_p, wall_p = timed(args.steps)
         tot_ms, nl = D.dflash_prof_stop()
         avg_s = tot_ms / 1e3 / max(nl, 1)
-        gb = gateup_bytes(cfg, b)
+        gb = round_kernel_bytes(cfg, ctx, b)
         ach = gb / avg_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": "gemm gate|up + SwiGLU (M=16, N=2x6144, K=2048, bf16)",
+                    "kernel": "persistent forward_round kernel (8 layers, b=16, 4112 keys)",
                     "bytes_per_launch": gb, "avg_launch_us": round(avg_s * 1e6, 2), "launches": nl,
                     "ms_per_step_while_timed": round(max(gpu_p, wall_p) * 1e3 / args.steps, 4)}
 

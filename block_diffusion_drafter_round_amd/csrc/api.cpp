@@ -4,6 +4,7 @@
 // Pages: [DflashDraft] (docs.rs memra_engine::dflash::DflashDraft) sections
 // "ctx_features", "forward", "ingest_ctx", "forward_round", "rope_yarn";
 // [memra dflash module] "DflashKv"; [atlas dflash_head] "DflashScratch".
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -16,6 +17,7 @@
 #include "dflash.h"
 #include "dflash_prof.h"
 #include "kernels.h"
+#include "round.h"
 
 struct dflash_model {
     dflash_cfg cfg;
@@ -74,7 +76,7 @@ constexpr int MAX_ATTN_SPLITS = 64;
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct WsLayout {
-    size_t x, xn, qkv, q, o, z, feats, part_o, part_ml, gpart, gcnt, total;
+    size_t x, xn, qkv, q, o, z, feats, part_o, part_ml, gpart, gcnt, bar, ssq, rpart, total;
 };
 
 WsLayout ws_layout(const dflash_cfg &c, int max_rows) {
@@ -87,6 +89,7 @@ WsLayout ws_layout(const dflash_cfg &c, int max_rows) {
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     // fixed-size regions first, so their offsets do not depend on max_rows
     L.gcnt = take(sizeof(unsigned) * dfl::GEMM_MAX_COUNTERS);
+    L.bar = take(sizeof(unsigned) * dfl::BAR_WORDS);
     L.x = take(4 * MAX_BLOCK * H);
     L.xn = take(4 * MAX_BLOCK * H);
     L.q = take(4 * MAX_BLOCK * qd);
@@ -95,6 +98,8 @@ WsLayout ws_layout(const dflash_cfg &c, int max_rows) {
     L.part_o = take(4 * (size_t)c.n_kv_heads * MAX_ATTN_SPLITS * qpad * c.head_dim);
     L.part_ml = take(4 * (size_t)c.n_kv_heads * MAX_ATTN_SPLITS * qpad * 2);
     L.gpart = take(4 * dfl::GEMM_PART_FLOATS);
+    L.ssq = take(4 * (H / 128) * MAX_BLOCK);
+    L.rpart = take(4 * (size_t)dfl::MAX_NWG * dfl::MAXSLOT * MAX_BLOCK * 256);
     // row-dependent regions
     size_t qkv_rows = MAX_BLOCK * (qd + 2 * kvd), ing = rows * 2 * kvd;
     L.qkv = take(4 * (qkv_rows > ing ? qkv_rows : ing));
@@ -252,99 +257,90 @@ hipError_t run_ingest(const dflash_model *m, dflash_kv *kv, const float *feats, 
     return hipSuccess;
 }
 
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+int ks_of(int wt) { return wt == DFLASH_BF16 ? 32 : wt == DFLASH_FP8_E4M3 ? 64 : 16; }
+
+dfl::GemmPlanDev plan_gemm(int N, int K, int wt, int nwg) {
+    dfl::GemmPlanDev p;
+    p.K = K;
+    p.steps = K / ks_of(wt);
+    p.total = (N / 128) * p.steps;
+    p.upw = (p.total + nwg - 1) / nwg;
+    return p;
+}
+
+bool plan_ok(const dfl::GemmPlanDev &p) { return (p.upw + p.steps - 1) / p.steps + 1 <= dfl::MAXSLOT; }
+
+dfl::MatRef mref(const dflash_matrix &m, int n) { return dfl::MatRef{m.data, m.scale, n, 0}; }
+
 hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *noise, const int32_t *pos, int b, float *out,
                      void *ws, const WsLayout &L, hipStream_t s) {
     const dflash_cfg &c = m->cfg;
-    const int H = c.hidden, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim, I = c.intermediate;
-    float *X = at<float>(ws, L.x), *XN = at<float>(ws, L.xn), *QKV = at<float>(ws, L.qkv);
-    float *Q = at<float>(ws, L.q), *O = at<float>(ws, L.o), *Z = at<float>(ws, L.z);
-    float *gp = at<float>(ws, L.gpart);
-    unsigned *gc = at<unsigned>(ws, L.gcnt);
-    const int wt = wtype(c);
-    hipError_t e;
-    if (c.n_layers == 0) {
-        ProfScope p(DFLASH_K_NORM, s);
-        return dfl::rmsnorm(noise, H, m->w.g_norm, out, H, nullptr, b, H, c.rms_eps, s);
-    }
-
-    for (int l = 0; l < c.n_layers; ++l) {
-        const dflash_layer_weights &W = m->layers[l];
-        // input norm (layer 0 also copies the block embeddings into the residual stream)
+    const int nwg = std::min(device_cus(), dfl::MAX_NWG);
+    if (nwg <= 0) return hipErrorInvalidDevice;
+    dfl::RoundArgs ra{};
+    dfl::RoundScalars &a = ra.s;
+    a.H = c.hidden; a.nq = c.n_q_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim; a.I = c.intermediate;
+    a.qd = c.n_q_heads * c.head_dim; a.kvd = c.n_kv_heads * c.head_dim;
+    a.wt = c.weight_dtype; a.kv_f32 = c.kv_dtype == DFLASH_F32;
+    a.b = b; a.len = kv->len; a.cap = kv->capacity;
+    a.eps = c.rms_eps; a.mscale = (float)m->mscale;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+    // attention key splits: at most one item per workgroup, keys per split a multiple of 32
+    const int n_keys = kv->len + b;
+    int ns = std::min({dfl::RND_MAX_SPLITS, (n_keys + 31) / 32, std::max(1, nwg / c.n_kv_heads)});
+    int kps = (n_keys + ns - 1) / ns;
+    kps = (kps + 31) / 32 * 32;
+    a.attn_kps = kps;
+    a.attn_nsplit = (n_keys + kps - 1) / kps;
+    a.qpad = (b * (c.n_q_heads / c.n_kv_heads) + 15) / 16 * 16;
+    a.noise = noise; a.pos = pos; a.out = out; a.g_norm = m->w.g_norm;
+    a.kv_lstride = (long long)c.n_kv_heads * kv->capacity * c.head_dim * (long long)kv_elem(c);
+    a.X = at<float>(ws, L.x); a.ssq = at<float>(ws, L.ssq); a.Q = at<float>(ws, L.q); a.O = at<float>(ws, L.o);
+    a.Z = at<float>(ws, L.z); a.part = at<float>(ws, L.rpart);
+    a.attn_o = at<float>(ws, L.part_o); a.attn_ml = at<float>(ws, L.part_ml);
+    a.bar = at<unsigned>(ws, L.bar);
+    a.p_qkv = plan_gemm(a.qd + 2 * a.kvd, a.H, a.wt, nwg);
+    a.p_o = plan_gemm(a.H, a.qd, a.wt, nwg);
+    a.p_gu = plan_gemm(a.I, a.H, a.wt, nwg);
+    a.p_d = plan_gemm(a.H, a.I, a.wt, nwg);
+    if (!plan_ok(a.p_qkv) || !plan_ok(a.p_o) || !plan_ok(a.p_gu) || !plan_ok(a.p_d)) return hipErrorInvalidValue;
+    memcpy(ra.inv_freq, m->inv_freq, sizeof ra.inv_freq);
+    int l0 = 0;
+    do {
+        const int nl = std::min(dfl::RND_MAXL, c.n_layers - l0);
+        a.nl = nl;
+        a.first = l0 == 0;
+        a.last = l0 + nl == c.n_layers;
+        a.kc = static_cast<char *>(layer_ptr(kv->k, c, kv->capacity, l0));
+        a.vc = static_cast<char *>(layer_ptr(kv->v, c, kv->capacity, l0));
+        for (int i = 0; i < nl; ++i) {
+            const dflash_layer_weights &W = m->layers[l0 + i];
+            dfl::LayerRefs &R = ra.L[i];
+            R.q = mref(W.wq, a.qd); R.k = mref(W.wk, a.kvd); R.v = mref(W.wv, a.kvd);
+            R.o = mref(W.wo, a.H); R.g = mref(W.wg, a.I); R.u = mref(W.wu, a.I); R.d = mref(W.wd, a.H);
+            R.g_in = W.g_in; R.g_post = W.g_post; R.g_q = W.g_q; R.g_k = W.g_k;
+        }
+        hipError_t e;
         {
-            ProfScope p(DFLASH_K_NORM, s);
-            e = l == 0 ? dfl::rmsnorm(noise, H, W.g_in, XN, H, X, b, H, c.rms_eps, s)
-                       : dfl::rmsnorm(X, H, W.g_in, XN, H, nullptr, b, H, c.rms_eps, s);
+            ProfScope p(DFLASH_K_ROUND, s);
+            e = dfl::round_launch(ra, nwg, s);
         }
         if (e != hipSuccess) return e;
-        // q | k | v projections of the block rows
-        dfl::GemmArgs g{};
-        g.A = XN; g.lda = H; g.M = b; g.K = H;
-        g.seg[0] = seg(W.wq, qd); g.seg[1] = seg(W.wk, kvd); g.seg[2] = seg(W.wv, kvd); g.nseg = 3;
-        g.Y = QKV; g.ldy = qd + 2 * kvd; g.epi = dfl::EPI_STORE; g.wtype = wt;
-        {
-            ProfScope p(DFLASH_K_GEMM_QKV, s);
-            e = dfl::gemm(g, gp, gc, s);
-        }
-        if (e != hipSuccess) return e;
-        // q/k head norm + rope; block K/V into cache rows [len, len + b)
-        dfl::RopeArgs r{};
-        r.src = QKV; r.ld = qd + 2 * kvd; r.q_off = 0; r.k_off = qd; r.v_off = qd + kvd;
-        r.g_q = W.g_q; r.g_k = W.g_k; r.pos = pos; r.rows = b;
-        r.nq = c.n_q_heads; r.nkv = c.n_kv_heads; r.d = c.head_dim; r.eps = c.rms_eps; r.mscale = (float)m->mscale;
-        r.q_out = Q; r.kc = layer_ptr(kv->k, c, kv->capacity, l); r.vc = layer_ptr(kv->v, c, kv->capacity, l);
-        r.cap = kv->capacity; r.row0 = kv->len; r.kv_f32 = c.kv_dtype == DFLASH_F32;
-        memcpy(r.inv_freq, m->inv_freq, sizeof r.inv_freq);
-        {
-            ProfScope p(DFLASH_K_ROPE, s);
-            e = dfl::qk_norm_rope(r, s);
-        }
-        if (e != hipSuccess) return e;
-        // attention over all len + b keys
-        dfl::AttnArgs a{};
-        a.q = Q; a.kc = r.kc; a.vc = r.vc; a.cap = kv->capacity; a.n_keys = kv->len + b;
-        a.b = b; a.nq = c.n_q_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim; a.kv_f32 = r.kv_f32;
-        a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
-        dfl::attn_plan(a, MAX_ATTN_SPLITS);
-        a.part_o = at<float>(ws, L.part_o); a.part_ml = at<float>(ws, L.part_ml); a.out = O;
-        {
-            ProfScope p(DFLASH_K_ATTN, s);
-            e = dfl::attention(a, s);
-        }
-        if (e != hipSuccess) return e;
-        // o_proj + residual
-        g = dfl::GemmArgs{};
-        g.A = O; g.lda = qd; g.M = b; g.K = qd; g.seg[0] = seg(W.wo, H); g.nseg = 1;
-        g.Y = X; g.ldy = H; g.epi = dfl::EPI_ADD; g.wtype = wt;
-        {
-            ProfScope p(DFLASH_K_GEMM_O, s);
-            e = dfl::gemm(g, gp, gc, s);
-        }
-        if (e != hipSuccess) return e;
-        // post-attention norm, gate|up + SwiGLU, down + residual
-        {
-            ProfScope p(DFLASH_K_NORM, s);
-            e = dfl::rmsnorm(X, H, W.g_post, XN, H, nullptr, b, H, c.rms_eps, s);
-        }
-        if (e != hipSuccess) return e;
-        g = dfl::GemmArgs{};
-        g.A = XN; g.lda = H; g.M = b; g.K = H; g.seg[0] = seg(W.wg, I); g.seg[1] = seg(W.wu, I); g.nseg = 2;
-        g.Y = Z; g.ldy = I; g.epi = dfl::EPI_SWIGLU; g.wtype = wt;
-        {
-            ProfScope p(DFLASH_K_GEMM_GATEUP, s);
-            e = dfl::gemm(g, gp, gc, s);
-        }
-        if (e != hipSuccess) return e;
-        g = dfl::GemmArgs{};
-        g.A = Z; g.lda = I; g.M = b; g.K = I; g.seg[0] = seg(W.wd, H); g.nseg = 1;
-        g.Y = X; g.ldy = H; g.epi = dfl::EPI_ADD; g.wtype = wt;
-        {
-            ProfScope p(DFLASH_K_GEMM_DOWN, s);
-            e = dfl::gemm(g, gp, gc, s);
-        }
-        if (e != hipSuccess) return e;
-    }
-    ProfScope p(DFLASH_K_NORM, s);
-    return dfl::rmsnorm(X, H, m->w.g_norm, out, H, nullptr, b, H, c.rms_eps, s);
+        l0 += nl;
+    } while (l0 < c.n_layers);
+    return hipSuccess;
 }
 
 }  // namespace
@@ -476,9 +472,28 @@ int dflash_forward_full(const dflash_model *m, const float *taps, const float *n
     return DFLASH_OK;
 }
 
+int dflash_workspace_status(const dflash_model *m, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    if (!m) return fail(DFLASH_E_INVAL, "model is null");
+    int rc = check_ws(m, ws, ws_bytes, 0);
+    if (rc) return rc;
+    const WsLayout L = ws_layout(m->cfg, 0);
+    unsigned *err = at<unsigned>(ws, L.bar) + dfl::BAR_ERR;
+    unsigned h = 0;
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e == hipSuccess) e = hipMemcpy(&h, err, sizeof h, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "workspace_status");
+    if (h != 0) {
+        const unsigned zero = 0;
+        hipMemcpy(err, &zero, sizeof zero, hipMemcpyHostToDevice);
+        return fail(DFLASH_E_HIP, "a grid barrier of the round kernel timed out (not all workgroups were resident)");
+    }
+    return DFLASH_OK;
+}
+
 int dflash_prof_start(int32_t kernel_class, int32_t max_launches) {
     g_err.clear();
-    if (kernel_class < DFLASH_K_GEMM_FC || kernel_class > DFLASH_K_NORM || max_launches <= 0 || max_launches > (1 << 20))
+    if (kernel_class < DFLASH_K_GEMM_FC || kernel_class > DFLASH_K_ROUND || max_launches <= 0 || max_launches > (1 << 20))
         return fail(DFLASH_E_INVAL, "bad kernel class %d or launch count %d", kernel_class, max_launches);
     std::lock_guard<std::mutex> lk(g_prof.mu);
     while ((int)g_prof.ev.size() < 2 * max_launches) {

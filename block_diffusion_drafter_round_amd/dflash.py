@@ -60,10 +60,10 @@ class dflash_kv(C.Structure):
 _lib = None
 EXPORTS = ("dflash_load_weights", "dflash_free", "dflash_workspace_bytes", "dflash_ctx_features",
            "dflash_ingest_ctx", "dflash_forward_round", "dflash_forward_full", "dflash_last_error",
-           "dflash_rope_table", "dflash_prof_start", "dflash_prof_stop")
+           "dflash_rope_table", "dflash_prof_start", "dflash_prof_stop", "dflash_workspace_status")
 
 # kernel classes of the measurement hook (include/dflash_prof.h)
-K_GEMM_FC, K_GEMM_KV, K_GEMM_QKV, K_GEMM_O, K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN, K_ROPE, K_NORM = range(1, 10)
+K_GEMM_FC, K_GEMM_KV, K_GEMM_QKV, K_GEMM_O, K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN, K_ROPE, K_NORM, K_ROUND = range(1, 11)
 
 
 def lib():
@@ -88,6 +88,7 @@ def lib():
     L.dflash_rope_table.argtypes = [vp, C.POINTER(C.c_double), i32, C.POINTER(C.c_double)]
     L.dflash_prof_start.argtypes = [i32, i32]
     L.dflash_prof_stop.argtypes = [C.POINTER(C.c_double), C.POINTER(i32)]
+    L.dflash_workspace_status.argtypes = [vp, vp, sz, vp]
     for name in EXPORTS:
         if name not in ("dflash_free", "dflash_workspace_bytes", "dflash_last_error"):
             getattr(L, name).restype = C.c_int
@@ -163,6 +164,10 @@ def dflash_rope_table(model, half: int):
     ms = C.c_double()
     _check(lib().dflash_rope_table(model, buf, half, C.byref(ms)))
     return list(buf), ms.value
+
+
+def dflash_workspace_status(model, ws, ws_bytes, stream=None) -> None:
+    _check(lib().dflash_workspace_status(model, _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def dflash_prof_start(kernel_class: int, max_launches: int) -> None:
@@ -298,6 +303,10 @@ class Drafter:
                 self.model = None
         except Exception:
             pass
+
+    def status(self) -> None:
+        """Raise if a kernel that used this workspace timed out at a grid barrier."""
+        dflash_workspace_status(self.model, self.ws, self.ws_bytes)
 
     def ctx_features(self, taps: torch.Tensor) -> torch.Tensor:
         t = taps.shape[0]

@@ -208,6 +208,14 @@ int dflash_forward_full(const dflash_model *m, const float *taps, const float *n
                         const int32_t *pos, int32_t n, int32_t b, float *out,
                         dflash_kv *scratch, void *ws, size_t ws_bytes, void *stream);
 
+/* Synchronise `stream`, then report whether a kernel that used `ws` hit its
+ * bounded grid-barrier wait.  The persistent round kernel needs one resident
+ * workgroup per CU; if some could not start, its barriers time out after
+ * about a second.  The kernel then exits with an undefined output and sets a
+ * flag in the workspace.  Returns DFLASH_E_HIP (and clears the flag) if the
+ * flag was set, else DFLASH_OK.  A diagnostic call: it blocks the host. */
+int dflash_workspace_status(const dflash_model *m, void *ws, size_t ws_bytes, void *stream);
+
 /* Message for the calling thread's last error ("" if none). */
 const char *dflash_last_error(void);
 

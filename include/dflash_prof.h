@@ -29,6 +29,7 @@ extern "C" {
 #define DFLASH_K_ATTN         7   /* attention (splits + merge) */
 #define DFLASH_K_ROPE         8   /* head norm + rope + KV stores */
 #define DFLASH_K_NORM         9   /* row RMSNorm */
+#define DFLASH_K_ROUND       10   /* persistent forward_round kernel (one launch per 8 layers) */
 
 /* Start timing launches of `kernel_class`, for up to `max_launches`
  * launches.  Later launches are not timed.  DFLASH_E_INVAL for a bad class or

@@ -41,7 +41,9 @@ def kv_rows_f64(kv, layer: int, start: int, stop: int):
     return host(k), host(v)
 
 
-def check(name, gpu, ref, tol):
+def check(name, gpu, ref, tol, drafter=None):
+    if drafter is not None:
+        drafter.status()
     err = rel_rows(gpu, ref)
     print(f"[parity] {name}: rel={err:.3e} tol={tol:.1e}", flush=True)
     assert np.all(np.isfinite(gpu)), f"{name}: non-finite GPU output"
