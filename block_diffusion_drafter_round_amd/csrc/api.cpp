@@ -52,6 +52,7 @@ struct Prof {
     std::vector<hipEvent_t> ev;   // start, stop pairs
     int used = 0, cap = 0;
 } g_prof;
+std::atomic<int> g_trace{0};
 
 struct ProfScope {
     int idx = -1;
@@ -76,7 +77,7 @@ constexpr int MAX_ATTN_SPLITS = 64;
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct WsLayout {
-    size_t x, xn, qkv, q, o, z, feats, part_o, part_ml, gpart, gcnt, bar, ssq, rpart, total;
+    size_t x, xn, qkv, q, o, z, feats, part_o, part_ml, gpart, gcnt, bar, ssq, rpart, trace, total;
 };
 
 WsLayout ws_layout(const dflash_cfg &c, int max_rows) {
@@ -90,6 +91,7 @@ WsLayout ws_layout(const dflash_cfg &c, int max_rows) {
     // fixed-size regions first, so their offsets do not depend on max_rows
     L.gcnt = take(sizeof(unsigned) * dfl::GEMM_MAX_COUNTERS);
     L.bar = take(sizeof(unsigned) * dfl::BAR_WORDS);
+    L.trace = take(8 * dfl::RND_TRACE_WORDS);
     L.x = take(4 * MAX_BLOCK * H);
     L.xn = take(4 * MAX_BLOCK * H);
     L.q = take(4 * MAX_BLOCK * qd);
@@ -148,6 +150,7 @@ int check_cfg(const dflash_cfg &c) {
                           (c.weight_dtype == DFLASH_BF16 && c.kv_dtype == DFLASH_BF16) ||
                           (c.weight_dtype == DFLASH_FP8_E4M3 && c.kv_dtype == DFLASH_BF16);
     if (!ok_types) return fail(DFLASH_E_UNSUPPORTED, "weight/kv dtype combination %d/%d not built", c.weight_dtype, c.kv_dtype);
+    if (c.kv_dtype == DFLASH_F32 && c.head_dim != 64) return fail(DFLASH_E_UNSUPPORTED, "an f32 KV cache is built for head_dim 64 only");
     if (c.d2_groups < 0) return fail(DFLASH_E_INVAL, "d2_groups must be >= 0");
     if (c.d2_groups > 0) return fail(DFLASH_E_UNSUPPORTED, "the DFlash2 conv wrap is not built yet");
     return DFLASH_OK;
@@ -311,6 +314,7 @@ hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *no
     a.Z = at<float>(ws, L.z); a.part = at<float>(ws, L.rpart);
     a.attn_o = at<float>(ws, L.part_o); a.attn_ml = at<float>(ws, L.part_ml);
     a.bar = at<unsigned>(ws, L.bar);
+    a.trace = g_trace.load() ? at<unsigned long long>(ws, L.trace) : nullptr;
     a.p_qkv = plan_gemm(a.qd + 2 * a.kvd, a.H, a.wt, nwg);
     a.p_o = plan_gemm(a.H, a.qd, a.wt, nwg);
     a.p_gu = plan_gemm(a.I, a.H, a.wt, nwg);
@@ -489,6 +493,22 @@ int dflash_workspace_status(const dflash_model *m, void *ws, size_t ws_bytes, vo
         return fail(DFLASH_E_HIP, "a grid barrier of the round kernel timed out (not all workgroups were resident)");
     }
     return DFLASH_OK;
+}
+
+int dflash_prof_trace(int32_t enable) {
+    g_trace.store(enable ? 1 : 0);
+    return DFLASH_OK;
+}
+
+int dflash_prof_trace_read(const dflash_model *m, void *ws, size_t ws_bytes, uint64_t *out, int32_t n, void *stream) {
+    g_err.clear();
+    if (!m || !out || n < 0 || n > dfl::RND_TRACE_WORDS) return fail(DFLASH_E_INVAL, "bad trace read arguments");
+    int rc = check_ws(m, ws, ws_bytes, 0);
+    if (rc) return rc;
+    const WsLayout L = ws_layout(m->cfg, 0);
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e == hipSuccess) e = hipMemcpy(out, at<unsigned long long>(ws, L.trace), sizeof(uint64_t) * n, hipMemcpyDeviceToHost);
+    return e == hipSuccess ? DFLASH_OK : hip_fail(e, "trace_read");
 }
 
 int dflash_prof_start(int32_t kernel_class, int32_t max_launches) {

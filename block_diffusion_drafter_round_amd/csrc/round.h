@@ -48,8 +48,10 @@ struct RoundScalars {
     long long kv_lstride;            // bytes per layer (K and V alike)
     float *X, *ssq, *Q, *O, *Z, *part, *attn_o, *attn_ml;
     unsigned *bar;
+    unsigned long long *trace;       // phase timestamps (workgroup 0), or nullptr
     GemmPlanDev p_qkv, p_o, p_gu, p_d;
 };
+constexpr int RND_TRACE_WORDS = 1024;
 
 // Kernel arguments.  The arrays are indexed at run time, so the kernel reads
 // them in place from the kernel-argument segment.

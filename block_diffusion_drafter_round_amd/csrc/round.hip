@@ -71,6 +71,13 @@ __device__ __forceinline__ u32x4 ldc4(const void *base, uint32_t byte_off) {
 __device__ __forceinline__ u32x2 ldc2(const void *base, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b64(cbuf(base), byte_off, 0, CPOL_SC1);
 }
+__device__ __forceinline__ void stc4(void *base, uint32_t byte_off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, cbuf(base), byte_off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ void stc2f(float *base, size_t elem, float x0, float x1) {
+    const u32x2 v = {__float_as_uint(x0), __float_as_uint(x1)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, cbuf(base), (uint32_t)(elem * 4), 0, CPOL_SC1);
+}
 __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ float ldc(const float *p) {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -170,6 +177,12 @@ __device__ __forceinline__ bool grid_sync(unsigned *st, unsigned &gen) {
     return ok != 0;
 }
 
+// Phase trace: workgroup 0 stamps the 100 MHz wall clock after each barrier.
+__device__ __forceinline__ void trace_mark(unsigned long long *tr, int &k) {
+    if (tr && blockIdx.x == 0 && threadIdx.x == 0 && k < RND_TRACE_WORDS) tr[k] = wall_clock64();
+    ++k;
+}
+
 // ---------------------------------------------------------------------------
 // stream-K GEMM phase
 // ---------------------------------------------------------------------------
@@ -239,24 +252,28 @@ __device__ __forceinline__ void gemm_issue_first(const GemmIO &io, Prefetch &pf)
     gemm_issue<WT, DUAL>(io, u0, min(n, maxu<WT, DUAL>()), pf);
 }
 
+// acc = W_frag . A_frag^T: the weights are the A operand (MFMA row = output
+// column n), the activations the B operand (MFMA column = row m).  Lane
+// (r16, g) then holds output columns 4g..4g+3 of row r16, contiguous in a
+// row-major [m][n] tile.
 template <int WT>
 __device__ __forceinline__ void mac_unit(f32x4 &acc, const u32x4 &wv, const u32x4 *af) {
     if constexpr (WT == WT_BF16) {
         const bf16x8 b = __builtin_bit_cast(bf16x8, wv);
-        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[0]), b, acc);
-        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[64]), b, acc);
+        acc = mfma_bf16(b, __builtin_bit_cast(bf16x8, af[0]), acc);
+        acc = mfma_bf16(b, __builtin_bit_cast(bf16x8, af[64]), acc);
     } else if constexpr (WT == WT_FP8) {
         const bf16x8 b0 = fp8x8_to_bf16x8(wv.x, wv.y), b1 = fp8x8_to_bf16x8(wv.z, wv.w);
-        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[0]), b0, acc);
-        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[64]), b0, acc);
-        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[128]), b1, acc);
-        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[192]), b1, acc);
+        acc = mfma_bf16(b0, __builtin_bit_cast(bf16x8, af[0]), acc);
+        acc = mfma_bf16(b0, __builtin_bit_cast(bf16x8, af[64]), acc);
+        acc = mfma_bf16(b1, __builtin_bit_cast(bf16x8, af[128]), acc);
+        acc = mfma_bf16(b1, __builtin_bit_cast(bf16x8, af[192]), acc);
     } else {
         const u32x4 a = af[0];
-        acc = mfma_f32(f_of(a.x), f_of(wv.x), acc);
-        acc = mfma_f32(f_of(a.y), f_of(wv.y), acc);
-        acc = mfma_f32(f_of(a.z), f_of(wv.z), acc);
-        acc = mfma_f32(f_of(a.w), f_of(wv.w), acc);
+        acc = mfma_f32(f_of(wv.x), f_of(a.x), acc);
+        acc = mfma_f32(f_of(wv.y), f_of(a.y), acc);
+        acc = mfma_f32(f_of(wv.z), f_of(a.z), acc);
+        acc = mfma_f32(f_of(wv.w), f_of(a.w), acc);
     }
 }
 
@@ -352,12 +369,11 @@ __device__ __forceinline__ void gemm_run(const GemmIO &io, Prefetch &pf, u32x4 *
                 const bool seg_end = (c0 + i == n - 1) || ((unit + 1) % io.p.steps == 0);
                 if (seg_end) {
                     const int grp = unit / io.p.steps;
-                    float *dst = io.part + ((size_t)(blockIdx.x * MAXSLOT + (grp - first_grp)) * 16) * PW;
+                    const size_t tile = (size_t)(blockIdx.x * MAXSLOT + (grp - first_grp)) * 16 * PW;
 #pragma unroll
                     for (int m = 0; m < NM; ++m)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            stc(dst + (size_t)(4 * g + j) * PW + m * 128 + wave * 16 + r16, acc[m][j]);
+                        stc4(io.part, (uint32_t)((tile + (size_t)r16 * PW + m * 128 + wave * 16 + 4 * g) * 4),
+                             __builtin_bit_cast(u32x4, acc[m]));
 #pragma unroll
                     for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
@@ -411,8 +427,7 @@ __device__ __forceinline__ void init_phase(const RoundScalars &a) {
     for (int it = gwave(); it < ng * a.b; it += nwaves()) {
         const int grp = it % ng, r = it / ng, c = grp * 128 + 2 * lane;
         const float2 x = *reinterpret_cast<const float2 *>(a.noise + (size_t)r * a.H + c);
-        stc(a.X + (size_t)r * a.H + c, x.x);
-        stc(a.X + (size_t)r * a.H + c + 1, x.y);
+        stc2f(a.X, (size_t)r * a.H + c, x.x, x.y);
         const float ss = wave_sum(x.x * x.x + x.y * x.y);
         if (lane == 0) stc(a.ssq + grp * 16 + r, ss);
     }
@@ -426,8 +441,7 @@ __device__ __forceinline__ void residual_phase(const RoundScalars &a, const Gemm
         float2 s = sum_slots2(p, a.part, grp, r, cl, 128);
         const u32x2 xo = ldc2(a.X, (uint32_t)(((size_t)r * a.H + c) * 4));
         const float x0 = f_of(xo.x) + s.x * col_scale(m, c), x1 = f_of(xo.y) + s.y * col_scale(m, c + 1);
-        stc(a.X + (size_t)r * a.H + c, x0);
-        stc(a.X + (size_t)r * a.H + c + 1, x1);
+        stc2f(a.X, (size_t)r * a.H + c, x0, x1);
         const float ss = wave_sum(x0 * x0 + x1 * x1);
         if (lane == 0) stc(a.ssq + grp * 16 + r, ss);
     }
@@ -445,8 +459,7 @@ __device__ __forceinline__ void swiglu_phase(const RoundScalars &a, const LayerR
         const float2 us = sum_slots2(a.p_gu, a.part, grp, r, 128 + cl, 256);
         const float g0 = gs.x * rs * col_scale(L.g, c), g1 = gs.y * rs * col_scale(L.g, c + 1);
         const float u0 = us.x * rs * col_scale(L.u, c), u1 = us.y * rs * col_scale(L.u, c + 1);
-        stc(a.Z + (size_t)r * a.I + c, silu(g0) * u0);
-        stc(a.Z + (size_t)r * a.I + c + 1, silu(g1) * u1);
+        stc2f(a.Z, (size_t)r * a.I + c, silu(g0) * u0, silu(g1) * u1);
     }
 }
 
@@ -542,108 +555,148 @@ __device__ __forceinline__ void qkv_phase(const RoundScalars &a, const LayerRefs
 }
 
 // ---------------------------------------------------------------------------
-// attention: item (kv head h, key split s); wave w takes query tiles w, w + 8
+// attention: item (kv head h, key split s); wave w takes query tiles w, w + 8.
+// The workgroup stages K and V^T of each 32-key block in LDS (one
+// device-coherent 16-byte load per thread and tensor, double-buffered), and
+// all waves read their MFMA fragments from there.
 // S^T = K.Q^T puts one query per lane (l % 16) and keys 8g..8g+7 per lane
 // group; O^T = V^T.P^T keeps the same query per lane, so the online softmax
 // is lane-local apart from the 4-group row max / sum.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ u32x4 kv_frag(const char *base, size_t off, bool coh) {
-    if (coh) return ldc4(base, (uint32_t)off);
-    return *reinterpret_cast<const u32x4 *>(base + off);
-}
+template <bool F32, int D>
+struct AttnLds {
+    static constexpr int ES = F32 ? 4 : 2;
+    static constexpr int KC = D * ES / 16;          // 16-byte chunks per key row
+    static constexpr int VC = 32 * ES / 16;         // 16-byte chunks per V^T row of a block
+    static constexpr int KW = KC + 1, VW = VC + 1;  // padded row widths
+    static constexpr int STAGE = 32 * KW + D * VW;  // u32x4 per staged block
+};
 
 template <bool F32, int D>
-__device__ __forceinline__ void attn_phase(const RoundScalars &a, const char *kc, const char *vc) {
-    constexpr int NDS = F32 ? D / 16 : D / 32;
-    constexpr int NDT = D / 16;
-    constexpr int ES = F32 ? 4 : 2;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void attn_phase(const RoundScalars &a, const char *kc, const char *vc, u32x4 *lds) {
+    using AL = AttnLds<F32, D>;
+    constexpr int ES = AL::ES, KC = AL::KC, VC = AL::VC, KW = AL::KW, VW = AL::VW;
+    constexpr int NDS = F32 ? D / 16 : D / 32;       // MFMA d-steps per score tile
+    constexpr int NDT = D / 16;                      // output d-tiles
+    constexpr int TQ = 1;                            // query tiles per wave and pass
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r16 = lane & 15;
     const int G = a.nq / a.nkv, nqh = a.b * G, qtiles = a.qpad / 16;
     const int n_keys = a.len + a.b;
     const int items = a.nkv * a.attn_nsplit;
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
-        const int h = item / a.attn_nsplit, split = item - h * a.attn_nsplit;
+    const int npass = (qtiles + 7) / 8;              // more than 8 query tiles: a second pass over the keys
+    for (int item = blockIdx.x; item < items * npass; item += gridDim.x) {
+        const int pass = item / items, it0 = item - pass * items;
+        const int h = it0 / a.attn_nsplit, split = it0 - h * a.attn_nsplit;
         const int kbeg = split * a.attn_kps, kend = min(kbeg + a.attn_kps, n_keys);
-        for (int qt = wave; qt < qtiles; qt += RND_THREADS / 64) {
+        const int nblk = (kend - kbeg + 31) / 32;
+        // this thread's share of a staged block: one K chunk and one V^T chunk
+        const bool kact = tid < 32 * KC, vact = tid < D * VC;
+        const int kkey = tid / KC, kcol = tid - kkey * KC;
+        const int vrow = tid / VC, vcol = tid - vrow * VC;
+        auto kof = [&](int k0) { return (uint32_t)((((size_t)h * a.cap + k0 + kkey) * D) * ES + kcol * 16); };
+        auto vof = [&](int k0) { return (uint32_t)((((size_t)h * D + vrow) * a.cap + k0) * ES + vcol * 16); };
+        u32x4 kr = {0, 0, 0, 0}, vr = {0, 0, 0, 0};
+        if (kact) kr = ldc4(kc, kof(kbeg));
+        if (vact) vr = ldc4(vc, vof(kbeg));
+        __syncthreads();                            // LDS free (previous phase / item)
+        if (kact) lds[kkey * KW + kcol] = kr;
+        if (vact) lds[32 * KW + vrow * VW + vcol] = vr;
+
+        // query fragments (B operand of S^T) and running state per query tile
+        bf16x8 qb[TQ][F32 ? 1 : NDS];
+        float4 qf[TQ][F32 ? NDS : 1];
+        float m_run[TQ], l_run[TQ];
+        f32x4 o[TQ][NDT];
+#pragma unroll
+        for (int tq = 0; tq < TQ; ++tq) {
+            const int qt = wave + 8 * (tq + pass);
             const int qi = qt * 16 + r16;
-            const bool qvalid = qi < nqh;
+            const bool qvalid = qt < qtiles && qi < nqh;
             const uint32_t qoff = (uint32_t)(((size_t)(qvalid ? qi / G : 0) * a.nq + h * G + (qvalid ? qi % G : 0)) * D * 4);
-            bf16x8 qb[F32 ? 1 : NDS];
-            float4 qf[F32 ? NDS : 1];
 #pragma unroll
             for (int s = 0; s < NDS; ++s) {
                 if constexpr (!F32) {
-                    u32x4 p0 = ldc4(a.Q, qoff + (32 * s + 8 * g) * 4), p1 = ldc4(a.Q, qoff + (32 * s + 8 * g + 4) * 4);
+                    const u32x4 p0 = ldc4(a.Q, qoff + (32 * s + 8 * g) * 4), p1 = ldc4(a.Q, qoff + (32 * s + 8 * g + 4) * 4);
                     float x[8] = {f_of(p0.x), f_of(p0.y), f_of(p0.z), f_of(p0.w), f_of(p1.x), f_of(p1.y), f_of(p1.z), f_of(p1.w)};
                     if (!qvalid)
 #pragma unroll
                         for (int q = 0; q < 8; ++q) x[q] = 0.f;
-                    qb[s] = to_bf16x8(x);
+                    qb[tq][s] = to_bf16x8(x);
                 } else {
-                    u32x4 p0 = ldc4(a.Q, qoff + (16 * s + 4 * g) * 4);
-                    qf[s] = qvalid ? make_float4(f_of(p0.x), f_of(p0.y), f_of(p0.z), f_of(p0.w)) : make_float4(0, 0, 0, 0);
+                    const u32x4 p0 = ldc4(a.Q, qoff + (16 * s + 4 * g) * 4);
+                    qf[tq][s] = qvalid ? make_float4(f_of(p0.x), f_of(p0.y), f_of(p0.z), f_of(p0.w)) : make_float4(0, 0, 0, 0);
                 }
             }
-            float m_run = -1e30f, l_run = 0.f;
-            f32x4 o[NDT];
+            m_run[tq] = -1e30f;
+            l_run[tq] = 0.f;
 #pragma unroll
-            for (int t = 0; t < NDT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int k0 = kbeg; k0 < kend; k0 += 32) {
-                const bool coh = k0 + 32 > a.len;          // tile holds block rows written in this launch
+            for (int t = 0; t < NDT; ++t) o[tq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        __syncthreads();
+
+        for (int bi = 0; bi < nblk; ++bi) {
+            const int k0 = kbeg + 32 * bi;
+            const u32x4 *Kl = lds + (bi & 1) * AL::STAGE;
+            const u32x4 *Vl = Kl + 32 * KW;
+            // next block's loads overlap this block's math
+            if (bi + 1 < nblk) {
+                if (kact) kr = ldc4(kc, kof(k0 + 32));
+                if (vact) vr = ldc4(vc, vof(k0 + 32));
+            }
+            const bool full = k0 + 32 <= kend;
+#pragma unroll
+            for (int tq = 0; tq < TQ; ++tq) {
+                if (wave + 8 * (tq + pass) >= qtiles) continue;
                 f32x4 st[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    const int key = k0 + 8 * (r16 >> 2) + 4 * t + (r16 & 3);
-                    const size_t kr = ((size_t)h * a.cap + key) * D * ES;
+                    const int key = 8 * (r16 >> 2) + 4 * t + (r16 & 3);     // MFMA row r16 of tile t
 #pragma unroll
                     for (int s = 0; s < NDS; ++s) {
+                        const u32x4 kf = Kl[key * KW + 4 * s + g];
                         if constexpr (!F32) {
-                            u32x4 kv = kv_frag(kc, kr + (32 * s + 8 * g) * ES, coh);
-                            st[t] = mfma_bf16(__builtin_bit_cast(bf16x8, kv), qb[s], st[t]);
+                            st[t] = mfma_bf16(__builtin_bit_cast(bf16x8, kf), qb[tq][s], st[t]);
                         } else {
-                            u32x4 kv = kv_frag(kc, kr + (16 * s + 4 * g) * ES, coh);
-                            st[t] = mfma_f32(f_of(kv.x), qf[s].x, st[t]);
-                            st[t] = mfma_f32(f_of(kv.y), qf[s].y, st[t]);
-                            st[t] = mfma_f32(f_of(kv.z), qf[s].z, st[t]);
-                            st[t] = mfma_f32(f_of(kv.w), qf[s].w, st[t]);
+                            st[t] = mfma_f32(f_of(kf.x), qf[tq][s].x, st[t]);
+                            st[t] = mfma_f32(f_of(kf.y), qf[tq][s].y, st[t]);
+                            st[t] = mfma_f32(f_of(kf.z), qf[tq][s].z, st[t]);
+                            st[t] = mfma_f32(f_of(kf.w), qf[tq][s].w, st[t]);
                         }
                     }
                 }
+                // lane (query r16, group g) holds keys k0 + 8g + 4t + j
                 float sc[8];
                 float bmax = -INFINITY;
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
-                        const int key = k0 + 8 * g + 4 * t + jj;
                         float v = st[t][jj] * a.scale_log2;
-                        v = key < kend ? v : -INFINITY;
+                        v = k0 + 8 * g + 4 * t + jj < kend ? v : -INFINITY;
                         sc[4 * t + jj] = v;
                         bmax = fmaxf(bmax, v);
                     }
                 bmax = group4_max(bmax);
-                const float m_new = fmaxf(m_run, bmax);
-                const float corr = exp2f(m_run - m_new);
+                const float m_new = fmaxf(m_run[tq], bmax);
+                const float corr = __builtin_amdgcn_exp2f(m_run[tq] - m_new);
                 float psum = 0.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    sc[i] = exp2f(sc[i] - m_new);
+                    sc[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
                     psum += sc[i];
                 }
                 psum = group4_sum(psum);
-                l_run = l_run * corr + psum;
-                m_run = m_new;
+                l_run[tq] = l_run[tq] * corr + psum;
+                m_run[tq] = m_new;
 #pragma unroll
-                for (int t = 0; t < NDT; ++t) o[t] *= corr;
-                const bool full = (k0 + 32 <= kend);
+                for (int t = 0; t < NDT; ++t) o[tq][t] *= corr;
                 if constexpr (!F32) {
                     const bf16x8 pb = to_bf16x8(sc);
 #pragma unroll
                     for (int t = 0; t < NDT; ++t) {
-                        const size_t vr = (((size_t)h * D + 16 * t + r16) * a.cap + k0 + 8 * g) * ES;
-                        u32x4 vv = kv_frag(vc, vr, coh);
+                        u32x4 vv = Vl[(16 * t + r16) * VW + g];
                         if (!full) {
 #pragma unroll
                             for (int w = 0; w < 4; ++w) {
@@ -652,31 +705,41 @@ __device__ __forceinline__ void attn_phase(const RoundScalars &a, const char *kc
                                 vv[w] &= msk;
                             }
                         }
-                        o[t] = mfma_bf16(__builtin_bit_cast(bf16x8, vv), pb, o[t]);
+                        o[tq][t] = mfma_bf16(__builtin_bit_cast(bf16x8, vv), pb, o[tq][t]);
                     }
                 } else {
 #pragma unroll
                     for (int t = 0; t < NDT; ++t) {
-                        const size_t vr = (((size_t)h * D + 16 * t + r16) * a.cap + k0 + 8 * g) * ES;
-                        u32x4 v0 = kv_frag(vc, vr, coh), v1 = kv_frag(vc, vr + 16, coh);
+                        const u32x4 v0 = Vl[(16 * t + r16) * VW + 2 * g], v1 = Vl[(16 * t + r16) * VW + 2 * g + 1];
                         float vk[8] = {f_of(v0.x), f_of(v0.y), f_of(v0.z), f_of(v0.w), f_of(v1.x), f_of(v1.y), f_of(v1.z), f_of(v1.w)};
 #pragma unroll
                         for (int i = 0; i < 8; ++i) {
                             if (!full && k0 + 8 * g + i >= kend) vk[i] = 0.f;
-                            o[t] = mfma_f32(vk[i], sc[i], o[t]);
+                            o[tq][t] = mfma_f32(vk[i], sc[i], o[tq][t]);
                         }
                     }
                 }
             }
-            const size_t pq = ((size_t)h * a.attn_nsplit + split) * a.qpad + qi;
+            if (bi + 1 < nblk) {
+                u32x4 *Kn = lds + ((bi + 1) & 1) * AL::STAGE;
+                if (kact) Kn[kkey * KW + kcol] = kr;
+                if (vact) Kn[32 * KW + vrow * VW + vcol] = vr;
+            }
+            __syncthreads();
+        }
+        // partials: lane holds O^T[d = 16t + 4g + j][query r16]
+#pragma unroll
+        for (int tq = 0; tq < TQ; ++tq) {
+            const int qt = wave + 8 * (tq + pass);
+            if (qt >= qtiles) continue;
+            const size_t pq = ((size_t)h * a.attn_nsplit + split) * a.qpad + qt * 16 + r16;
             if (g == 0) {
-                stc(a.attn_ml + pq * 2 + 0, m_run);
-                stc(a.attn_ml + pq * 2 + 1, l_run);
+                stc(a.attn_ml + pq * 2 + 0, m_run[tq]);
+                stc(a.attn_ml + pq * 2 + 1, l_run[tq]);
             }
 #pragma unroll
             for (int t = 0; t < NDT; ++t)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) stc(a.attn_o + pq * D + 16 * t + 4 * g + jj, o[t][jj]);
+                stc4(a.attn_o, (uint32_t)((pq * D + 16 * t + 4 * g) * 4), __builtin_bit_cast(u32x4, o[tq][t]));
         }
     }
 }
@@ -697,14 +760,14 @@ __device__ __forceinline__ void merge_phase(const RoundScalars &a) {
         float M = m;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-        const float w = lane < ns ? exp2f(m - M) : 0.f;
+        const float w = lane < ns ? __builtin_amdgcn_exp2f(m - M) : 0.f;
         const float L = wave_sum(w * l);
         float acc0 = 0.f, acc1 = 0.f;
-        for (int sb = 0; sb < ns; sb += 8) {
-            float v0[8], v1[8], ws[8];
+        constexpr int MB = 16;
+        for (int sb = 0; sb < ns; sb += MB) {
+            float v0[MB], v1[MB];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                ws[q] = __shfl(w, min(sb + q, 63), 64);
+            for (int q = 0; q < MB; ++q) {
                 if (sb + q < ns) {
                     const float *src = a.attn_o + (base + (size_t)(sb + q) * a.qpad) * D;
                     v0[q] = ldc(src + lane);
@@ -712,8 +775,12 @@ __device__ __forceinline__ void merge_phase(const RoundScalars &a) {
                 }
             }
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                if (sb + q < ns) { acc0 += ws[q] * v0[q]; acc1 += ws[q] * v1[q]; }
+            for (int q = 0; q < MB; ++q)
+                if (sb + q < ns) {
+                    const float wq = __shfl(w, sb + q, 64);
+                    acc0 += wq * v0[q];
+                    acc1 += wq * v1[q];
+                }
         }
         const int r = qi / G, hq = h * G + qi % G;
         float *dst = a.O + ((size_t)r * a.nq + hq) * D;
@@ -727,14 +794,18 @@ __device__ __forceinline__ void merge_phase(const RoundScalars &a) {
 // ---------------------------------------------------------------------------
 template <int WT, bool KVF32, int D>
 __global__ __launch_bounds__(RND_THREADS, 1) void round_kernel(RoundArgs) {
-    __shared__ u32x4 lds[2048];                      // 32 KiB: GEMM activation fragments
+    // GEMM activation fragments (32 KiB) / attention K, V^T blocks (2 stages)
+    constexpr int LDS_U4 = 2 * AttnLds<KVF32, D>::STAGE > 2048 ? 2 * AttnLds<KVF32, D>::STAGE : 2048;
+    __shared__ u32x4 lds[LDS_U4];
     Prefetch pf;
     unsigned *bar;
+    unsigned long long *tr;
     unsigned gen;
-    int nl, first, last;
+    int nl, first, last, tk = 0;
     {
         const RoundScalars a = kscalars();
         bar = a.bar;
+        tr = a.trace;
         nl = a.nl; first = a.first; last = a.last;
         gen = ldc_u(a.bar + BAR_GEN + (blockIdx.x & 7) * 32);
     }
@@ -752,57 +823,71 @@ __global__ __launch_bounds__(RND_THREADS, 1) void round_kernel(RoundArgs) {
         return io;
     };
 
+    trace_mark(tr, tk);
     if (nl > 0) gemm_issue_first<WT, false>(io_make(0, 0), pf);
     if (first) {
         init_phase(kscalars());
         if (!grid_sync(bar, gen)) return;
+        trace_mark(tr, tk);
     }
     for (int l = 0; l < nl; ++l) {
         gemm_run<WT, false>(io_make(0, l), pf, lds);
         if (!grid_sync(bar, gen)) return;
+        trace_mark(tr, tk);
         {
             const RoundScalars a = kscalars();
             qkv_phase<KVF32, D>(a, klayer(l), opaque(kargs())->inv_freq, a.kc + (size_t)l * a.kv_lstride,
                                 a.vc + (size_t)l * a.kv_lstride);
         }
         if (!grid_sync(bar, gen)) return;
+        trace_mark(tr, tk);
         {
             const RoundScalars a = kscalars();
-            attn_phase<KVF32, D>(a, a.kc + (size_t)l * a.kv_lstride, a.vc + (size_t)l * a.kv_lstride);
+            attn_phase<KVF32, D>(a, a.kc + (size_t)l * a.kv_lstride, a.vc + (size_t)l * a.kv_lstride, lds);
         }
         gemm_issue_first<WT, false>(io_make(1, l), pf);
         if (!grid_sync(bar, gen)) return;
+        trace_mark(tr, tk);
         merge_phase<D>(kscalars());
         if (!grid_sync(bar, gen)) return;
+        trace_mark(tr, tk);
         gemm_run<WT, false>(io_make(1, l), pf, lds);
         gemm_issue_first<WT, true>(io_make(2, l), pf);
         if (!grid_sync(bar, gen)) return;
+        trace_mark(tr, tk);
         {
             const RoundScalars a = kscalars();
             residual_phase(a, a.p_o, klayer(l).o);
         }
         if (!grid_sync(bar, gen)) return;
+        trace_mark(tr, tk);
         gemm_run<WT, true>(io_make(2, l), pf, lds);
         gemm_issue_first<WT, false>(io_make(3, l), pf);
         if (!grid_sync(bar, gen)) return;
+        trace_mark(tr, tk);
         swiglu_phase(kscalars(), klayer(l));
         if (!grid_sync(bar, gen)) return;
+        trace_mark(tr, tk);
         gemm_run<WT, false>(io_make(3, l), pf, lds);
         if (l + 1 < nl) gemm_issue_first<WT, false>(io_make(0, l + 1), pf);
         if (!grid_sync(bar, gen)) return;
+        trace_mark(tr, tk);
         {
             const RoundScalars a = kscalars();
             residual_phase(a, a.p_d, klayer(l).d);
         }
         if (!grid_sync(bar, gen)) return;
+        trace_mark(tr, tk);
     }
     if (last) final_phase(kscalars());
+    __syncthreads();
+    trace_mark(tr, tk);
 }
 
 template <int WT, bool KVF32>
 static void launch_d(const RoundArgs &a, int nwg, hipStream_t s) {
     if (a.s.d == 64) hipLaunchKernelGGL((round_kernel<WT, KVF32, 64>), dim3(nwg), dim3(RND_THREADS), 0, s, a);
-    else hipLaunchKernelGGL((round_kernel<WT, KVF32, 128>), dim3(nwg), dim3(RND_THREADS), 0, s, a);
+    else if constexpr (!KVF32) hipLaunchKernelGGL((round_kernel<WT, KVF32, 128>), dim3(nwg), dim3(RND_THREADS), 0, s, a);
 }
 
 hipError_t round_launch(const RoundArgs &a, int nwg, hipStream_t s) {

@@ -60,7 +60,8 @@ class dflash_kv(C.Structure):
 _lib = None
 EXPORTS = ("dflash_load_weights", "dflash_free", "dflash_workspace_bytes", "dflash_ctx_features",
            "dflash_ingest_ctx", "dflash_forward_round", "dflash_forward_full", "dflash_last_error",
-           "dflash_rope_table", "dflash_prof_start", "dflash_prof_stop", "dflash_workspace_status")
+           "dflash_rope_table", "dflash_prof_start", "dflash_prof_stop", "dflash_workspace_status",
+           "dflash_prof_trace", "dflash_prof_trace_read")
 
 # kernel classes of the measurement hook (include/dflash_prof.h)
 K_GEMM_FC, K_GEMM_KV, K_GEMM_QKV, K_GEMM_O, K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN, K_ROPE, K_NORM, K_ROUND = range(1, 11)
@@ -89,6 +90,8 @@ def lib():
     L.dflash_prof_start.argtypes = [i32, i32]
     L.dflash_prof_stop.argtypes = [C.POINTER(C.c_double), C.POINTER(i32)]
     L.dflash_workspace_status.argtypes = [vp, vp, sz, vp]
+    L.dflash_prof_trace.argtypes = [i32]
+    L.dflash_prof_trace_read.argtypes = [vp, vp, sz, C.POINTER(C.c_uint64), i32, vp]
     for name in EXPORTS:
         if name not in ("dflash_free", "dflash_workspace_bytes", "dflash_last_error"):
             getattr(L, name).restype = C.c_int
@@ -168,6 +171,16 @@ def dflash_rope_table(model, half: int):
 
 def dflash_workspace_status(model, ws, ws_bytes, stream=None) -> None:
     _check(lib().dflash_workspace_status(model, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dflash_prof_trace(enable: bool) -> None:
+    _check(lib().dflash_prof_trace(1 if enable else 0))
+
+
+def dflash_prof_trace_read(model, ws, ws_bytes, n: int, stream=None):
+    buf = (C.c_uint64 * n)()
+    _check(lib().dflash_prof_trace_read(model, _ptr(ws), ws_bytes, buf, n, _stream(stream)))
+    return list(buf)
 
 
 def dflash_prof_start(kernel_class: int, max_launches: int) -> None:

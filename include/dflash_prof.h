@@ -13,6 +13,7 @@
 #ifndef DFLASH_PROF_H
 #define DFLASH_PROF_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -39,6 +40,18 @@ int dflash_prof_start(int32_t kernel_class, int32_t max_launches);
 /* Stop the timer.  Synchronises on the recorded events, then writes the
  * summed duration (ms) and the number of timed launches. */
 int dflash_prof_stop(double *total_ms, int32_t *launches);
+
+/* Phase trace of the persistent forward_round kernel.  While enabled, each
+ * later launch makes workgroup 0 record the GPU wall clock (100 MHz
+ * counter): once at kernel start, once after every grid barrier, once at the
+ * end.  The stamps go to a region of the launch's workspace.  The trace
+ * slots of one layer follow the phase order: qkv GEMM, qkv reduce,
+ * attention, merge, o GEMM, o reduce, gate|up GEMM, SwiGLU, down GEMM,
+ * down reduce.  dflash_prof_trace_read synchronises `stream` and copies the
+ * first n stamps (n <= 1024) to host memory. */
+int dflash_prof_trace(int32_t enable);
+int dflash_prof_trace_read(const struct dflash_model *m, void *ws, size_t ws_bytes, uint64_t *out, int32_t n,
+                           void *stream);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,8 @@ SMALL_BF16 = synth.DraftConfig(
     name="small_bf16", n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64,
     intermediate=768, n_taps=2, weight_dtype="bf16", kv_dtype="bf16", path="round",
     ctx=100, block=16, seed=21)
-SMALL_BF16_D128 = SMALL_BF16.replace(name="small_bf16_d128", hidden=1024, n_q_heads=8, n_kv_heads=2,
+# head_dim 128 with 16 q heads on one kv head: 256 queries per kv head, two attention passes
+SMALL_BF16_D128 = SMALL_BF16.replace(name="small_bf16_d128", hidden=1024, n_q_heads=16, n_kv_heads=1,
                                      head_dim=128, seed=22)
 
 
