@@ -22,6 +22,11 @@ SMALL_BF16 = synth.DraftConfig(
 # head_dim 128 with 16 q heads on one kv head: 256 queries per kv head, two attention passes
 SMALL_BF16_D128 = SMALL_BF16.replace(name="small_bf16_d128", hidden=1024, n_q_heads=16, n_kv_heads=1,
                                      head_dim=128, seed=22)
+# fp8 e4m3fn weights with per-row f32 scales
+SMALL_FP8 = SMALL_BF16.replace(name="small_fp8", weight_dtype="fp8", seed=23)
+SMALL_FP8_D128 = SMALL_BF16_D128.replace(name="small_fp8_d128", weight_dtype="fp8", seed=24)
+# YaRN rope (factor 32 over an original context of 8192), exercised at positions past 30000
+SMALL_YARN = SMALL_BF16_D128.replace(name="small_yarn_d128", rope_type="yarn", seed=25)
 
 
 def _setup(cfg, max_rows=16):
@@ -47,7 +52,7 @@ def test_zero_layers_final_norm():
     check("L=0 final norm", out, ref, 1e-6)
 
 
-@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_BF16_D128], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_BF16_D128, SMALL_FP8], ids=lambda c: c.name)
 @pytest.mark.parametrize("t", [1, 5, 64])
 def test_ctx_features(cfg, t):
     sw, m, dr, D = _setup(cfg, max_rows=t)
@@ -56,14 +61,15 @@ def test_ctx_features(cfg, t):
     check(f"{cfg.name} ctx_features t={t}", out, O.ctx_features(m, taps), tol_for(cfg) / 10)
 
 
-@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_BF16_D128], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_BF16_D128, SMALL_FP8, SMALL_YARN],
+                         ids=lambda c: c.name)
 def test_ingest_cache_rows(cfg):
     """Cache rows after ingesting in uneven chunks: K normed+roped, V raw, at
     the right rows and positions.  len advances by t per call."""
     sw, m, dr, D = _setup(cfg, max_rows=64)
     n = 37
     taps = synth.make_taps(cfg, n)
-    pos = synth.positions(1000, n)
+    pos = synth.positions(31000 if cfg.rope_type == "yarn" else 1000, n)
     kv = D.KVCache(cfg, 128)
     feats = dr.ctx_features(dev(taps))
     for lo, hi in ((0, 1), (1, 17), (17, 37)):
@@ -78,7 +84,8 @@ def test_ingest_cache_rows(cfg):
         check(f"{cfg.name} layer {l} cached V", v, okv.v[l], tol)
 
 
-@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_BF16_D128], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_BF16_D128, SMALL_FP8, SMALL_FP8_D128],
+                         ids=lambda c: c.name)
 @pytest.mark.parametrize("b", [16, 5, 1])
 def test_forward_full_vs_oracle(cfg, b):
     sw, m, dr, D = _setup(cfg, max_rows=cfg.ctx)
@@ -91,7 +98,7 @@ def test_forward_full_vs_oracle(cfg, b):
     check(f"{cfg.name} forward_full n={n} b={b}", out, ref, tol_for(cfg))
 
 
-@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_FP8], ids=lambda c: c.name)
 def test_round_equals_full_bitwise(cfg):
     """[DflashDraft] forward_round: bit-class-identical to the fresh forward.
     On the GPU the two run the same kernels, so they must agree bit for bit,
@@ -113,14 +120,14 @@ def test_round_equals_full_bitwise(cfg):
     assert torch.equal(r1, r2), "forward_round is not deterministic"
 
 
-@pytest.mark.parametrize("cfg", [SMALL_BF16], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_FP8_D128, SMALL_YARN], ids=lambda c: c.name)
 def test_multi_round_append_then_round(cfg):
     """Several rounds: each ingests 16 committed rows, then drafts; every
     round matches the oracle's cached path."""
     sw, m, dr, D = _setup(cfg, max_rows=64)
     kv = D.KVCache(cfg, 256)
     okv = O.OracleKV(cfg)
-    p = 0
+    p = 30000 if cfg.rope_type == "yarn" else 0     # YaRN: positions far past the original context
     for rnd, t in enumerate((40, 16, 16, 3)):
         taps = synth.make_taps(cfg, t, stream=100 + rnd)
         pos = synth.positions(p, t)
