@@ -476,8 +476,11 @@ __device__ __forceinline__ void final_phase(const RoundScalars &a) {
 }
 
 // qkv reduce: input-norm row scale, q/k head RMSNorm + rope (+ mscale), stores.
+// The per-matrix pointers come in as separate values: selecting among members
+// of a layer struct at run time would put the struct in scratch memory.
 template <bool KVF32, int D>
-__device__ __forceinline__ void qkv_phase(const RoundScalars &a, const LayerRefs &L, KDouble *inv_freq, char *kc, char *vc) {
+__device__ __forceinline__ void qkv_phase(const RoundScalars &a, const float *sq, const float *sk, const float *sv,
+                                          const float *g_q, const float *g_k, KDouble *inv_freq, char *kc, char *vc) {
     constexpr int HALF = D / 2;
     const int lane = threadIdx.x & 63;
     const int nh = a.nq + 2 * a.nkv;
@@ -509,9 +512,9 @@ __device__ __forceinline__ void qkv_phase(const RoundScalars &a, const LayerRefs
             for (int q = 0; q < 8; ++q)
                 if (wb + q <= w1) { x0 += v0[q]; x1 += v1[q]; }
         }
-        const MatRef &M = kind == 0 ? L.q : kind == 1 ? L.k : L.v;
-        x0 *= rs * col_scale(M, hh * D + j);
-        x1 *= rs * col_scale(M, hh * D + j + HALF);
+        const float *msc = kind == 0 ? sq : kind == 1 ? sk : sv;   // fp8 row scales, or null
+        x0 *= rs * (msc ? msc[hh * D + j] : 1.f);
+        x1 *= rs * (msc ? msc[hh * D + j + HALF] : 1.f);
         if (!act) { x0 = 0.f; x1 = 0.f; }
         const size_t crow = (size_t)(a.len + r);
         if (kind == 2) {
@@ -529,7 +532,7 @@ __device__ __forceinline__ void qkv_phase(const RoundScalars &a, const LayerRefs
         }
         const float ss = wave_sum(x0 * x0 + x1 * x1);
         const float inv = 1.f / sqrtf(ss / (float)D + a.eps);
-        const float *gain = kind == 0 ? L.g_q : L.g_k;
+        const float *gain = kind == 0 ? g_q : g_k;
         if (act) {
             const float y0 = gain[j] * (x0 * inv), y1 = gain[j + HALF] * (x1 * inv);
             double sv, cv;
@@ -836,8 +839,9 @@ __global__ __launch_bounds__(RND_THREADS, 1) void round_kernel(RoundArgs) {
         trace_mark(tr, tk);
         {
             const RoundScalars a = kscalars();
-            qkv_phase<KVF32, D>(a, klayer(l), opaque(kargs())->inv_freq, a.kc + (size_t)l * a.kv_lstride,
-                                a.vc + (size_t)l * a.kv_lstride);
+            const LayerRefs L = klayer(l);
+            qkv_phase<KVF32, D>(a, L.q.s, L.k.s, L.v.s, L.g_q, L.g_k, opaque(kargs())->inv_freq,
+                                a.kc + (size_t)l * a.kv_lstride, a.vc + (size_t)l * a.kv_lstride);
         }
         if (!grid_sync(bar, gen)) return;
         trace_mark(tr, tk);
