@@ -77,7 +77,7 @@ constexpr int MAX_ATTN_SPLITS = 64;
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct WsLayout {
-    size_t x, xn, qkv, q, o, z, feats, part_o, part_ml, gpart, gcnt, bar, ssq, rpart, trace, total;
+    size_t x, xn, qkv, q, o, z, feats, part_o, part_ml, gpart, gcnt, bar, ssq, rpart, trace, d2a, d2m, d2r, total;
 };
 
 WsLayout ws_layout(const dflash_cfg &c, int max_rows) {
@@ -102,6 +102,9 @@ WsLayout ws_layout(const dflash_cfg &c, int max_rows) {
     L.gpart = take(4 * dfl::GEMM_PART_FLOATS);
     L.ssq = take(4 * (H / 128) * MAX_BLOCK);
     L.rpart = take(4 * (size_t)dfl::MAX_NWG * dfl::MAXSLOT * MAX_BLOCK * 256);
+    L.d2a = take(4 * MAX_BLOCK * 4 * dfl::RND_MAX_D2);
+    L.d2m = take(4 * MAX_BLOCK * 4 * dfl::RND_MAX_D2);
+    L.d2r = take(4 * MAX_BLOCK);
     // row-dependent regions
     size_t qkv_rows = MAX_BLOCK * (qd + 2 * kvd), ing = rows * 2 * kvd;
     L.qkv = take(4 * (qkv_rows > ing ? qkv_rows : ing));
@@ -152,7 +155,11 @@ int check_cfg(const dflash_cfg &c) {
     if (!ok_types) return fail(DFLASH_E_UNSUPPORTED, "weight/kv dtype combination %d/%d not built", c.weight_dtype, c.kv_dtype);
     if (c.kv_dtype == DFLASH_F32 && c.head_dim != 64) return fail(DFLASH_E_UNSUPPORTED, "an f32 KV cache is built for head_dim 64 only");
     if (c.d2_groups < 0) return fail(DFLASH_E_INVAL, "d2_groups must be >= 0");
-    if (c.d2_groups > 0) return fail(DFLASH_E_UNSUPPORTED, "the DFlash2 conv wrap is not built yet");
+    if (c.d2_groups > 0) {
+        if (c.d2_groups > dfl::RND_MAX_D2 || c.hidden % c.d2_groups || (c.hidden / c.d2_groups) % 8)
+            return fail(DFLASH_E_UNSUPPORTED, "d2_groups %d: built for G <= %d with hidden/G a multiple of 8", c.d2_groups,
+                        dfl::RND_MAX_D2);
+    }
     return DFLASH_OK;
 }
 
@@ -320,6 +327,8 @@ hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *no
     a.p_gu = plan_gemm(a.I, a.H, a.wt, nwg);
     a.p_d = plan_gemm(a.H, a.I, a.wt, nwg);
     if (!plan_ok(a.p_qkv) || !plan_ok(a.p_o) || !plan_ok(a.p_gu) || !plan_ok(a.p_d)) return hipErrorInvalidValue;
+    a.d2 = c.d2_groups;
+    a.d2_Da = at<float>(ws, L.d2a); a.d2_Dm = at<float>(ws, L.d2m); a.d2_rinv = at<float>(ws, L.d2r);
     memcpy(ra.inv_freq, m->inv_freq, sizeof ra.inv_freq);
     int l0 = 0;
     do {
@@ -335,6 +344,10 @@ hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *no
             R.q = mref(W.wq, a.qd); R.k = mref(W.wk, a.kvd); R.v = mref(W.wv, a.kvd);
             R.o = mref(W.wo, a.H); R.g = mref(W.wg, a.I); R.u = mref(W.wu, a.I); R.d = mref(W.wd, a.H);
             R.g_in = W.g_in; R.g_post = W.g_post; R.g_q = W.g_q; R.g_k = W.g_k;
+            if (c.d2_groups > 0) {
+                R.aw = mref(W.attn_w_dyn, 4 * c.d2_groups); R.mw = mref(W.mlp_w_dyn, 4 * c.d2_groups);
+                R.abase = W.attn_base; R.mbase = W.mlp_base;
+            }
         }
         hipError_t e;
         {
@@ -372,6 +385,11 @@ int dflash_load_weights(const dflash_cfg *cfg, const dflash_weights *w, dflash_m
         if ((rc = check_vec(L.g_in, "g_in", l)) || (rc = check_vec(L.g_post, "g_post", l)) ||
             (rc = check_vec(L.g_q, "g_q", l)) || (rc = check_vec(L.g_k, "g_k", l)))
             return rc;
+        if (c.d2_groups > 0) {
+            if ((rc = check_matrix(c, L.attn_w_dyn, "attn_w_dyn", l)) || (rc = check_matrix(c, L.mlp_w_dyn, "mlp_w_dyn", l)) ||
+                (rc = check_vec(L.attn_base, "attn_base", l)) || (rc = check_vec(L.mlp_base, "mlp_base", l)))
+                return rc;
+        }
     }
     dflash_model *m = new dflash_model{};
     m->cfg = c;

@@ -29,7 +29,9 @@ struct GemmPlanDev {
 
 struct LayerRefs {
     MatRef q, k, v, o, g, u, d;
+    MatRef aw, mw;                   // DFlash2 dynamic-kernel projections [4G][H] (attention, MLP)
     const float *g_in, *g_post, *g_q, *g_k;
+    const float *abase, *mbase;      // DFlash2 static taps f32 [2][H][2]
 };
 
 // Scalars of a launch (kept in registers by value).
@@ -50,8 +52,12 @@ struct RoundScalars {
     unsigned *bar;
     unsigned long long *trace;       // phase timestamps (workgroup 0), or nullptr
     GemmPlanDev p_qkv, p_o, p_gu, p_d;
+    int d2;                          // DFlash2 conv groups G (0: no conv wrap)
+    float *d2_Da, *d2_Dm;            // per-row dynamic coefficients [16][4G] (attention, MLP)
+    float *d2_rinv;                  // 1/rms of the rows the last coefficient phase normalised [16]
 };
 constexpr int RND_TRACE_WORDS = 1024;
+constexpr int RND_MAX_D2 = 64;       // DFlash2 groups G: 4G coefficients per row
 
 // Kernel arguments.  The arrays are indexed at run time, so the kernel reads
 // them in place from the kernel-argument segment.

@@ -132,6 +132,7 @@ __device__ __forceinline__ LayerRefs klayer(int l) {
     L.q = kmat(ka->L[l].q); L.k = kmat(ka->L[l].k); L.v = kmat(ka->L[l].v); L.o = kmat(ka->L[l].o);
     L.g = kmat(ka->L[l].g); L.u = kmat(ka->L[l].u); L.d = kmat(ka->L[l].d);
     L.g_in = ka->L[l].g_in; L.g_post = ka->L[l].g_post; L.g_q = ka->L[l].g_q; L.g_k = ka->L[l].g_k;
+    L.aw = kmat(ka->L[l].aw); L.mw = kmat(ka->L[l].mw); L.abase = ka->L[l].abase; L.mbase = ka->L[l].mbase;
     return L;
 }
 
@@ -208,6 +209,13 @@ struct GemmIO {
     const float *gain;       // [K] multiplies A while staging, or nullptr
     int rows;
     float *part;             // partial slots [NWG][MAXSLOT][16][PW]
+    // DFlash2 prepare conv applied while staging (G > 0, K = hidden): the
+    // staged row r is (base[c,0] + D[r,g(c),0]) xn[r-1] + (base[c,1] + D[r,g(c),1]) xn[r]
+    // with xn[r] = A[r] * gain * rinv[r] and xn[-1] = 0.
+    int G;
+    const float *cD;         // coefficients [16][4G], half 0 used here
+    const float *cbase;      // static taps [2][K][2], half 0 used here
+    const float *crinv;      // [16]
 };
 
 __device__ __forceinline__ void unit_range(const GemmPlanDev &p, int &u0, int &n) {
@@ -285,7 +293,7 @@ __device__ __forceinline__ void stage_units(const GemmIO &io, int u0, int n, u32
     constexpr int KS = KT<WT>::KS, FR = KT<WT>::FR;
     constexpr int G8 = KS / 8;                          // 8-float groups per row and unit
     const int total = n * 16 * G8;                      // <= 2 * RND_THREADS
-    u32x4 v[2][2];
+    u32x4 v[2][2], vp[2][2];
     int kk[2], ii[2], rr[2], jj[2];
     bool live[2];
 #pragma unroll
@@ -302,6 +310,10 @@ __device__ __forceinline__ void stage_units(const GemmIO &io, int u0, int n, u32
             const uint32_t off = (uint32_t)(((size_t)row * io.p.K + kk[t]) * 4);
             v[t][0] = ldc4(io.A, off);
             v[t][1] = ldc4(io.A, off + 16);
+            if (io.G && row > 0) {
+                vp[t][0] = ldc4(io.A, off - (uint32_t)io.p.K * 4);
+                vp[t][1] = ldc4(io.A, off - (uint32_t)io.p.K * 4 + 16);
+            }
         }
     }
 #pragma unroll
@@ -316,6 +328,28 @@ __device__ __forceinline__ void stage_units(const GemmIO &io, int u0, int n, u32
                 const float4 g0 = ld_f4(io.gain + kk[t]), g1 = ld_f4(io.gain + kk[t] + 4);
                 x[0] *= g0.x; x[1] *= g0.y; x[2] *= g0.z; x[3] *= g0.w;
                 x[4] *= g1.x; x[5] *= g1.y; x[6] *= g1.z; x[7] *= g1.w;
+                if (io.G) {
+                    // 8 consecutive channels share one group (K / G is a multiple of 8)
+                    const int grp = kk[t] * io.G / io.p.K;
+                    const float rr_ = ldc(io.crinv + row), rp = row > 0 ? ldc(io.crinv + row - 1) : 0.f;
+                    const float d0 = ldc(io.cD + row * 4 * io.G + 2 * grp), d1 = ldc(io.cD + row * 4 * io.G + 2 * grp + 1);
+                    float xp[8];
+                    if (row > 0) {
+                        xp[0] = f_of(vp[t][0].x); xp[1] = f_of(vp[t][0].y); xp[2] = f_of(vp[t][0].z); xp[3] = f_of(vp[t][0].w);
+                        xp[4] = f_of(vp[t][1].x); xp[5] = f_of(vp[t][1].y); xp[6] = f_of(vp[t][1].z); xp[7] = f_of(vp[t][1].w);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) xp[q] = 0.f;
+                    }
+                    const float gq[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+                    for (int q = 0; q < 8; q += 2) {
+                        const float4 b = ld_f4(io.cbase + (size_t)(kk[t] + q) * 2);   // taps of channels c, c+1
+                        const float p0 = xp[q] * gq[q] * rp, p1 = xp[q + 1] * gq[q + 1] * rp;
+                        x[q] = (b.x + d0) * p0 + (b.y + d1) * (x[q] * rr_);
+                        x[q + 1] = (b.z + d0) * p1 + (b.w + d1) * (x[q + 1] * rr_);
+                    }
+                }
             }
         } else {
 #pragma unroll
@@ -433,14 +467,28 @@ __device__ __forceinline__ void init_phase(const RoundScalars &a) {
     }
 }
 
-// X += sum of partials (+ fp8 column scale); slice sums of squares.
-__device__ __forceinline__ void residual_phase(const RoundScalars &a, const GemmPlanDev &p, const MatRef &m) {
+// X += y (+ fp8 column scale); slice sums of squares.  y is the sum of the
+// partials, or with a DFlash2 wrap (cD != nullptr) the finish conv of it:
+// y'[r,c] = (base1[c,0] + D[r,1,g(c),0]) y[r-1,c] + (base1[c,1] + D[r,1,g(c),1]) y[r,c].
+__device__ __forceinline__ void residual_phase(const RoundScalars &a, const GemmPlanDev &p, const MatRef &m,
+                                               const float *cD = nullptr, const float *base1 = nullptr) {
     const int lane = threadIdx.x & 63, ng = a.H / 128;
     for (int it = gwave(); it < ng * a.b; it += nwaves()) {
         const int grp = it % ng, r = it / ng, cl = 2 * lane, c = grp * 128 + cl;
         float2 s = sum_slots2(p, a.part, grp, r, cl, 128);
         const u32x2 xo = ldc2(a.X, (uint32_t)(((size_t)r * a.H + c) * 4));
-        const float x0 = f_of(xo.x) + s.x * col_scale(m, c), x1 = f_of(xo.y) + s.y * col_scale(m, c + 1);
+        float y0 = s.x * col_scale(m, c), y1 = s.y * col_scale(m, c + 1);
+        if (cD) {
+            float2 sp = make_float2(0.f, 0.f);
+            if (r > 0) sp = sum_slots2(p, a.part, grp, r - 1, cl, 128);
+            const float p0 = sp.x * col_scale(m, c), p1 = sp.y * col_scale(m, c + 1);
+            const int gi = c * a.d2 / a.H;
+            const float d0 = ldc(cD + r * 4 * a.d2 + 2 * (a.d2 + gi)), d1 = ldc(cD + r * 4 * a.d2 + 2 * (a.d2 + gi) + 1);
+            const float4 bb = ld_f4(base1 + (size_t)c * 2);
+            y0 = (bb.x + d0) * p0 + (bb.y + d1) * y0;
+            y1 = (bb.z + d0) * p1 + (bb.w + d1) * y1;
+        }
+        const float x0 = f_of(xo.x) + y0, x1 = f_of(xo.y) + y1;
         stc2f(a.X, (size_t)r * a.H + c, x0, x1);
         const float ss = wave_sum(x0 * x0 + x1 * x1);
         if (lane == 0) stc(a.ssq + grp * 16 + r, ss);
@@ -449,12 +497,58 @@ __device__ __forceinline__ void residual_phase(const RoundScalars &a, const Gemm
 
 __device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
 
+// four consecutive weights of one row, widened to f32
+template <int WT>
+__device__ __forceinline__ float4 ld_w4(const void *w, size_t idx) {
+    if constexpr (WT == WT_F32) {
+        return ld_f4(reinterpret_cast<const float *>(w) + idx);
+    } else if constexpr (WT == WT_BF16) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(w) + idx);
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    } else {
+        const uint32_t u = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(w) + idx);
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(u, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(u, true);
+        return make_float4(lo[0], lo[1], hi[0], hi[1]);
+    }
+}
+
+// DFlash2 coefficients of a sublayer: D[r][j] = rinv[r] * s_j * sum_c X[r,c] g[c] W[j,c]
+// (the projection of the normalised rows, j over [half][group][tap]), and
+// rinv[r] = 1/rms(X[r]).  One wave per (row, 8 consecutive j).
+template <int WT>
+__device__ __forceinline__ void d2_phase(const RoundScalars &a, const MatRef &w, const float *gain, float *Dout) {
+    const int lane = threadIdx.x & 63;
+    const int nj = 4 * a.d2, njb = nj / 8;
+    for (int it = gwave(); it < a.b * njb; it += nwaves()) {
+        const int r = it / njb, j0 = (it - r * njb) * 8;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int c = lane * 4; c < a.H; c += 256) {
+            const u32x4 xv = ldc4(a.X, (uint32_t)(((size_t)r * a.H + c) * 4));
+            const float4 g = ld_f4(gain + c);
+            const float x0 = f_of(xv.x) * g.x, x1 = f_of(xv.y) * g.y, x2 = f_of(xv.z) * g.z, x3 = f_of(xv.w) * g.w;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float4 wv = ld_w4<WT>(w.w, (size_t)(j0 + q) * a.H + c);
+                acc[q] += x0 * wv.x + x1 * wv.y + x2 * wv.z + x3 * wv.w;
+            }
+        }
+        const float rs = inv_rms_row(a, r);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float v = wave_sum(acc[q]);
+            if (lane == q) stc(Dout + r * nj + j0 + q, v * rs * (w.s ? w.s[j0 + q] : 1.f));
+        }
+        if (j0 == 0 && lane == 0) stc(a.d2_rinv + r, rs);
+    }
+}
+
 // Z = silu(s * gate) * (s * up), s = 1/rms(X) (the post-attention norm's row scale)
 __device__ __forceinline__ void swiglu_phase(const RoundScalars &a, const LayerRefs &L) {
     const int lane = threadIdx.x & 63, ng = a.I / 128;
     for (int it = gwave(); it < ng * a.b; it += nwaves()) {
         const int grp = it % ng, r = it / ng, cl = 2 * lane, c = grp * 128 + cl;
-        const float rs = inv_rms_row(a, r);
+        const float rs = a.d2 ? 1.f : inv_rms_row(a, r);      // the conv staging already normalised the rows
         const float2 gs = sum_slots2(a.p_gu, a.part, grp, r, cl, 256);
         const float2 us = sum_slots2(a.p_gu, a.part, grp, r, 128 + cl, 256);
         const float g0 = gs.x * rs * col_scale(L.g, c), g1 = gs.y * rs * col_scale(L.g, c + 1);
@@ -492,7 +586,7 @@ __device__ __forceinline__ void qkv_phase(const RoundScalars &a, const float *sq
         const int hh = kind == 0 ? h : kind == 1 ? h - a.nq : h - a.nq - a.nkv;
         const int col0 = kind == 0 ? hh * D : kind == 1 ? a.qd + hh * D : a.qd + a.kvd + hh * D;
         const int grp = col0 / 128, cin = col0 % 128;
-        const float rs = inv_rms_row(a, r);
+        const float rs = a.d2 ? 1.f : inv_rms_row(a, r);      // the conv staging already normalised the rows
         // partials for columns (j, j + HALF) of the head
         const int w0 = (grp * a.p_qkv.steps) / a.p_qkv.upw, w1 = ((grp + 1) * a.p_qkv.steps - 1) / a.p_qkv.upw;
         float x0 = 0.f, x1 = 0.f;
@@ -819,10 +913,13 @@ __global__ __launch_bounds__(RND_THREADS, 1) void round_kernel(RoundArgs) {
         const LayerRefs L = klayer(l);
         GemmIO io;
         io.rows = a.b; io.part = a.part;
+        io.G = 0; io.cD = nullptr; io.cbase = nullptr; io.crinv = a.d2_rinv;
         if (which == 0) { io.p = a.p_qkv; io.s0 = L.q; io.s1 = L.k; io.s2 = L.v; io.A = a.X; io.gain = L.g_in; }
         else if (which == 1) { io.p = a.p_o; io.s0 = L.o; io.s1 = none; io.s2 = none; io.A = a.O; io.gain = nullptr; }
         else if (which == 2) { io.p = a.p_gu; io.s0 = L.g; io.s1 = L.u; io.s2 = none; io.A = a.X; io.gain = L.g_post; }
         else { io.p = a.p_d; io.s0 = L.d; io.s1 = none; io.s2 = none; io.A = a.Z; io.gain = nullptr; }
+        if (a.d2 && which == 0) { io.G = a.d2; io.cD = a.d2_Da; io.cbase = L.abase; }
+        if (a.d2 && which == 2) { io.G = a.d2; io.cD = a.d2_Dm; io.cbase = L.mbase; }
         return io;
     };
 
@@ -833,7 +930,15 @@ __global__ __launch_bounds__(RND_THREADS, 1) void round_kernel(RoundArgs) {
         if (!grid_sync(bar, gen)) return;
         trace_mark(tr, tk);
     }
+    const int d2 = kscalars().d2;
     for (int l = 0; l < nl; ++l) {
+        if (d2) {                                   // DFlash2: attention prepare coefficients
+            const RoundScalars a = kscalars();
+            const LayerRefs L = klayer(l);
+            d2_phase<WT>(a, L.aw, L.g_in, a.d2_Da);
+            if (!grid_sync(bar, gen)) return;
+            trace_mark(tr, tk);
+        }
         gemm_run<WT, false>(io_make(0, l), pf, lds);
         if (!grid_sync(bar, gen)) return;
         trace_mark(tr, tk);
@@ -861,10 +966,19 @@ __global__ __launch_bounds__(RND_THREADS, 1) void round_kernel(RoundArgs) {
         trace_mark(tr, tk);
         {
             const RoundScalars a = kscalars();
-            residual_phase(a, a.p_o, klayer(l).o);
+            const LayerRefs L = klayer(l);
+            if (a.d2) residual_phase(a, a.p_o, L.o, a.d2_Da, L.abase + 2 * (size_t)a.H);
+            else residual_phase(a, a.p_o, L.o);
         }
         if (!grid_sync(bar, gen)) return;
         trace_mark(tr, tk);
+        if (d2) {                                   // DFlash2: MLP prepare coefficients
+            const RoundScalars a = kscalars();
+            const LayerRefs L = klayer(l);
+            d2_phase<WT>(a, L.mw, L.g_post, a.d2_Dm);
+            if (!grid_sync(bar, gen)) return;
+            trace_mark(tr, tk);
+        }
         gemm_run<WT, true>(io_make(2, l), pf, lds);
         gemm_issue_first<WT, false>(io_make(3, l), pf);
         if (!grid_sync(bar, gen)) return;
@@ -878,7 +992,9 @@ __global__ __launch_bounds__(RND_THREADS, 1) void round_kernel(RoundArgs) {
         trace_mark(tr, tk);
         {
             const RoundScalars a = kscalars();
-            residual_phase(a, a.p_d, klayer(l).d);
+            const LayerRefs L = klayer(l);
+            if (a.d2) residual_phase(a, a.p_d, L.d, a.d2_Dm, L.mbase + 2 * (size_t)a.H);
+            else residual_phase(a, a.p_d, L.d);
         }
         if (!grid_sync(bar, gen)) return;
         trace_mark(tr, tk);

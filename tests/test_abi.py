@@ -66,12 +66,15 @@ class FakeWeights:
                 setattr(lw, n, mat(f"{n}"))
             for n in ("g_in", "g_post", "g_q", "g_k"):
                 setattr(lw, n, ptr(n))
+            if cfg.d2_groups:
+                lw.attn_w_dyn, lw.mlp_w_dyn = mat("attn_w_dyn"), mat("mlp_w_dyn")
+                lw.attn_base, lw.mlp_base = ptr("attn_base"), ptr("mlp_base")
         self.struct = D.dflash_weights(fc=mat("fc"), g_hidden_norm=ptr("g_hidden_norm"), g_norm=ptr("g_norm"),
                                        layers=self.layers)
 
 
-@pytest.mark.parametrize("cfg", [synth.TINY_F32, synth.FULL5_BF16, synth.ROUND8_BF16, synth.ROUND8_YARN],
-                         ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [synth.TINY_F32, synth.FULL5_BF16, synth.ROUND8_BF16, synth.ROUND8_YARN,
+                                 synth.ROUND8_FP8_D2], ids=lambda c: c.name)
 def test_load_weights_and_rope_tables_match_oracle(D, cfg):
     fw = FakeWeights(D, cfg)
     m = D.dflash_load_weights(D.make_cfg(cfg), fw.struct)
@@ -91,7 +94,8 @@ def test_load_weights_and_rope_tables_match_oracle(D, cfg):
     (dict(hidden=300), 3), (dict(head_dim=96), 3), (dict(n_q_heads=6, n_kv_heads=4), 1),
     (dict(n_q_heads=64, n_kv_heads=2), 3), (dict(rms_eps=0.0), 1), (dict(rope_base=1.0), 1),
     (dict(weight_dtype="fp8", kv_dtype="f32"), 3), (dict(weight_dtype="f32", kv_dtype="bf16"), 3),
-    (dict(n_layers=-1), 1),
+    (dict(n_layers=-1), 1), (dict(d2_groups=-1), 1), (dict(d2_groups=3), 3), (dict(d2_groups=128), 3),
+    (dict(d2_groups=512), 3),
 ])
 def test_bad_configs_rejected(D, change, code):
     cfg = synth.ROUND8_BF16.replace(**change)
@@ -106,6 +110,15 @@ def test_bad_configs_rejected(D, change, code):
 def test_bad_weight_pointers_rejected(D, misalign, null):
     cfg = synth.TINY_F32
     fw = FakeWeights(D, cfg, misalign=misalign, null=null)
+    with pytest.raises(D.DflashError) as ei:
+        D.dflash_load_weights(D.make_cfg(cfg), fw.struct)
+    assert ei.value.code == D.DFLASH_E_INVAL
+
+
+@pytest.mark.parametrize("null", ["attn_base", "mlp_w_dyn"])
+def test_d2_weights_required(D, null):
+    cfg = synth.ROUND8_FP8_D2
+    fw = FakeWeights(D, cfg, null=null)
     with pytest.raises(D.DflashError) as ei:
         D.dflash_load_weights(D.make_cfg(cfg), fw.struct)
     assert ei.value.code == D.DFLASH_E_INVAL

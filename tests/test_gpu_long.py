@@ -1,7 +1,11 @@
-"""GPU parity at long context: the 8-layer bf16 drafter with YaRN rope
-(factor 32), one cached round at ctx 32768 per sequence, in the launch
-configuration of the multi-sequence benchmark (one forward_round call per
-sequence, each on its own cache, back to back).
+"""GPU parity at long context.
+
+* The 8-layer bf16 drafter with YaRN rope (factor 32), one cached round at
+  ctx 32768 per sequence, in the launch configuration of the multi-sequence
+  benchmark (one forward_round call per sequence, each on its own cache,
+  back to back).
+* The 8-layer fp8 e4m3fn drafter (per-row f32 scales) with the DFlash2 conv
+  wrap (G = 16) around every sublayer, one cached round at ctx 65536.
 
 The oracle cannot ingest 32,752 rows per sequence in reasonable time, so each
 cache is prefilled directly with the same seeded bf16 K/V on both sides; the
@@ -103,3 +107,46 @@ def test_c4_eight_sequences_reproducible(c4):
         print(f"[c4] sweep seq {seq} ok", flush=True)
     for s in range(1, len(outs)):
         assert not np.array_equal(outs[0], outs[s])
+
+
+def test_c5_fp8_d2conv_round_matches_oracle():
+    """fp8 weights + DFlash2 conv at ctx 65536: the full round against the
+    oracle on a directly prefilled cache, plus the argmax check and a bitwise
+    repeat."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from block_diffusion_drafter_round_amd import dflash as D
+    cfg = synth.ROUND8_FP8_D2
+    sw = synth.make_weights(cfg)
+    m = O.OracleModel(sw)
+    dr = D.Drafter(sw, max_rows=64)
+    ctx, t, b = cfg.ctx, cfg.new_rows, cfg.block
+    base = ctx - t
+    ks, vs = synth.make_prefill_kv(cfg, base)
+    print(f"[c5] prefilled {base} rows", flush=True)
+    kv, out = _gpu_round(cfg, dr, D, ks, vs, 0)
+    dr.status()
+    kv.len = base
+    taps, noise, pos_new, pos_blk = _round_inputs(cfg, 0)
+    dr.ingest_ctx(kv, dr.ctx_features(dev(taps)), dev(pos_new))
+    out2 = host(dr.forward_round(kv, dev(noise), dev(pos_blk)))
+    assert np.array_equal(out, out2), "c5 round is not bitwise deterministic"
+
+    okv = O.OracleKV(cfg)
+    okv.prefill(ks, vs)
+    del ks, vs
+    O.ingest_ctx(m, okv, O.ctx_features(m, taps), pos_new)
+    k, v = kv_rows_f64(kv, cfg.n_layers - 1, base, ctx)
+    check("c5 last layer ingested K", k, okv.k[cfg.n_layers - 1][base:], 1e-2)
+    check("c5 last layer ingested V", v, okv.v[cfg.n_layers - 1][base:], 1e-2)
+    ref = O.forward_round(m, okv, noise, pos_blk)
+    check(f"c5 fp8 + DFlash2 conv forward_round ctx {ctx}", out, ref, tol_for(cfg))
+
+    lm = synth.make_lm_head(cfg).astype(np.float64)
+    am_o, lo_o = O.lm_argmax(ref, lm)
+    am_g, lo_g = O.lm_argmax(out, lm)
+    pert = np.abs(lo_g - lo_o).max(axis=1)
+    mism = [(r, am_g[r], am_o[r]) for r in range(b) if am_g[r] != am_o[r]]
+    real = [x for x in mism if lo_o[x[0], x[2]] - lo_o[x[0], x[1]] > pert[x[0]]]
+    print(f"[c5] argmax mismatches: {len(mism)} (beyond perturbation: {len(real)})", flush=True)
+    assert not real, real

@@ -27,6 +27,11 @@ SMALL_FP8 = SMALL_BF16.replace(name="small_fp8", weight_dtype="fp8", seed=23)
 SMALL_FP8_D128 = SMALL_BF16_D128.replace(name="small_fp8_d128", weight_dtype="fp8", seed=24)
 # YaRN rope (factor 32 over an original context of 8192), exercised at positions past 30000
 SMALL_YARN = SMALL_BF16_D128.replace(name="small_yarn_d128", rope_type="yarn", seed=25)
+# DFlash2 conv wrap around every sublayer: f32 (G = 2), bf16 (G = 4), fp8 head_dim 128 (G = 16)
+TINY_F32_D2 = synth.TINY_F32.replace(name="tiny_f32_d2", d2_groups=2, seed=26)
+SMALL_D2 = SMALL_BF16.replace(name="small_bf16_d2", d2_groups=4, seed=27)
+SMALL_FP8_D2 = SMALL_FP8_D128.replace(name="small_fp8_d128_d2", d2_groups=16, seed=28)
+D2_CFGS = [TINY_F32_D2, SMALL_D2, SMALL_FP8_D2]
 
 
 def _setup(cfg, max_rows=16):
@@ -84,7 +89,7 @@ def test_ingest_cache_rows(cfg):
         check(f"{cfg.name} layer {l} cached V", v, okv.v[l], tol)
 
 
-@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_BF16_D128, SMALL_FP8, SMALL_FP8_D128],
+@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_BF16_D128, SMALL_FP8, SMALL_FP8_D128] + D2_CFGS,
                          ids=lambda c: c.name)
 @pytest.mark.parametrize("b", [16, 5, 1])
 def test_forward_full_vs_oracle(cfg, b):
@@ -98,7 +103,7 @@ def test_forward_full_vs_oracle(cfg, b):
     check(f"{cfg.name} forward_full n={n} b={b}", out, ref, tol_for(cfg))
 
 
-@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_FP8], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_FP8, SMALL_D2], ids=lambda c: c.name)
 def test_round_equals_full_bitwise(cfg):
     """[DflashDraft] forward_round: bit-class-identical to the fresh forward.
     On the GPU the two run the same kernels, so they must agree bit for bit,
@@ -120,7 +125,7 @@ def test_round_equals_full_bitwise(cfg):
     assert torch.equal(r1, r2), "forward_round is not deterministic"
 
 
-@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_FP8_D128, SMALL_YARN], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_FP8_D128, SMALL_YARN, SMALL_FP8_D2], ids=lambda c: c.name)
 def test_multi_round_append_then_round(cfg):
     """Several rounds: each ingests 16 committed rows, then drafts; every
     round matches the oracle's cached path."""
@@ -138,6 +143,32 @@ def test_multi_round_append_then_round(cfg):
         bpos = synth.positions(p, cfg.block)
         out = host(dr.forward_round(kv, dev(noise), dev(bpos)))
         check(f"{cfg.name} round {rnd} len={p}", out, O.forward_round(m, okv, noise, bpos), tol_for(cfg))
+
+
+def test_d2_identity_taps_equal_backbone():
+    """DFlash2 special case: with zero dynamic projections and static taps
+    [0, 1] the wrap is the identity, so the output equals the same weights
+    without the wrap (the conv path and the plain path run different code).
+    The two agree to rounding only: the conv path splits the normalised rows
+    x*g/rms into bf16 hi + lo halves (about 16 significant bits, ~1e-5
+    relative) before the GEMM, the plain path splits x*g and scales after, so
+    they round different values; 1e-4 bounds that over two layers."""
+    from block_diffusion_drafter_round_amd import dflash as D
+    cfg = SMALL_D2
+    sw = synth.make_weights(cfg)
+    for l in range(cfg.n_layers):
+        for sub in ("attn", "mlp"):
+            w = sw.layers[l][f"{sub}.w_dyn"]
+            w.data[...] = 0
+            base = sw.layers[l][f"{sub}.base"]
+            base[..., 0] = 0.0
+            base[..., 1] = 1.0
+    plain = synth.StoredWeights(cfg.replace(d2_groups=0), sw.fc, sw.g_hidden_norm, sw.g_norm, sw.layers)
+    n, b = cfg.ctx, cfg.block
+    taps, noise, pos = synth.make_taps(cfg, n), synth.make_noise(cfg), synth.positions(0, n + b)
+    o_d2 = host(D.Drafter(sw, max_rows=n).forward_full(dev(taps), dev(noise), dev(pos)))
+    o_plain = host(D.Drafter(plain, max_rows=n).forward_full(dev(taps), dev(noise), dev(pos)))
+    check("d2 identity taps vs plain backbone", o_d2, o_plain, 1e-4)
 
 
 def test_errors_leave_state_unchanged():
