@@ -506,8 +506,11 @@ int dflash_workspace_status(const dflash_model *m, void *ws, size_t ws_bytes, vo
     if (e == hipSuccess) e = hipMemcpy(&h, err, sizeof h, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "workspace_status");
     if (h != 0) {
-        const unsigned zero = 0;
-        hipMemcpy(err, &zero, sizeof zero, hipMemcpyHostToDevice);
+        // the barrier counters are inconsistent after a timed-out barrier: start them over
+        unsigned *bar = at<unsigned>(ws, L.bar);
+        e = hipMemset(bar, 0, sizeof(unsigned) * dfl::BAR_WORDS);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e, "workspace_status");
         return fail(DFLASH_E_HIP, "a grid barrier of the round kernel timed out (not all workgroups were resident)");
     }
     return DFLASH_OK;

@@ -47,8 +47,12 @@
 // Grid barrier.  Each workgroup bumps a counter for its XCD slot
 // (blockIdx % 8).  The last arrival of a slot bumps a global counter.  The
 // last global arrival publishes a new generation to one flag per slot, and
-// the waiting workgroups poll the flag of their own slot.  The spin is
-// bounded: on expiry the kernel sets an error word and every workgroup exits.
+// the waiting workgroups poll the flag of their own slot.  The counters are
+// never reset: after g barriers over the workspace's lifetime a slot counter
+// holds g * (workgroups in the slot) and the global one g * (slots), mod 2^32,
+// so each arrival learns from the returned value whether it is the last.
+// The spin is bounded: on expiry the kernel sets an error word and every
+// workgroup exits.
 #include "common.h"
 #include "round.h"
 
@@ -152,15 +156,10 @@ __device__ __forceinline__ bool grid_sync(unsigned *st, unsigned &gen) {
         const unsigned target = gen + 1;
         unsigned *xc = st + BAR_XCNT + x * 32, *gc = st + BAR_GCNT, *gf = st + BAR_GEN + x * 32;
         const unsigned prev = add_u(xc, 1u);
-        if (prev + 1 == per_x) {
-            stc_u(xc, 0u);
-            vm_wait();
+        if (prev + 1 == target * per_x) {
             const unsigned g = add_u(gc, 1u);
-            if (g + 1 == nx) {
-                stc_u(gc, 0u);
-                vm_wait();
+            if (g + 1 == target * nx)
                 for (unsigned k = 0; k < nx; ++k) stc_u(st + BAR_GEN + k * 32, target);
-            }
         }
         int spins = 0, good = 1;
         while (ldc_u(gf) != target) {

@@ -159,8 +159,10 @@ void dflash_free(dflash_model *m);
 /* Bytes of device workspace (the per-step scratch of [atlas dflash_head]
  * "DflashScratch") needed by calls that process up to `max_rows` ctx rows at
  * once: ctx_features t, ingest_ctx t, or forward_full n.  The workspace must
- * be 256-byte aligned and zero-filled once before its first use.  The library
- * leaves its counters at zero after every call.  Returns 0 if max_rows < 0. */
+ * be 256-byte aligned and zero-filled once before its first use.  It then
+ * belongs to one device: the round kernel's grid-barrier counters only grow,
+ * and their meaning depends on that device's CU count.  The other counters
+ * are left at zero after every call.  Returns 0 if max_rows < 0. */
 size_t dflash_workspace_bytes(const dflash_model *m, int32_t max_rows);
 
 /* Context features ([DflashDraft] "ctx_features"): feats = hidden_norm(fc(taps)).
