@@ -17,7 +17,7 @@
 #include "dflash.h"
 #include "dflash_prof.h"
 #include "kernels.h"
-#include "round.h"
+#include "sround.h"
 
 struct dflash_model {
     dflash_cfg cfg;
@@ -77,37 +77,33 @@ constexpr int MAX_ATTN_SPLITS = 64;
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct WsLayout {
-    size_t x, xn, qkv, q, o, z, feats, part_o, part_ml, gpart, gcnt, bar, ssq, rpart, trace, d2a, d2m, d2r, total;
+    size_t gcnt, gpart, ctr, trace, cs, xsave, lay, lay_stride, qkv, feats, total;
+    dfl::SrLayout sl;
 };
 
+// workgroups the round kernel is laid out for at most (partial sums of
+// squares are stored per workgroup)
+constexpr int WS_MAX_NWG = 256;
+
 WsLayout ws_layout(const dflash_cfg &c, int max_rows) {
-    const size_t H = c.hidden, qd = (size_t)c.n_q_heads * c.head_dim, kvd = (size_t)c.n_kv_heads * c.head_dim;
-    const size_t G = c.n_q_heads / c.n_kv_heads;
-    const size_t qpad = (MAX_BLOCK * G + 15) / 16 * 16;
+    const size_t H = c.hidden, kvd = (size_t)c.n_kv_heads * c.head_dim;
     const size_t rows = (size_t)(max_rows > MAX_BLOCK ? max_rows : MAX_BLOCK);
     WsLayout L{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     // fixed-size regions first, so their offsets do not depend on max_rows
     L.gcnt = take(sizeof(unsigned) * dfl::GEMM_MAX_COUNTERS);
-    L.bar = take(sizeof(unsigned) * dfl::BAR_WORDS);
-    L.trace = take(8 * dfl::RND_TRACE_WORDS);
-    L.x = take(4 * MAX_BLOCK * H);
-    L.xn = take(4 * MAX_BLOCK * H);
-    L.q = take(4 * MAX_BLOCK * qd);
-    L.o = take(4 * MAX_BLOCK * qd);
-    L.z = take(4 * MAX_BLOCK * (size_t)c.intermediate);
-    L.part_o = take(4 * (size_t)c.n_kv_heads * MAX_ATTN_SPLITS * qpad * c.head_dim);
-    L.part_ml = take(4 * (size_t)c.n_kv_heads * MAX_ATTN_SPLITS * qpad * 2);
     L.gpart = take(4 * dfl::GEMM_PART_FLOATS);
-    L.ssq = take(4 * (H / 128) * MAX_BLOCK);
-    L.rpart = take(4 * (size_t)dfl::MAX_NWG * dfl::MAXSLOT * MAX_BLOCK * 256);
-    L.d2a = take(4 * MAX_BLOCK * 4 * dfl::RND_MAX_D2);
-    L.d2m = take(4 * MAX_BLOCK * 4 * dfl::RND_MAX_D2);
-    L.d2r = take(4 * MAX_BLOCK);
+    L.ctr = take(sizeof(unsigned) * dfl::SR_CTR_WORDS);
+    L.trace = take(8 * dfl::SR_TRACE);
+    L.cs = take(4 * (size_t)MAX_BLOCK * c.head_dim);
+    L.xsave = take(4 * (size_t)MAX_BLOCK * H);
+    L.sl = dfl::sround_layout(c.hidden, c.intermediate, c.n_q_heads * c.head_dim, (int)kvd, c.n_kv_heads,
+                              c.n_q_heads / c.n_kv_heads, c.head_dim, c.weight_dtype, WS_MAX_NWG, c.d2_groups);
+    L.lay_stride = (size_t)L.sl.stride;
+    L.lay = take(L.lay_stride * (dfl::SR_MAXL + 1));
     // row-dependent regions
-    size_t qkv_rows = MAX_BLOCK * (qd + 2 * kvd), ing = rows * 2 * kvd;
-    L.qkv = take(4 * (qkv_rows > ing ? qkv_rows : ing));
+    L.qkv = take(4 * rows * 2 * kvd);
     L.feats = take(4 * rows * H);
     L.total = off;
     return L;
@@ -138,7 +134,8 @@ int check_cfg(const dflash_cfg &c) {
     if (c.head_dim != 64 && c.head_dim != 128) return fail(DFLASH_E_UNSUPPORTED, "head_dim %d: only 64 and 128 are built", c.head_dim);
     if (c.n_q_heads <= 0 || c.n_kv_heads <= 0 || c.n_q_heads % c.n_kv_heads)
         return fail(DFLASH_E_INVAL, "n_q_heads %d must be a positive multiple of n_kv_heads %d", c.n_q_heads, c.n_kv_heads);
-    if (c.n_q_heads / c.n_kv_heads > 16) return fail(DFLASH_E_UNSUPPORTED, "more than 16 q heads per kv head");
+    if (c.n_q_heads / c.n_kv_heads > dfl::SR_MAXG)
+        return fail(DFLASH_E_UNSUPPORTED, "more than %d q heads per kv head", dfl::SR_MAXG);
     if ((c.n_q_heads * c.head_dim) % 256) return fail(DFLASH_E_UNSUPPORTED, "n_q_heads*head_dim must be a multiple of 256");
     if (c.n_taps <= 0 || ((size_t)c.n_taps * c.hidden) % 256) return fail(DFLASH_E_INVAL, "n_taps %d invalid", c.n_taps);
     if (!(c.rms_eps > 0.f) || !std::isfinite(c.rms_eps)) return fail(DFLASH_E_INVAL, "rms_eps must be positive");
@@ -156,10 +153,13 @@ int check_cfg(const dflash_cfg &c) {
     if (c.kv_dtype == DFLASH_F32 && c.head_dim != 64) return fail(DFLASH_E_UNSUPPORTED, "an f32 KV cache is built for head_dim 64 only");
     if (c.d2_groups < 0) return fail(DFLASH_E_INVAL, "d2_groups must be >= 0");
     if (c.d2_groups > 0) {
-        if (c.d2_groups > dfl::RND_MAX_D2 || c.hidden % c.d2_groups || (c.hidden / c.d2_groups) % 8)
-            return fail(DFLASH_E_UNSUPPORTED, "d2_groups %d: built for G <= %d with hidden/G a multiple of 8", c.d2_groups,
-                        dfl::RND_MAX_D2);
+        if (c.d2_groups > dfl::SR_MAX_D2 || c.hidden % c.d2_groups || (c.hidden / c.d2_groups) % 16)
+            return fail(DFLASH_E_UNSUPPORTED, "d2_groups %d: built for G <= %d with hidden/G a multiple of 16",
+                        c.d2_groups, dfl::SR_MAX_D2);
     }
+    if (dfl::sround_nwg(c.hidden, c.intermediate, c.n_q_heads * c.head_dim, c.n_kv_heads * c.head_dim, c.weight_dtype,
+                        c.d2_groups, WS_MAX_NWG) <= 0)
+        return fail(DFLASH_E_UNSUPPORTED, "no workgroup layout of the round kernel fits these dimensions");
     return DFLASH_OK;
 }
 
@@ -279,60 +279,44 @@ int device_cus() {
     return cus[dev];
 }
 
-int ks_of(int wt) { return wt == DFLASH_BF16 ? 32 : wt == DFLASH_FP8_E4M3 ? 64 : 16; }
+dfl::SrMat smat(const dflash_matrix &m) { return dfl::SrMat{m.data, m.scale}; }
 
-dfl::GemmPlanDev plan_gemm(int N, int K, int wt, int nwg) {
-    dfl::GemmPlanDev p;
-    p.K = K;
-    p.steps = K / ks_of(wt);
-    p.total = (N / 128) * p.steps;
-    p.upw = (p.total + nwg - 1) / nwg;
-    return p;
-}
-
-bool plan_ok(const dfl::GemmPlanDev &p) { return (p.upw + p.steps - 1) / p.steps + 1 <= dfl::MAXSLOT; }
-
-dfl::MatRef mref(const dflash_matrix &m, int n) { return dfl::MatRef{m.data, m.scale, n, 0}; }
-
+// forward_round: the streamed round kernel, one launch per SR_MAXL layers
 hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *noise, const int32_t *pos, int b, float *out,
                      void *ws, const WsLayout &L, hipStream_t s) {
     const dflash_cfg &c = m->cfg;
-    const int nwg = std::min(device_cus(), dfl::MAX_NWG);
+    const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+    const int nwg = dfl::sround_nwg(c.hidden, c.intermediate, qd, kvd, c.weight_dtype, c.d2_groups,
+                                    std::min(device_cus(), WS_MAX_NWG));
     if (nwg <= 0) return hipErrorInvalidDevice;
-    dfl::RoundArgs ra{};
-    dfl::RoundScalars &a = ra.s;
-    a.H = c.hidden; a.nq = c.n_q_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim; a.I = c.intermediate;
-    a.qd = c.n_q_heads * c.head_dim; a.kvd = c.n_kv_heads * c.head_dim;
-    a.wt = c.weight_dtype; a.kv_f32 = c.kv_dtype == DFLASH_F32;
-    a.b = b; a.len = kv->len; a.cap = kv->capacity;
-    a.eps = c.rms_eps; a.mscale = (float)m->mscale;
-    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+    dfl::SrArgs ra{};
+    dfl::SrScalars &a = ra.s;
+    a.H = c.hidden; a.I = c.intermediate; a.nq = c.n_q_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim;
+    a.qd = qd; a.kvd = kvd; a.G = c.n_q_heads / c.n_kv_heads;
+    a.b = b; a.len = kv->len; a.cap = kv->capacity; a.d2 = c.d2_groups;
+    a.nwg = nwg; a.cq = (qd + 2 * kvd) / nwg; a.ch = c.hidden / nwg; a.ci = c.intermediate / nwg;
     // attention key splits: at most one item per workgroup, keys per split a multiple of 32
-    const int n_keys = kv->len + b;
-    int ns = std::min({dfl::RND_MAX_SPLITS, (n_keys + 31) / 32, std::max(1, nwg / c.n_kv_heads)});
-    int kps = (n_keys + ns - 1) / ns;
+    int ns = std::max(1, std::min({dfl::SR_MAX_SPLITS, nwg / c.n_kv_heads, (kv->len + 31) / 32}));
+    int kps = kv->len > 0 ? (kv->len + ns - 1) / ns : 32;
     kps = (kps + 31) / 32 * 32;
-    a.attn_kps = kps;
-    a.attn_nsplit = (n_keys + kps - 1) / kps;
-    a.qpad = (b * (c.n_q_heads / c.n_kv_heads) + 15) / 16 * 16;
+    a.kps = kps;
+    a.nsplit = kv->len > 0 ? (kv->len + kps - 1) / kps : 1;
+    a.eps = c.rms_eps; a.mscale = (float)m->mscale;
+    a.qscale = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
     a.noise = noise; a.pos = pos; a.out = out; a.g_norm = m->w.g_norm;
     a.kv_lstride = (long long)c.n_kv_heads * kv->capacity * c.head_dim * (long long)kv_elem(c);
-    a.X = at<float>(ws, L.x); a.ssq = at<float>(ws, L.ssq); a.Q = at<float>(ws, L.q); a.O = at<float>(ws, L.o);
-    a.Z = at<float>(ws, L.z); a.part = at<float>(ws, L.rpart);
-    a.attn_o = at<float>(ws, L.part_o); a.attn_ml = at<float>(ws, L.part_ml);
-    a.bar = at<unsigned>(ws, L.bar);
+    a.ctr = at<unsigned>(ws, L.ctr);
+    a.cs = at<float>(ws, L.cs);
+    a.xsave = at<float>(ws, L.xsave);
+    a.lay = at<char>(ws, L.lay);
+    a.lay_stride = (long long)L.lay_stride;
+    a.o_xa = L.sl.xa; a.o_ssa = L.sl.ssa; a.o_qkv = L.sl.qkv; a.o_po = L.sl.po; a.o_pml = L.sl.pml;
+    a.o_of = L.sl.of; a.o_xm = L.sl.xm; a.o_ssm = L.sl.ssm; a.o_zf = L.sl.zf; a.o_da = L.sl.da; a.o_dm = L.sl.dm;
     a.trace = g_trace.load() ? at<unsigned long long>(ws, L.trace) : nullptr;
-    a.p_qkv = plan_gemm(a.qd + 2 * a.kvd, a.H, a.wt, nwg);
-    a.p_o = plan_gemm(a.H, a.qd, a.wt, nwg);
-    a.p_gu = plan_gemm(a.I, a.H, a.wt, nwg);
-    a.p_d = plan_gemm(a.H, a.I, a.wt, nwg);
-    if (!plan_ok(a.p_qkv) || !plan_ok(a.p_o) || !plan_ok(a.p_gu) || !plan_ok(a.p_d)) return hipErrorInvalidValue;
-    a.d2 = c.d2_groups;
-    a.d2_Da = at<float>(ws, L.d2a); a.d2_Dm = at<float>(ws, L.d2m); a.d2_rinv = at<float>(ws, L.d2r);
     memcpy(ra.inv_freq, m->inv_freq, sizeof ra.inv_freq);
     int l0 = 0;
     do {
-        const int nl = std::min(dfl::RND_MAXL, c.n_layers - l0);
+        const int nl = std::min(dfl::SR_MAXL, c.n_layers - l0);
         a.nl = nl;
         a.first = l0 == 0;
         a.last = l0 + nl == c.n_layers;
@@ -340,19 +324,19 @@ hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *no
         a.vc = static_cast<char *>(layer_ptr(kv->v, c, kv->capacity, l0));
         for (int i = 0; i < nl; ++i) {
             const dflash_layer_weights &W = m->layers[l0 + i];
-            dfl::LayerRefs &R = ra.L[i];
-            R.q = mref(W.wq, a.qd); R.k = mref(W.wk, a.kvd); R.v = mref(W.wv, a.kvd);
-            R.o = mref(W.wo, a.H); R.g = mref(W.wg, a.I); R.u = mref(W.wu, a.I); R.d = mref(W.wd, a.H);
+            dfl::SrLayer &R = ra.L[i];
+            R.q = smat(W.wq); R.k = smat(W.wk); R.v = smat(W.wv); R.o = smat(W.wo);
+            R.g = smat(W.wg); R.u = smat(W.wu); R.d = smat(W.wd);
             R.g_in = W.g_in; R.g_post = W.g_post; R.g_q = W.g_q; R.g_k = W.g_k;
             if (c.d2_groups > 0) {
-                R.aw = mref(W.attn_w_dyn, 4 * c.d2_groups); R.mw = mref(W.mlp_w_dyn, 4 * c.d2_groups);
+                R.aw = smat(W.attn_w_dyn); R.mw = smat(W.mlp_w_dyn);
                 R.abase = W.attn_base; R.mbase = W.mlp_base;
             }
         }
         hipError_t e;
         {
             ProfScope p(DFLASH_K_ROUND, s);
-            e = dfl::round_launch(ra, nwg, s);
+            e = dfl::sround_launch(ra, c.weight_dtype, nwg, s);
         }
         if (e != hipSuccess) return e;
         l0 += nl;
@@ -500,18 +484,17 @@ int dflash_workspace_status(const dflash_model *m, void *ws, size_t ws_bytes, vo
     int rc = check_ws(m, ws, ws_bytes, 0);
     if (rc) return rc;
     const WsLayout L = ws_layout(m->cfg, 0);
-    unsigned *err = at<unsigned>(ws, L.bar) + dfl::BAR_ERR;
+    unsigned *ctr = at<unsigned>(ws, L.ctr);
     unsigned h = 0;
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);
-    if (e == hipSuccess) e = hipMemcpy(&h, err, sizeof h, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(&h, ctr + dfl::SR_CTR_ERR, sizeof h, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "workspace_status");
     if (h != 0) {
-        // the barrier counters are inconsistent after a timed-out barrier: start them over
-        unsigned *bar = at<unsigned>(ws, L.bar);
-        e = hipMemset(bar, 0, sizeof(unsigned) * dfl::BAR_WORDS);
+        // the phase counters are inconsistent after a timed-out wait: start them over
+        e = hipMemset(ctr, 0, sizeof(unsigned) * dfl::SR_CTR_WORDS);
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) return hip_fail(e, "workspace_status");
-        return fail(DFLASH_E_HIP, "a grid barrier of the round kernel timed out (not all workgroups were resident)");
+        return fail(DFLASH_E_HIP, "a bounded wait of the round kernel timed out (not all workgroups were resident)");
     }
     return DFLASH_OK;
 }
@@ -523,7 +506,7 @@ int dflash_prof_trace(int32_t enable) {
 
 int dflash_prof_trace_read(const dflash_model *m, void *ws, size_t ws_bytes, uint64_t *out, int32_t n, void *stream) {
     g_err.clear();
-    if (!m || !out || n < 0 || n > dfl::RND_TRACE_WORDS) return fail(DFLASH_E_INVAL, "bad trace read arguments");
+    if (!m || !out || n < 0 || n > dfl::SR_TRACE) return fail(DFLASH_E_INVAL, "bad trace read arguments");
     int rc = check_ws(m, ws, ws_bytes, 0);
     if (rc) return rc;
     const WsLayout L = ws_layout(m->cfg, 0);

@@ -59,21 +59,5 @@ struct RopeArgs {
 };
 hipError_t qk_norm_rope(const RopeArgs &a, hipStream_t s);
 
-// ---- non-causal GQA attention over the cache ------------------------------
-struct AttnArgs {
-    const float *q;               // [b][nq][d] f32, normed + roped + scaled
-    const void *kc; const void *vc; int cap;
-    int n_keys;                   // keys [0, n_keys) of the layer's cache
-    int b, nq, nkv, d;
-    int kv_f32;
-    float scale_log2;             // log2(e) / sqrt(d)
-    int kps, nsplit;              // keys per split (multiple of 32), number of splits
-    int qpad;                     // queries per kv head, padded to 16
-    float *part_o;                // [nkv][nsplit][qpad][d]
-    float *part_ml;               // [nkv][nsplit][qpad][2]
-    float *out;                   // [b][nq*d]
-};
-void attn_plan(AttnArgs &a, int max_splits);
-hipError_t attention(const AttnArgs &a, hipStream_t s);
 
 }  // namespace dfl

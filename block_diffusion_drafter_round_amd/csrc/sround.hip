@@ -1,0 +1,1478 @@
+// Streamed forward_round kernel for gfx950: every layer of a drafting round
+// in one persistent launch ([DflashDraft] "forward_round": only the b block
+// rows are projected per layer, block K/V land at cache rows [len, len + b),
+// attention is full and non-causal over all len + b keys; [atlas dflash_head]
+// overview: pre-norm Qwen3 layers with GQA and a SwiGLU MLP).
+//
+// One workgroup per CU: one loader wave and eight compute waves.
+//
+// Loader wave.  Weights and the committed K/V rows do not depend on the
+// round's activations, so the loader streams them, in the exact order the
+// compute waves use them, into a ring of LDS slots with direct-to-LDS loads
+// (global_load_lds_dwordx4).  It keeps SR_DEPTH slots in flight, publishes a
+// slot once its loads have landed, and reuses a slot once every compute wave
+// has released it.  Its only memory operations are these loads, so its
+// vector-memory counter tracks them exactly.  HBM keeps streaming while the
+// compute waves wait for activations.
+//
+// Compute waves.  Each layer is a chain of phases.  A phase starts when every
+// workgroup has signalled the previous one:
+//   Q  q|k|v projection: columns split over workgroups, K split over waves
+//   A  attention: (kv head, key split) items; q/k head RMSNorm + NeoX rope
+//      in registers; online softmax over the ring's K/V blocks and the
+//      block's own K/V; partial (m, l, O) per split
+//   M  merge of the splits -> O, written as o_proj input fragments
+//   O  o_proj + residual -> post-attention-norm input fragments
+//   G  gate|up + SwiGLU -> down input fragments
+//   D  down + residual -> next layer's input fragments
+// (with the DFlash2 wrap, a coefficient phase precedes Q and G).
+// A workgroup owns the same hidden columns in O and D, so it keeps its slice
+// of the residual stream X in LDS for the whole launch.
+//
+// Activations between phases are bf16 (f32 in the f32 arm) in MFMA fragment
+// order, so a compute wave loads its K range with one coalesced 16-byte load
+// per lane and k step.  RMSNorm is split: the producer applies the gain, the
+// consumer the 1/rms row scale (from per-workgroup partial sums of squares)
+// to its GEMM output.
+//
+// Synchronisation.  Inside a workgroup: LDS words only (no s_barrier; the
+// loader never waits for compute waves except for free ring slots).  The last
+// compute wave to finish a phase runs the epilogue, waits for its stores and
+// bumps the counter of its XCD slot (blockIdx % 8).  Wave 0 polls the eight
+// counters with device-coherent loads and publishes the phase in LDS.  Each
+// (layer, phase) output has its own workspace buffer, written with
+// device-coherent (sc1) stores and first read after the counter says it is
+// complete, so plain loads can use the L2 of each XCD.  Counters are never
+// reset: the workspace's epoch word counts the phases of earlier launches.
+// Every spin is bounded; on expiry the kernel sets the error word and all
+// waves leave.
+#include "common.h"
+#include "sround.h"
+
+namespace dfl {
+namespace {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ---------------------------------------------------------------------------
+// memory helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t cbuf(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
+}
+constexpr int CPOL_SC1 = 16;
+// device-coherent stores: written through to memory.  `base` must be
+// uniform over the wave; the byte offset is per lane.
+__device__ __forceinline__ void st16(void *base, size_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, cbuf(base), (uint32_t)off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ void st8(void *base, size_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, cbuf(base), (uint32_t)off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ void st4(void *base, size_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, cbuf(base), (uint32_t)off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ void st2(void *base, size_t off, uint16_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, cbuf(base), (uint32_t)off, 0, CPOL_SC1);
+}
+// s_waitcnt through the builtin, so the compiler's own counter tracking
+// sees the wait (gfx9 encoding: vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14)
+__device__ __forceinline__ void vm_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }     // vmcnt(0)
+__device__ __forceinline__ unsigned ldc_u(unsigned *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stc_u(unsigned *p, unsigned v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void add_u(unsigned *p, unsigned v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// LDS words shared by the waves of the workgroup.  Loads return a
+// wave-uniform value, so the spin loops around them branch on scalars.
+__device__ __forceinline__ unsigned lds_ld(unsigned *p) {
+    return __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+}
+__device__ __forceinline__ void lds_st(unsigned *p, unsigned v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ unsigned lds_add(unsigned *p, unsigned v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void cbar() { asm volatile("" ::: "memory"); }
+// LDS word access for the loader wave.  Its direct-to-LDS loads are
+// outstanding while it touches its counters; through the builtins the
+// compiler would drain them (vmcnt(0)) before every such access, since it
+// cannot tell the counters apart from the ring.  These never alias the ring.
+__device__ __forceinline__ uint32_t lds_off(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ unsigned lds_ld_nodep(const unsigned *p) {
+    unsigned v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(p)) : "memory");
+    return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ void lds_st_nodep(unsigned *p, unsigned v) {
+    asm volatile("ds_write_b32 %0, %1" : : "v"(lds_off(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ float f_of(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t bf2(float a, float b) { return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16); }
+
+// Lane and wave index behind an opaque copy: values derived from them are
+// recomputed inside each phase rather than hoisted out of the layer loop
+// (which would keep them live, in registers, for the whole kernel).
+__device__ __forceinline__ int lane_id() {
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    return l;
+}
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// The arguments are read in place from the kernel-argument segment.  Code
+// outside the kernel function itself has no kernarg-segment pointer (that
+// intrinsic yields null there), but it does receive the implicit-argument
+// pointer, and the implicit arguments start right after the explicit ones.
+typedef const __attribute__((address_space(4))) SrArgs KArgs;
+static_assert(sizeof(SrArgs) % 8 == 0, "implicit arguments follow SrArgs directly");
+__device__ __forceinline__ KArgs *ka() {
+    return (KArgs *)((const __attribute__((address_space(4))) char *)__builtin_amdgcn_implicitarg_ptr() - sizeof(SrArgs));
+}
+#define SS (ka()->s)
+
+constexpr int SPIN_LIMIT = 1 << 22;
+
+// ---------------------------------------------------------------------------
+// per-dtype constants
+//   KW: K values per 16-byte weight load of one lane times the 4 lane groups
+//   ES: bytes per weight, P: activation values per lane and k step,
+//   AB: bytes per activation value, AFR: 16-byte activation pieces per step
+// ---------------------------------------------------------------------------
+template <int WT> struct TR;
+template <> struct TR<WT_BF16> { static constexpr int KW = 32, ES = 2, P = 8, AB = 2, AFR = 1; };
+template <> struct TR<WT_FP8>  { static constexpr int KW = 64, ES = 1, P = 16, AB = 2, AFR = 2; };
+template <> struct TR<WT_F32>  { static constexpr int KW = 16, ES = 4, P = 4, AB = 4, AFR = 1; };
+
+// element offset of activation (row r, column c) in fragment order: lane
+// (r, g) of k step c / KW holds the P consecutive columns of group g
+template <int WT>
+__device__ __forceinline__ size_t frag_idx(int r, int c) {
+    constexpr int KW = TR<WT>::KW, P = TR<WT>::P;
+    const int ks = c / KW, rem = c - ks * KW, g = rem / P, j = rem - g * P;
+    return ((size_t)(ks * 4 + g) * 16 + r) * P + j;
+}
+
+// store 4 consecutive activation values (c 4-aligned) as fragment elements
+template <int WT>
+__device__ __forceinline__ void put4(void *buf, int r, int c, float x0, float x1, float x2, float x3) {
+    const size_t e = frag_idx<WT>(r, c);
+    if constexpr (TR<WT>::AB == 4) st16(buf, e * 4, u32x4{__float_as_uint(x0), __float_as_uint(x1), __float_as_uint(x2), __float_as_uint(x3)});
+    else st8(buf, e * 2, u32x2{bf2(x0, x1), bf2(x2, x3)});
+}
+
+// ---------------------------------------------------------------------------
+// LDS
+// ---------------------------------------------------------------------------
+struct SrLds {
+    u32x4 ring[SR_NSLOT][SR_CW][64];
+    f32x4 red[SR_CW][SR_MAXT][64];
+    float xown[16][SR_MAXCH];
+    float rinv[16];
+    unsigned cons[SR_CW];      // slots each compute wave has released
+    unsigned pub;              // slots the loader has published
+    unsigned phase;            // global phases known complete
+    unsigned rphase;           // phase whose row scales rinv holds (+1)
+    unsigned done;             // compute-wave arrivals (8 per phase)
+    unsigned abort_;
+};
+
+// the workgroup's LDS (each kernel instance allocates its own copy)
+__shared__ SrLds S;
+
+
+// a bounded wait ran out: every wave leaves; the kernel's exit path records
+// the error in the workspace
+
+__device__ __forceinline__ void set_error(SrLds &S) { lds_st(&S.abort_, 1u); }
+
+// Phase trace (workgroup 0, when enabled): stamp k of phase p at word 8p + k.
+//   0 wave 0 sees the phase's inputs complete   1 wave 0 done with its share
+//   2 epilogue done and signalled                3 loader issues the phase's first slot
+//   4 loader has issued the phase's last slot
+__device__ __forceinline__ void trace_at(unsigned p, int k) {
+    if (blockIdx.x == 0 && (threadIdx.x & 63) == 0 && SS.trace && 8 * p + k < SR_TRACE) SS.trace[8 * p + k] = wall_clock64();
+}
+
+// ---------------------------------------------------------------------------
+// phase list of a launch
+// ---------------------------------------------------------------------------
+enum Kind { K_INIT, K_DA, K_Q, K_A, K_M, K_O, K_DM, K_G, K_D };
+__device__ __forceinline__ int npl() { return SS.d2 ? 8 : 6; }
+__device__ __forceinline__ int kind_at(int i) {   // i-th phase of a layer
+    if (SS.d2) {
+        switch (i) {
+            case 0: return K_DA; case 1: return K_Q; case 2: return K_A; case 3: return K_M;
+            case 4: return K_O; case 5: return K_DM; case 6: return K_G; default: return K_D;
+        }
+    }
+    switch (i) {
+        case 0: return K_Q; case 1: return K_A; case 2: return K_M; case 3: return K_O; case 4: return K_G; default: return K_D;
+    }
+}
+__device__ __forceinline__ char *layer_buf(int l) { return SS.lay + (size_t)l * SS.lay_stride; }
+
+// ---------------------------------------------------------------------------
+// GEMM tiles: output columns of this workgroup in pieces of <= 16
+// ---------------------------------------------------------------------------
+struct GT {
+    const char *w;       // weight row of the tile's first column
+    const float *sc;     // fp8 row scales of the tile's first column, or nullptr
+    int n;               // columns (<= 16, multiple of 4)
+    int col;             // first column within its matrix
+    int seg;             // Q: 0 q, 1 k, 2 v;  G: 0 gate, 1 up
+};
+
+__device__ __forceinline__ SrMat kmat(const __attribute__((address_space(4))) SrMat &m) { return SrMat{m.w, m.s}; }
+
+__device__ __forceinline__ int gemm_K(int kind) {
+    return kind == K_O ? SS.qd : kind == K_D ? SS.I : SS.H;
+}
+
+// number of tiles of this workgroup for a GEMM phase
+__device__ __forceinline__ int gemm_nt(int kind) {
+    const int w = blockIdx.x;
+    switch (kind) {
+        case K_Q: {
+            const int c0 = w * SS.cq, c1 = c0 + SS.cq;
+            const int b1 = SS.qd, b2 = SS.qd + SS.kvd, b3 = SS.qd + 2 * SS.kvd;
+            int nt = 0;
+            const int a[3] = {0, b1, b2}, e[3] = {b1, b2, b3};
+#pragma unroll
+            for (int s = 0; s < 3; ++s) {
+                const int lo = max(c0, a[s]), hi = min(c1, e[s]);
+                if (hi > lo) nt += (hi - lo + 15) / 16;
+            }
+            return nt;
+        }
+        case K_O: case K_D: return (SS.ch + 15) / 16;
+        case K_G: return 2 * ((SS.ci + 15) / 16);
+        default: return 16 * w < 4 * SS.d2 ? 1 : 0;     // K_DA, K_DM
+    }
+}
+
+template <int WT>
+__device__ __forceinline__ GT gemm_tile(int kind, int l, int t) {
+    constexpr int ES = TR<WT>::ES;
+    const int w = blockIdx.x;
+    const int K = gemm_K(kind);
+    GT r{nullptr, nullptr, 0, 0, 0};
+    auto mk = [&](SrMat m, int col, int n, int seg) {
+        r.w = (const char *)m.w + (size_t)col * K * ES;
+        r.sc = m.s ? m.s + col : nullptr;
+        r.n = n; r.col = col; r.seg = seg;
+    };
+    switch (kind) {
+        case K_Q: {
+            const int c0 = w * SS.cq, c1 = c0 + SS.cq;
+            const int a[3] = {0, SS.qd, SS.qd + SS.kvd}, e[3] = {SS.qd, SS.qd + SS.kvd, SS.qd + 2 * SS.kvd};
+            int base = 0;
+#pragma unroll
+            for (int s = 0; s < 3; ++s) {
+                const int lo = max(c0, a[s]), hi = min(c1, e[s]);
+                if (hi > lo) {
+                    const int n = (hi - lo + 15) / 16;
+                    if (t >= base && t < base + n) {
+                        const int cl = lo - a[s] + 16 * (t - base);
+                        const SrMat m = s == 0 ? kmat(ka()->L[l].q) : s == 1 ? kmat(ka()->L[l].k) : kmat(ka()->L[l].v);
+                        mk(m, cl, min(16, hi - a[s] - cl), s);
+                    }
+                    base += n;
+                }
+            }
+            break;
+        }
+        case K_O: case K_D: {
+            const int c = w * SS.ch + 16 * t;
+            mk(kind == K_O ? kmat(ka()->L[l].o) : kmat(ka()->L[l].d), c, min(16, (w + 1) * SS.ch - c), 0);
+            break;
+        }
+        case K_G: {
+            const int ntg = (SS.ci + 15) / 16;
+            const int s = t < ntg ? 0 : 1, tt = t - s * ntg;
+            const int c = w * SS.ci + 16 * tt;
+            mk(s == 0 ? kmat(ka()->L[l].g) : kmat(ka()->L[l].u), c, min(16, (w + 1) * SS.ci - c), s);
+            break;
+        }
+        default: {   // K_DA, K_DM
+            const int c = 16 * w;
+            mk(kind == K_DA ? kmat(ka()->L[l].aw) : kmat(ka()->L[l].mw), c, min(16, 4 * SS.d2 - c), 0);
+            break;
+        }
+    }
+    return r;
+}
+
+// k steps of one GEMM pass per wave (activations of one pass are held in
+// registers; the next pass's are loaded while this one runs) and the most
+// passes built.  Each wave takes npass * NF consecutive k steps; steps past
+// the end of K are dead (loader and compute waves agree on the count).
+template <int WT> struct PassCfg { static constexpr int NF = WT == WT_FP8 ? 4 : 8; };
+constexpr int SR_MAXPASS = 3;
+template <int WT>
+__device__ __forceinline__ int gemm_npass(int nst) {
+    constexpr int NF = PassCfg<WT>::NF;
+    const int nkw = (nst + SR_CW - 1) / SR_CW;
+    return (nkw + NF - 1) / NF;
+}
+
+// attention item of this workgroup: kv head, key range, whether it holds the block
+struct AItem {
+    int h, k_lo, k_hi, last, nblk;
+};
+__device__ __forceinline__ bool attn_item(AItem &it) {
+    const int item = blockIdx.x;
+    if (item >= SS.nkv * SS.nsplit) return false;
+    it.h = item / SS.nsplit;
+    const int s = item - it.h * SS.nsplit;
+    it.k_lo = s * SS.kps;
+    it.k_hi = min(SS.len, it.k_lo + SS.kps);
+    if (it.k_hi < it.k_lo) it.k_hi = it.k_lo;
+    it.last = s == SS.nsplit - 1;
+    it.nblk = (it.k_hi - it.k_lo + 31) / 32;
+    return true;
+}
+
+// K/V parts of one 32-key block: K parts (key tile kt, d chunk c), then V^T
+// parts (d tile t, half hv); eight parts fill one ring slot
+template <int WT, int D> struct AT {
+    static constexpr bool F32 = WT == WT_F32;
+    static constexpr int KVB = F32 ? 4 : 2;          // bytes per cached K/V value
+    static constexpr int NC = D * KVB / 64;          // d chunks of 16 bytes per lane group
+    static constexpr int KP = 2 * NC;
+    static constexpr int VH = F32 ? 2 : 1;
+    static constexpr int VP = (D / 16) * VH;
+    static constexpr int SLOTS = (KP + VP) / 8;
+    static constexpr int PQ = F32 ? 4 : 8;           // values per lane per d chunk
+    static constexpr int NQV = D / 4;                // values per lane per head row
+};
+
+// ---------------------------------------------------------------------------
+// loader wave
+// ---------------------------------------------------------------------------
+struct Loader {
+    unsigned seq;       // next slot to fill
+    unsigned freed;     // slots known released by every compute wave
+};
+
+__device__ __forceinline__ bool loader_wait_free(SrLds &S, Loader &ld) {
+    // slot seq reuses the storage of slot seq - NSLOT
+    if (ld.seq < SR_NSLOT) return true;
+    const unsigned need = ld.seq - SR_NSLOT + 1;
+    int spins = 0;
+    bool drained = false;
+    while (ld.freed < need) {
+        unsigned m = 0xffffffffu;
+#pragma unroll
+        for (int v = 0; v < SR_CW; ++v) m = min(m, lds_ld_nodep(&S.cons[v]));
+        ld.freed = m;
+        if (ld.freed >= need) break;
+        if (!drained && ld.seq > SR_DEPTH) {
+            // the ring is full and the compute waves are not consuming (they
+            // wait for a phase): hand them every slot already issued
+            drained = true;
+            vm_wait();
+            lds_st_nodep(&S.pub, ld.seq);
+        }
+        if (lds_ld_nodep(&S.abort_)) return false;
+        if (++spins > SPIN_LIMIT) { lds_st_nodep(&S.abort_, 1u); return false; }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return true;
+}
+
+// after the 8 loads of slot seq are issued: publish the slot SR_DEPTH behind
+__device__ __forceinline__ void loader_commit(SrLds &S, Loader &ld) {
+    ++ld.seq;
+    if (ld.seq > SR_DEPTH) {
+        static_assert(8 * SR_DEPTH == 56, "wait immediate");
+        __builtin_amdgcn_s_waitcnt(0xCF78);                  // vmcnt(56): 8 * SR_DEPTH loads may stay in flight
+        cbar();
+        lds_st_nodep(&S.pub, ld.seq - SR_DEPTH);
+    }
+}
+
+__device__ __forceinline__ void dma16(const void *g, u32x4 *ldsdst) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)ldsdst, 16, 0, 0);
+}
+
+template <int WT>
+__device__ __forceinline__ bool load_gemm(SrLds &S, Loader &ld, int kind, int l) {
+    constexpr int KW = TR<WT>::KW, ES = TR<WT>::ES, P = TR<WT>::P;
+    const int lane = lane_id(), n16 = lane & 15, g = lane >> 4;
+    const int nt = gemm_nt(kind);
+    if (nt == 0) return true;
+    const int K = gemm_K(kind), nst = K / KW, nkw = gemm_npass<WT>(nst) * PassCfg<WT>::NF;
+    // this lane's row of each tile (rows past a tile's width repeat its last row)
+    const char *row[SR_MAXT];
+#pragma unroll
+    for (int t = 0; t < SR_MAXT; ++t) {
+        row[t] = nullptr;
+        if (t < nt) {
+            const GT tl = gemm_tile<WT>(kind, l, t);
+            row[t] = tl.w + (size_t)min(n16, tl.n - 1) * K * ES + (size_t)g * P * ES;
+        }
+    }
+    for (int j = 0; j < nkw; ++j) {
+#pragma unroll
+        for (int t = 0; t < SR_MAXT; ++t) {
+            if (t < nt) {
+                if (!loader_wait_free(S, ld)) return false;
+                u32x4 *dst = &S.ring[ld.seq % SR_NSLOT][0][0];
+#pragma unroll
+                for (int v = 0; v < SR_CW; ++v) {
+                    int ks = v * nkw + j;
+                    ks = ks < nst ? ks : 0;
+                    dma16(row[t] + (size_t)ks * KW * ES, dst + v * 64);
+                }
+                loader_commit(S, ld);
+            }
+        }
+    }
+    return true;
+}
+
+template <int WT, int D>
+__device__ __forceinline__ bool load_attn(SrLds &S, Loader &ld, int l) {
+    using A = AT<WT, D>;
+    AItem it;
+    if (!attn_item(it)) return true;
+    const int lane = lane_id(), n16 = lane & 15, g = lane >> 4;
+    const char *kc = SS.kc + (size_t)l * SS.kv_lstride;
+    const char *vc = SS.vc + (size_t)l * SS.kv_lstride;
+    const int cap = SS.cap;
+    for (int blk = 0; blk < it.nblk; ++blk) {
+        const int k0 = it.k_lo + 32 * blk;
+        for (int sl = 0; sl < A::SLOTS; ++sl) {
+            if (!loader_wait_free(S, ld)) return false;
+            u32x4 *dst = &S.ring[ld.seq % SR_NSLOT][0][0];
+#pragma unroll
+            for (int v = 0; v < SR_CW; ++v) {
+                const int idx = sl * 8 + v;
+                const char *src;
+                if (idx < A::KP) {
+                    const int kt = idx / A::NC, c = idx - kt * A::NC;
+                    int key = k0 + 8 * (n16 >> 2) + 4 * kt + (n16 & 3);
+                    key = key < it.k_hi ? key : it.k_lo;                      // masked later
+                    src = kc + (((size_t)it.h * cap + key) * D) * A::KVB + c * 64 + g * 16;
+                } else {
+                    const int q = idx - A::KP, t = q / A::VH, hv = q - t * A::VH;
+                    int key = k0 + 8 * g + 4 * hv;
+                    key = key < it.k_hi ? key : it.k_lo;                      // masked later
+                    src = vc + (((size_t)it.h * D + 16 * t + n16) * cap + key) * A::KVB;
+                }
+                dma16(src, dst + v * 64);
+            }
+            loader_commit(S, ld);
+        }
+    }
+    return true;
+}
+
+template <int WT, int D>
+__device__ __forceinline__ void loader_main(SrLds &S) {
+    Loader ld{0u, 0u};
+    const int nl = SS.nl, np = npl();
+    bool ok = true;
+    for (int l = 0; l < nl && ok; ++l) {
+        for (int i = 0; i < np && ok; ++i) {
+            const int k = kind_at(i);
+            const unsigned p = 1 + (unsigned)(l * np + i);
+            trace_at(p, 3);
+            if (k == K_A) ok = load_attn<WT, D>(S, ld, l);
+            else if (k != K_M) ok = load_gemm<WT>(S, ld, k, l);
+            trace_at(p, 4);
+        }
+    }
+    vm_wait();
+    if (ok) lds_st_nodep(&S.pub, ld.seq);
+}
+
+// ---------------------------------------------------------------------------
+// compute waves: ring consumption
+// ---------------------------------------------------------------------------
+struct Cons {
+    unsigned seq;       // next slot to use
+    unsigned avail;     // slots known published
+};
+
+__device__ __forceinline__ bool ring_wait(SrLds &S, Cons &c, unsigned upto) {   // slots < upto available
+    upto = __builtin_amdgcn_readfirstlane(upto);
+    c.avail = __builtin_amdgcn_readfirstlane(c.avail);
+    int spins = 0;
+    while (c.avail < upto) {
+        c.avail = lds_ld(&S.pub);
+        if (c.avail >= upto) break;
+        if (lds_ld(&S.abort_)) return false;
+        if (++spins > SPIN_LIMIT) { set_error(S); return false; }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return true;
+}
+__device__ __forceinline__ void ring_release(SrLds &S, unsigned upto) {
+    cbar();
+    lds_st(&S.cons[threadIdx.x >> 6], upto);
+}
+
+// wait until `p` global phases are complete (wave 0 polls, the others read LDS)
+__device__ __forceinline__ bool wait_phase(SrLds &S, unsigned p, unsigned E) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int spins = 0;
+    if (wave == 0) {
+        const int x = lane & 7;
+        const unsigned nwg = gridDim.x;
+        const unsigned per = nwg > (unsigned)x ? (nwg - x + 7) / 8 : 0u;
+        const unsigned want = (E + p) * per;
+        unsigned *ctr = SS.ctr + x * 32;
+        while (true) {
+            const unsigned v = ldc_u(ctr);
+            if (__all((int)(v - want) >= 0)) break;
+            if (lds_ld(&S.abort_)) return false;
+            if (++spins > SPIN_LIMIT) { set_error(S); return false; }
+        }
+        if (blockIdx.x == 0 && lane == 0) {
+            if (SS.trace && 8 * p < SR_TRACE) SS.trace[8 * p] = wall_clock64();
+            // every workgroup has read the epoch before signalling phase 0
+            if (p == 1) stc_u(SS.ctr + SR_CTR_EPOCH, E + 1 + (unsigned)SS.nl * npl());
+        }
+        lds_st(&S.phase, p);
+        return true;
+    }
+    while (lds_ld(&S.phase) < p) {
+        if (lds_ld(&S.abort_)) return false;
+        if (++spins > SPIN_LIMIT) { set_error(S); return false; }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return true;
+}
+
+// 1/rms of the 16 rows from partial sums of squares [16][nwg] (wave 0).
+// Lane (r, q) sums workgroups q, q + 4, ...; every load is issued before the
+// first add.
+__device__ __forceinline__ void compute_rinv(SrLds &S, const float *ssq, unsigned p, int width) {
+    const int lane = lane_id(), r = lane & 15, q = lane >> 4;
+    const int nwg = gridDim.x;
+    const float *src = ssq + (size_t)r * nwg;
+    constexpr int NPL = 256 / 4;                       // workgroups per lane at most
+    float v[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int w = q + 4 * i;
+        v[i] = src[w < nwg ? w : 0];
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) s += q + 4 * i < nwg ? v[i] : 0.f;
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    if (q == 0) S.rinv[r] = 1.f / sqrtf(s / (float)width + SS.eps);
+    cbar();
+    if (lane == 0) lds_st(&S.rphase, p + 1);
+}
+__device__ __forceinline__ bool wait_rinv(SrLds &S, unsigned p) {
+    int spins = 0;
+    while (lds_ld(&S.rphase) < p + 1) {
+        if (lds_ld(&S.abort_)) return false;
+        if (++spins > SPIN_LIMIT) { set_error(S); return false; }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    cbar();
+    return true;
+}
+
+// arrival of a compute wave; true for the last of the eight
+__device__ __forceinline__ bool arrive(SrLds &S) {
+    cbar();
+    unsigned old = 0;
+    if ((threadIdx.x & 63) == 0) old = lds_add(&S.done, 1u);
+    old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
+    cbar();
+    return (old & 7u) == 7u;
+}
+__device__ __forceinline__ void signal_phase() {
+    vm_wait();
+    if ((threadIdx.x & 63) == 0) add_u(SS.ctr + (blockIdx.x & 7) * 32, 1u);
+}
+// wave 1 of workgroup 0: stamp k of phase p at trace word 512 + 8p + k
+__device__ __forceinline__ void dbg_at(unsigned p, int k) {
+    if (blockIdx.x == 0 && (threadIdx.x >> 6) == 1 && (threadIdx.x & 63) == 0 && SS.trace && 8 * p + k < 512)
+        SS.trace[512 + 8 * p + k] = wall_clock64();
+}
+// every workgroup's signal time of phases 7..18 (trace words 1024 + 256 (p - 7) + w)
+__device__ __forceinline__ void trace_all(unsigned p) {
+    if ((threadIdx.x & 63) == 0 && SS.trace && p >= 7 && p < 19) SS.trace[1024 + 256 * (p - 7) + blockIdx.x] = wall_clock64();
+}
+
+// ---------------------------------------------------------------------------
+// residual slice -> next GEMM input (X * gain in fragment order) and partial
+// sums of squares; with gain == nullptr only the sums (final norm)
+// ---------------------------------------------------------------------------
+template <int WT>
+__device__ __forceinline__ void emit_input(SrLds &S, const float *gain, char *frag, float *ssq) {
+    const int lane = lane_id();
+    const int ch = SS.ch, c0 = blockIdx.x * SS.ch, nq = ch / 4;
+    if (frag && gain) {
+        for (int i = lane; i < 16 * nq; i += 64) {
+            const int r = i / nq, q = i - r * nq, c = 4 * q;
+            const float4 gg = *reinterpret_cast<const float4 *>(gain + c0 + c);
+            put4<WT>(frag, r, c0 + c, S.xown[r][c] * gg.x, S.xown[r][c + 1] * gg.y, S.xown[r][c + 2] * gg.z,
+                     S.xown[r][c + 3] * gg.w);
+        }
+    }
+    if (lane < 16) {
+        float s = 0.f;
+        for (int c = 0; c < ch; ++c) s += S.xown[lane][c] * S.xown[lane][c];
+        st4(ssq, ((size_t)lane * gridDim.x + blockIdx.x) * 4, __float_as_uint(s));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM phase (compute waves)
+// ---------------------------------------------------------------------------
+template <int WT>
+__device__ __forceinline__ void mac(f32x4 &acc, const u32x4 &w, const u32x4 *a) {
+    if constexpr (WT == WT_BF16) {
+        acc = mfma_bf16(__builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, a[0]), acc);
+    } else if constexpr (WT == WT_FP8) {
+        acc = mfma_bf16(fp8x8_to_bf16x8(w.x, w.y), __builtin_bit_cast(bf16x8, a[0]), acc);
+        acc = mfma_bf16(fp8x8_to_bf16x8(w.z, w.w), __builtin_bit_cast(bf16x8, a[1]), acc);
+    } else {
+        acc = mfma_f32(f_of(w.x), f_of(a[0].x), acc);
+        acc = mfma_f32(f_of(w.y), f_of(a[0].y), acc);
+        acc = mfma_f32(f_of(w.z), f_of(a[0].z), acc);
+        acc = mfma_f32(f_of(w.w), f_of(a[0].w), acc);
+    }
+}
+
+// DFlash2 prepare conv on the staged activations of one k step ([DflashDraft]
+// "d2_conv_prepare"): xc[r,c] = (b[c,0] + D[r,g(c),0]) xn[r-1,c] + (b[c,1] +
+// D[r,g(c),1]) xn[r,c], xn = (X * gain) / rms, xn[-1] = 0.
+template <int WT>
+__device__ __forceinline__ void d2_prepare(SrLds &S, u32x4 *a, int kstep, const float *base, const float *Dc) {
+    constexpr int KW = TR<WT>::KW, P = TR<WT>::P, AFR = TR<WT>::AFR;
+    const int lane = lane_id(), r = lane & 15, g = lane >> 4;
+    const int c0 = kstep * KW + g * P;
+    const int G = SS.d2, grp = c0 * G / SS.H;
+    const float ri = S.rinv[r], rp = r > 0 ? S.rinv[r - 1] : 0.f;
+    const float d0 = Dc[r * 4 * G + 2 * grp], d1 = Dc[r * 4 * G + 2 * grp + 1];
+    float x[P];
+    if constexpr (TR<WT>::AB == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = f_of(a[0][i]);
+    } else {
+#pragma unroll
+        for (int f = 0; f < AFR; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[8 * f + 2 * i] = bf16_bits_to_f32(a[f][i] & 0xFFFFu);
+                x[8 * f + 2 * i + 1] = __uint_as_float(a[f][i] & 0xFFFF0000u);
+            }
+    }
+    float y[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const float xp = __shfl(x[i], lane - 1, 64);
+        const float2 bb = *reinterpret_cast<const float2 *>(base + (size_t)(c0 + i) * 2);
+        y[i] = (bb.x + d0) * (r > 0 ? xp * rp : 0.f) + (bb.y + d1) * (x[i] * ri);
+    }
+    if constexpr (TR<WT>::AB == 4) {
+        a[0] = u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
+    } else {
+#pragma unroll
+        for (int f = 0; f < AFR; ++f)
+            a[f] = u32x4{bf2(y[8 * f], y[8 * f + 1]), bf2(y[8 * f + 2], y[8 * f + 3]), bf2(y[8 * f + 4], y[8 * f + 5]),
+                         bf2(y[8 * f + 6], y[8 * f + 7])};
+    }
+}
+
+// the epilogue's view of one tile: lane (r, g) holds columns 4g..4g+3 of row r
+template <int WT>
+__device__ __forceinline__ f32x4 tile_sum(SrLds &S, int t) {
+    const int lane = lane_id();
+    f32x4 s = S.red[0][t][lane];
+#pragma unroll
+    for (int v = 1; v < SR_CW; ++v) s += S.red[v][t][lane];
+    return s;
+}
+
+// DFlash2 finish conv ([DflashDraft] "d2_conv_finish") of 4 columns of row r:
+// y'[r,c] = (b[c,0] + D[r,G+g(c),0]) y[r-1,c] + (b[c,1] + D[r,G+g(c),1]) y[r,c]
+__device__ __forceinline__ void d2_finish(float (&y)[4], int r, int c, const float *base, const float *Dc) {
+    const int lane = lane_id();
+    const int G = SS.d2, grp = c * G / SS.H;
+    const float d0 = Dc[r * 4 * G + 2 * (G + grp)], d1 = Dc[r * 4 * G + 2 * (G + grp) + 1];
+    const float *b1 = base + 2 * (size_t)SS.H;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float yp = __shfl(y[i], lane - 1, 64);
+        const float2 bb = *reinterpret_cast<const float2 *>(b1 + (size_t)(c + i) * 2);
+        y[i] = (bb.x + d0) * (r > 0 ? yp : 0.f) + (bb.y + d1) * y[i];
+    }
+}
+
+template <int WT, int D, bool C>
+__device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigned p, int nt) {
+    const int lane = lane_id(), r = lane & 15, g = lane >> 4;
+    char *lb = layer_buf(l), *ln = layer_buf(l + 1);
+    constexpr bool d2 = C;
+    const int b = SS.b;
+    if (kind == K_Q || kind == K_G || kind == K_DA || kind == K_DM)
+        if (!wait_rinv(S, p)) return;
+    const float rs = S.rinv[r];
+    if (kind == K_Q) {
+        constexpr int PQ = AT<WT, D>::PQ, KSA = 4 * PQ, AB = TR<WT>::AB;
+        char *qkv = lb + SS.o_qkv;
+        const size_t koff = (size_t)16 * SS.qd * AB, voff = (size_t)16 * (SS.qd + SS.kvd) * AB;
+        char *vcache = SS.vc + (size_t)l * SS.kv_lstride;
+        for (int t = 0; t < nt; ++t) {
+            const GT tl = gemm_tile<WT>(K_Q, l, t);
+            const f32x4 sum = tile_sum<WT>(S, t);
+            const int cl = 4 * g;
+            if (cl >= tl.n) continue;
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = sum[i] * (d2 ? 1.f : rs) * (tl.sc ? tl.sc[cl + i] : 1.f);
+            const int col = tl.col + cl;
+            if (tl.seg < 2) {
+                const int hh = col / D, dd = col - hh * D;
+                const int s = dd / KSA, rem = dd - s * KSA, g2 = rem / PQ, j = rem - g2 * PQ;
+                const size_t e = ((size_t)(hh * 16 + r) * 4 + g2) * (D / 4) + s * PQ + j;
+                char *dst = qkv + (tl.seg == 1 ? koff : 0);
+                if constexpr (AB == 4) st16(dst, e * 4, u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])});
+                else st8(dst, e * 2, u32x2{bf2(y[0], y[1]), bf2(y[2], y[3])});
+            } else {
+                const int hh = col / D, dd = col - hh * D;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const size_t e = ((size_t)hh * D + dd + i) * 16 + r;          // V^T of the block
+                    const size_t ce = ((size_t)hh * D + dd + i) * SS.cap + SS.len + r;
+                    if constexpr (AB == 4) {
+                        st4(qkv + voff, e * 4, __float_as_uint(y[i]));
+                        if (r < b) st4(vcache, ce * 4, __float_as_uint(y[i]));
+                    } else {
+                        const uint16_t hb = (uint16_t)f32_to_bf16_bits(y[i]);
+                        st2(qkv + voff, e * 2, hb);
+                        if (r < b) st2(vcache, ce * 2, hb);
+                    }
+                }
+            }
+        }
+    } else if (kind == K_O || kind == K_D) {
+        const int c0 = blockIdx.x * SS.ch;
+        const float *base = nullptr, *Dc = nullptr;
+        if constexpr (C) {
+            base = kind == K_O ? ka()->L[l].abase : ka()->L[l].mbase;
+            Dc = (const float *)(lb + (kind == K_O ? SS.o_da : SS.o_dm));
+        }
+        for (int t = 0; t < nt; ++t) {
+            const GT tl = gemm_tile<WT>(kind, l, t);
+            const f32x4 sum = tile_sum<WT>(S, t);
+            const int cl = 4 * g;
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = sum[i] * (tl.sc && cl < tl.n ? tl.sc[cl + i] : 1.f);
+            if constexpr (C) d2_finish(y, r, tl.col + cl, base, Dc);
+            if (cl < tl.n) {
+                const int xc = tl.col - c0 + cl;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S.xown[r][xc + i] += r < b ? y[i] : 0.f;
+            }
+        }
+        cbar();
+        __builtin_amdgcn_wave_barrier();
+        if (kind == K_O) {
+            emit_input<WT>(S, ka()->L[l].g_post, lb + SS.o_xm, (float *)(lb + SS.o_ssm));
+        } else {
+            const bool more = l + 1 < SS.nl;
+            emit_input<WT>(S, more ? ka()->L[l + 1].g_in : nullptr, more ? ln + SS.o_xa : nullptr, (float *)(ln + SS.o_ssa));
+            if (!more && !SS.last) {
+                for (int i = lane; i < 16 * SS.ch; i += 64) {
+                    const int rr = i / SS.ch, c = i - rr * SS.ch;
+                    st4(SS.xsave, ((size_t)rr * SS.H + c0 + c) * 4, __float_as_uint(S.xown[rr][c]));
+                }
+            }
+        }
+    } else if (kind == K_G) {
+        const int ntg = nt / 2;
+        char *zf = lb + SS.o_zf;
+        for (int t = 0; t < ntg; ++t) {
+            const GT tg = gemm_tile<WT>(K_G, l, t), tu = gemm_tile<WT>(K_G, l, t + ntg);
+            const f32x4 sg = tile_sum<WT>(S, t), su = tile_sum<WT>(S, t + ntg);
+            const int cl = 4 * g;
+            if (cl >= tg.n) continue;
+            float z[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float gv = sg[i] * (d2 ? 1.f : rs) * (tg.sc ? tg.sc[cl + i] : 1.f);
+                const float uv = su[i] * (d2 ? 1.f : rs) * (tu.sc ? tu.sc[cl + i] : 1.f);
+                z[i] = r < b ? gv / (1.f + __expf(-gv)) * uv : 0.f;
+            }
+            put4<WT>(zf, r, tg.col + cl, z[0], z[1], z[2], z[3]);
+        }
+    } else {   // K_DA, K_DM: dynamic conv coefficients D[r][j] = rinv[r] * s_j * (X * g)[r] . W_dyn[j]
+        if (nt > 0) {
+            const GT tl = gemm_tile<WT>(kind, l, 0);
+            const f32x4 sum = tile_sum<WT>(S, 0);
+            float *Dc = (float *)(lb + (kind == K_DA ? SS.o_da : SS.o_dm));
+            const int cl = 4 * g;
+            if (cl < tl.n) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st4(Dc, ((size_t)r * 4 * SS.d2 + tl.col + cl + i) * 4,
+                        __float_as_uint(sum[i] * rs * (tl.sc ? tl.sc[cl + i] : 1.f)));
+            }
+        }
+    }
+}
+
+// One pass of NF k steps with the pass's activations in registers.
+template <int WT, bool C>
+__device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, unsigned &slot, u32x4 *a, int ks, int nst, int nt, bool conv,
+                                          const float *cbase, const float *cD, f32x4 (&acc)[SR_MAXT]) {
+    constexpr int AFR = TR<WT>::AFR, NF = PassCfg<WT>::NF;
+    const int lane = lane_id(), v = wave_id();
+    const u32x4 *ringv = &S.ring[0][v][lane];
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+        u32x4 *aj = &a[j * AFR];
+        const bool live = ks + j < nst;
+        if constexpr (C) {
+            if (conv && live) d2_prepare<WT>(S, aj, ks + j, cbase, cD);
+        }
+        if (!ring_wait(S, cs, cs.seq + nt)) return false;
+#pragma unroll
+        for (int t = 0; t < SR_MAXT; ++t) {
+            if (t < nt) {
+                const u32x4 wv = ringv[(size_t)slot * (SR_SLOT / 16)];
+                slot = __builtin_amdgcn_readfirstlane(slot + 1 == SR_NSLOT ? 0 : slot + 1);
+                if (live) mac<WT>(acc[t], wv, aj);
+            }
+        }
+        cs.seq = __builtin_amdgcn_readfirstlane(cs.seq + nt);
+        ring_release(S, cs.seq);
+    }
+    return true;
+}
+
+// all k steps of one wave: up to SR_MAXPASS passes, activations double-buffered
+template <int WT, bool C>
+__device__ __forceinline__ bool gemm_steps(SrLds &S, Cons &cs, const char *act, int ks0, int nst, int nt, int npass, bool conv,
+                                           const float *cbase, const float *cD, f32x4 (&acc)[SR_MAXT], unsigned p) {
+    constexpr int AFR = TR<WT>::AFR, NF = PassCfg<WT>::NF;
+    u32x4 a0[NF * AFR], a1[NF * AFR];
+    auto load_pass = [&](int ps, u32x4 *dst) {
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+            int ks = ks0 + ps * NF + j;
+            ks = ks < nst ? ks : 0;                   // dead steps reread step 0
+#pragma unroll
+            for (int f = 0; f < AFR; ++f)
+                dst[j * AFR + f] = *reinterpret_cast<const u32x4 *>(act + (size_t)ks * 64 * 16 * AFR + 16 * f);
+        }
+    };
+    unsigned slot = __builtin_amdgcn_readfirstlane(cs.seq % SR_NSLOT);
+    load_pass(0, a0);
+    if (npass > 1) load_pass(1, a1);
+    if (blockIdx.x == 0 && (threadIdx.x >> 6) == 1 && SS.trace) {
+        vm_wait();
+        dbg_at(p, 1);
+        if (!ring_wait(S, cs, cs.seq + nt)) return false;
+        dbg_at(p, 4);
+    }
+    if (!gemm_pass<WT, C>(S, cs, slot, a0, ks0, nst, nt, conv, cbase, cD, acc)) return false;
+    if (npass > 1) {
+        if (npass > 2) load_pass(2, a0);
+        if (!gemm_pass<WT, C>(S, cs, slot, a1, ks0 + NF, nst, nt, conv, cbase, cD, acc)) return false;
+        if (npass > 2) {
+            if (!gemm_pass<WT, C>(S, cs, slot, a0, ks0 + 2 * NF, nst, nt, conv, cbase, cD, acc)) return false;
+        }
+    }
+    return true;
+}
+
+// Kept out of line: inlining every phase into one function makes the
+// register allocator spill heavily.  Arguments arrive in VGPRs and are made
+// scalar again.
+// Returns the consumer's next ring slot, or ~0u if the kernel is aborting.
+template <int WT, int D, bool C>
+__device__ __attribute__((noinline)) unsigned gemm_phase(int kind, int l, unsigned p, unsigned seq) {
+    constexpr int KW = TR<WT>::KW, AFR = TR<WT>::AFR;
+    kind = __builtin_amdgcn_readfirstlane(kind);
+    l = __builtin_amdgcn_readfirstlane(l);
+    p = __builtin_amdgcn_readfirstlane(p);
+    Cons cs{(unsigned)__builtin_amdgcn_readfirstlane(seq), 0u};
+    const int lane = lane_id(), v = wave_id();
+    const int nt = gemm_nt(kind);
+    char *lb = layer_buf(l);
+    if (nt > 0) {
+        const int K = gemm_K(kind), nst = K / KW, npass = gemm_npass<WT>(nst);
+        const char *act;
+        switch (kind) {
+            case K_O: act = lb + SS.o_of; break;
+            case K_G: case K_DM: act = lb + SS.o_xm; break;
+            case K_D: act = lb + SS.o_zf; break;
+            default: act = lb + SS.o_xa; break;     // K_Q, K_DA
+        }
+        act += (size_t)lane * 16 * AFR;
+        const int ks0 = v * npass * PassCfg<WT>::NF;
+        const bool conv = C && (kind == K_Q || kind == K_G);
+        const float *cbase = nullptr, *cD = nullptr;
+        if (conv) {
+            if (!wait_rinv(S, p)) return ~0u;
+            cbase = kind == K_Q ? ka()->L[l].abase : ka()->L[l].mbase;
+            cD = (const float *)(lb + (kind == K_Q ? SS.o_da : SS.o_dm));
+        }
+        f32x4 acc[SR_MAXT];
+#pragma unroll
+        for (int t = 0; t < SR_MAXT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dbg_at(p, 0);
+        const bool ok = gemm_steps<WT, C>(S, cs, act, ks0, nst, nt, npass, conv, cbase, cD, acc, p);
+        dbg_at(p, 2);
+        if (!ok) return ~0u;
+#pragma unroll
+        for (int t = 0; t < SR_MAXT; ++t)
+            if (t < nt) S.red[v][t][lane] = acc[t];
+    }
+    if (v == 0) trace_at(p, 1);
+    dbg_at(p, 3);
+    if (arrive(S)) {
+        if (blockIdx.x == 0) trace_at(p, 5);
+        if (nt > 0) gemm_epilogue<WT, D, C>(S, kind, l, p, nt);
+        signal_phase();
+        trace_at(p, 2);
+        trace_all(p);
+    }
+    return cs.seq;
+}
+
+// ---------------------------------------------------------------------------
+// attention phase (compute waves)
+// ---------------------------------------------------------------------------
+// q / k head vector of one lane: values (s, j) at d = KSA s + PQ g + j.
+// RMSNorm over head_dim (gain gk), NeoX rope at position pos (pairs s, s + NS/2),
+// times scale.
+template <int WT, int D>
+__device__ __forceinline__ void norm_rope(float (&x)[D / 4], const float *gk, int r, float scale) {
+    constexpr int PQ = AT<WT, D>::PQ, KSA = 4 * PQ, NS = D / KSA, NQV = AT<WT, D>::NQV;
+    const int g = lane_id() >> 4;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NQV; ++i) ss += x[i] * x[i];
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float inv = 1.f / sqrtf(ss / (float)D + SS.eps);
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int j = 0; j < PQ; ++j) x[s * PQ + j] *= inv * gk[KSA * s + PQ * g + j];
+    const float *cs = SS.cs + (size_t)r * D;      // [r][d/2][2]
+#pragma unroll
+    for (int s = 0; s < NS / 2; ++s)
+#pragma unroll
+        for (int j = 0; j < PQ; ++j) {
+            const int fi = KSA * s + PQ * g + j;
+            const float2 csv = *reinterpret_cast<const float2 *>(cs + 2 * fi);
+            const float y0 = x[s * PQ + j], y1 = x[(s + NS / 2) * PQ + j];
+            x[s * PQ + j] = (y0 * csv.x - y1 * csv.y) * scale;
+            x[(s + NS / 2) * PQ + j] = (y1 * csv.x + y0 * csv.y) * scale;
+        }
+}
+
+template <int WT, int D>
+__device__ __forceinline__ void load_head(float (&x)[D / 4], const char *src) {
+    constexpr int NQV = AT<WT, D>::NQV;
+    if constexpr (WT == WT_F32) {
+#pragma unroll
+        for (int i = 0; i < NQV; i += 4) {
+            const u32x4 u = *reinterpret_cast<const u32x4 *>(src + 4 * i);
+            x[i] = f_of(u.x); x[i + 1] = f_of(u.y); x[i + 2] = f_of(u.z); x[i + 3] = f_of(u.w);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NQV; i += 8) {
+            const u32x4 u = *reinterpret_cast<const u32x4 *>(src + 2 * i);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                x[i + 2 * k] = bf16_bits_to_f32(u[k] & 0xFFFFu);
+                x[i + 2 * k + 1] = __uint_as_float(u[k] & 0xFFFF0000u);
+            }
+        }
+    }
+}
+
+template <int WT, int D>
+struct AttnState {
+    static constexpr int NDT = D / 16;
+    float m, l;
+    f32x4 o[NDT];
+};
+
+// one 32-key block: S^T = K Q^T (two key tiles; lane (q, g) ends up with keys
+// 8g..8g+7), online softmax, O^T += V^T P^T.  kf(kt, c) / vf(t, hv) return
+// the A fragments; valid(i) tells whether key 8g + i of the block exists.
+template <int WT, int D, class KF, class VF, class VALID>
+__device__ __forceinline__ void attn_block(AttnState<WT, D> &st, const u32x4 *qf, KF kf, VF vf, VALID valid) {
+    using A = AT<WT, D>;
+    constexpr int NDT = D / 16;
+    f32x4 sc4[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < A::NC; ++c) {
+            const u32x4 k = kf(kt, c);
+            if constexpr (WT == WT_F32) {
+                acc = mfma_f32(f_of(k.x), f_of(qf[c].x), acc);
+                acc = mfma_f32(f_of(k.y), f_of(qf[c].y), acc);
+                acc = mfma_f32(f_of(k.z), f_of(qf[c].z), acc);
+                acc = mfma_f32(f_of(k.w), f_of(qf[c].w), acc);
+            } else {
+                acc = mfma_bf16(__builtin_bit_cast(bf16x8, k), __builtin_bit_cast(bf16x8, qf[c]), acc);
+            }
+        }
+        sc4[kt] = acc;
+    }
+    float sc[8];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float x = sc4[i >> 2][i & 3];
+        sc[i] = valid(i) ? x : -INFINITY;
+        bmax = fmaxf(bmax, sc[i]);
+    }
+    bmax = group4_max(bmax);
+    const float m_new = fmaxf(st.m, bmax);
+    const float corr = __builtin_amdgcn_exp2f(st.m - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        sc[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+        psum += sc[i];
+    }
+    psum = group4_sum(psum);
+    st.l = st.l * corr + psum;
+    st.m = m_new;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) st.o[t] *= corr;
+    if constexpr (WT == WT_F32) {
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+            const u32x4 v0 = vf(t, 0), v1 = vf(t, 1);
+            const float vk[8] = {f_of(v0.x), f_of(v0.y), f_of(v0.z), f_of(v0.w), f_of(v1.x), f_of(v1.y), f_of(v1.z), f_of(v1.w)};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) st.o[t] = mfma_f32(valid(i) ? vk[i] : 0.f, sc[i], st.o[t]);
+        }
+    } else {
+        const bf16x8 pb = to_bf16x8(sc);
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+            u32x4 vv = vf(t, 0);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t msk = (valid(2 * w) ? 0x0000FFFFu : 0u) | (valid(2 * w + 1) ? 0xFFFF0000u : 0u);
+                vv[w] &= msk;
+            }
+            st.o[t] = mfma_bf16(__builtin_bit_cast(bf16x8, vv), pb, st.o[t]);
+        }
+    }
+}
+
+template <int WT, int D>
+__device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p) {
+    using A = AT<WT, D>;
+    constexpr int NQV = A::NQV, NC = A::NC, NDT = D / 16, AB = TR<WT>::AB;
+    const int lane = lane_id(), v = wave_id(), r16 = lane & 15, g = lane >> 4;
+    AItem it;
+    if (attn_item(it)) {
+        char *lb = layer_buf(l);
+        const char *qkv = lb + SS.o_qkv;
+        const size_t koff = (size_t)16 * SS.qd * AB, voff = (size_t)16 * (SS.qd + SS.kvd) * AB;
+        const bool actw = v < SS.G;
+        const int hq = it.h * SS.G + (actw ? v : 0);
+        // query fragments of q head hq, rows r16
+        u32x4 qf[NC];
+        {
+            float x[NQV];
+            load_head<WT, D>(x, qkv + (((size_t)(hq * 16 + r16) * 4 + g) * (D / 4)) * AB);
+            norm_rope<WT, D>(x, ka()->L[l].g_q, r16, SS.mscale * SS.qscale);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                if constexpr (WT == WT_F32) {
+                    qf[c] = u32x4{__float_as_uint(x[4 * c]), __float_as_uint(x[4 * c + 1]), __float_as_uint(x[4 * c + 2]),
+                                  __float_as_uint(x[4 * c + 3])};
+                } else {
+                    float t8[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) t8[j] = x[8 * c + j];
+                    qf[c] = __builtin_bit_cast(u32x4, to_bf16x8(t8));
+                }
+            }
+        }
+        AttnState<WT, D> st;
+        st.m = -1e30f;
+        st.l = 0.f;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (it.last && actw) {
+            // the block's own keys: normed + roped k and raw v of the b block rows
+            u32x4 kb[2][NC];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const int key = 8 * (r16 >> 2) + 4 * kt + (r16 & 3);
+                float x[NQV];
+                if (key < 16) {
+                    load_head<WT, D>(x, qkv + koff + (((size_t)(it.h * 16 + key) * 4 + g) * (D / 4)) * AB);
+                    norm_rope<WT, D>(x, ka()->L[l].g_k, key, SS.mscale);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < NQV; ++i) x[i] = 0.f;
+                }
+                if (v == 0 && key < SS.b) {   // block K row to the cache (rows len + key)
+                    constexpr int PQ = A::PQ;
+                    char *kcache = SS.kc + (size_t)l * SS.kv_lstride;
+                    const size_t rowb = (((size_t)it.h * SS.cap + SS.len + key) * D) * A::KVB;
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        const size_t off = rowb + (size_t)(4 * PQ * c + PQ * g) * A::KVB;
+                        if constexpr (WT == WT_F32)
+                            st16(kcache, off, u32x4{__float_as_uint(x[4 * c]), __float_as_uint(x[4 * c + 1]),
+                                                    __float_as_uint(x[4 * c + 2]), __float_as_uint(x[4 * c + 3])});
+                        else
+                            st16(kcache, off, u32x4{bf2(x[8 * c], x[8 * c + 1]), bf2(x[8 * c + 2], x[8 * c + 3]),
+                                                    bf2(x[8 * c + 4], x[8 * c + 5]), bf2(x[8 * c + 6], x[8 * c + 7])});
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    if constexpr (WT == WT_F32) {
+                        kb[kt][c] = u32x4{__float_as_uint(x[4 * c]), __float_as_uint(x[4 * c + 1]), __float_as_uint(x[4 * c + 2]),
+                                          __float_as_uint(x[4 * c + 3])};
+                    } else {
+                        kb[kt][c] = u32x4{bf2(x[8 * c], x[8 * c + 1]), bf2(x[8 * c + 2], x[8 * c + 3]),
+                                          bf2(x[8 * c + 4], x[8 * c + 5]), bf2(x[8 * c + 6], x[8 * c + 7])};
+                    }
+                }
+            }
+            const char *vT = qkv + voff;
+            auto kf = [&](int kt, int c) -> u32x4 { return kb[kt][c]; };
+            auto vf = [&](int t, int hv) -> u32x4 {
+                if (g >= 2) return u32x4{0, 0, 0, 0};
+                const size_t e = ((size_t)it.h * D + 16 * t + r16) * 16 + 8 * g + 4 * hv;
+                return *reinterpret_cast<const u32x4 *>(vT + e * AB);
+            };
+            const int kend = SS.b - 8 * g;
+            auto valid = [&](int i) { return i < kend; };
+            attn_block<WT, D>(st, qf, kf, vf, valid);
+        }
+        for (int blk = 0; blk < it.nblk; ++blk) {
+            const int k0 = it.k_lo + 32 * blk;
+            if (!ring_wait(S, cs, cs.seq + A::SLOTS)) return false;
+            const unsigned s0 = cs.seq;
+            if (actw) {
+                auto kf = [&](int kt, int c) -> u32x4 {
+                    const int idx = kt * NC + c;
+                    return S.ring[(s0 + idx / 8) % SR_NSLOT][idx & 7][lane];
+                };
+                auto vf = [&](int t, int hv) -> u32x4 {
+                    const int idx = A::KP + t * A::VH + hv;
+                    return S.ring[(s0 + idx / 8) % SR_NSLOT][idx & 7][lane];
+                };
+                const int kend = it.k_hi - k0 - 8 * g;
+                auto valid = [&](int i) { return i < kend; };
+                attn_block<WT, D>(st, qf, kf, vf, valid);
+            }
+            cs.seq = __builtin_amdgcn_readfirstlane(cs.seq + A::SLOTS);
+            ring_release(S, cs.seq);
+        }
+        if (actw) {
+            const int item = blockIdx.x;
+            const int GQ = SS.G * 16, qi = v * 16 + r16;
+            const size_t row = (size_t)item * GQ + qi;
+            char *po = lb + SS.o_po;
+            float *pml = (float *)(lb + SS.o_pml);
+#pragma unroll
+            for (int t = 0; t < NDT; ++t) {
+                const size_t e = row * D + 16 * t + 4 * g;
+                if constexpr (AB == 4) st16(po, e * 4, __builtin_bit_cast(u32x4, st.o[t]));
+                else st8(po, e * 2, u32x2{bf2(st.o[t][0], st.o[t][1]), bf2(st.o[t][2], st.o[t][3])});
+            }
+            if (g == 0) st8(pml, row * 8, u32x2{__float_as_uint(st.m), __float_as_uint(st.l)});
+        }
+        vm_wait();
+    }
+    if (v == 0) trace_at(p, 1);
+    if (arrive(S)) {
+        signal_phase();
+        trace_at(p, 2);
+        trace_all(p);
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// merge phase: O[r, hq] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+// written as o_proj input fragments
+// ---------------------------------------------------------------------------
+template <int WT, int D>
+__device__ __forceinline__ bool merge_phase(SrLds &S, int l, unsigned p) {
+    constexpr int AB = TR<WT>::AB;
+    constexpr int NDG = D / 8, NSG = 64 / NDG;      // d groups of 8, split groups
+    const int lane = lane_id(), v = wave_id();
+    const int dg = lane % NDG, sg = lane / NDG;
+    char *lb = layer_buf(l);
+    const char *po = lb + SS.o_po;
+    const float *pml = (const float *)(lb + SS.o_pml);
+    char *of = lb + SS.o_of;
+    const int GQ = SS.G * 16, ns = SS.nsplit;
+    const int nqry = SS.nkv * GQ;
+    for (int qq = blockIdx.x * SR_CW + v; qq < nqry; qq += gridDim.x * SR_CW) {
+        const int h = qq / GQ, qi = qq - h * GQ;
+        const int j = qi >> 4, r = qi & 15;
+        const int hq = h * SS.G + j;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float L = 1.f;
+        if (r < SS.b) {
+            float m = -1e30f, lv = 0.f;
+            if (lane < ns) {
+                const float2 ml = *reinterpret_cast<const float2 *>(pml + ((size_t)(h * ns + lane) * GQ + qi) * 2);
+                m = ml.x;
+                lv = ml.y;
+            }
+            float M = m;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+            const float w = lane < ns ? __builtin_amdgcn_exp2f(m - M) : 0.f;
+            L = wave_sum(w * lv);
+            // every split's partial is loaded before the first add
+            constexpr int NPS = SR_MAX_SPLITS / NSG;       // splits per lane at most
+            u32x4 raw[NPS][AB == 4 ? 2 : 1];
+#pragma unroll
+            for (int i = 0; i < NPS; ++i) {
+                int sp = sg + NSG * i;
+                sp = sp < ns ? sp : 0;
+                const size_t e = ((size_t)(h * ns + sp) * GQ + qi) * D + 8 * dg;
+                raw[i][0] = *reinterpret_cast<const u32x4 *>(po + e * AB);
+                if constexpr (AB == 4) raw[i][AB == 4 ? 1 : 0] = *reinterpret_cast<const u32x4 *>(po + e * AB + 16);
+            }
+#pragma unroll
+            for (int i = 0; i < NPS; ++i) {
+                const int sp = sg + NSG * i;
+                float ws = __shfl(w, sp < 64 ? sp : 63, 64);
+                ws = sp < ns ? ws : 0.f;
+                if constexpr (AB == 4) {
+                    const u32x4 a0 = raw[i][0], a1 = raw[i][AB == 4 ? 1 : 0];
+                    acc[0] += ws * f_of(a0.x); acc[1] += ws * f_of(a0.y); acc[2] += ws * f_of(a0.z); acc[3] += ws * f_of(a0.w);
+                    acc[4] += ws * f_of(a1.x); acc[5] += ws * f_of(a1.y); acc[6] += ws * f_of(a1.z); acc[7] += ws * f_of(a1.w);
+                } else {
+                    const u32x4 u = raw[i][0];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        acc[2 * k] += ws * bf16_bits_to_f32(u[k] & 0xFFFFu);
+                        acc[2 * k + 1] += ws * __uint_as_float(u[k] & 0xFFFF0000u);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int o = NDG; o < 64; o <<= 1)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] += __shfl_xor(acc[k], o, 64);
+        if (sg == 0) {
+            const float il = 1.f / L;
+            const int c = hq * D + 8 * dg;
+            put4<WT>(of, r, c, acc[0] * il, acc[1] * il, acc[2] * il, acc[3] * il);
+            put4<WT>(of, r, c + 4, acc[4] * il, acc[5] * il, acc[6] * il, acc[7] * il);
+        }
+    }
+    vm_wait();
+    if (v == 0) trace_at(p, 1);
+    if (arrive(S)) {
+        signal_phase();
+        trace_at(p, 2);
+        trace_all(p);
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// init and final phases
+// ---------------------------------------------------------------------------
+template <int WT>
+__device__ __forceinline__ bool init_phase(SrLds &S) {
+    const int lane = lane_id(), v = wave_id();
+    const int ch = SS.ch, c0 = blockIdx.x * ch, H = SS.H, b = SS.b;
+    for (int i = threadIdx.x; i < 16 * ch; i += SR_CW * 64) {
+        const int r = i / ch, c = i - r * ch;
+        float x = 0.f;
+        if (r < b) x = SS.first ? SS.noise[(size_t)r * H + c0 + c] : SS.xsave[(size_t)r * H + c0 + c];
+        S.xown[r][c] = x;
+    }
+    // cos / sin of the block positions (rows 0..b-1), angles in f64
+    if (v == 0 && (int)blockIdx.x < b) {
+        const int r = blockIdx.x, half = SS.d / 2;
+        const double p = (double)SS.pos[r];
+        for (int i = lane; i < half; i += 64) {
+            double sv, cv;
+            sincos(p * ka()->inv_freq[i], &sv, &cv);
+            st8(SS.cs, ((size_t)r * half + i) * 8, u32x2{__float_as_uint((float)cv), __float_as_uint((float)sv)});
+        }
+    }
+    vm_wait();
+    if (arrive(S)) {
+        if (SS.nl > 0) emit_input<WT>(S, ka()->L[0].g_in, layer_buf(0) + SS.o_xa, (float *)(layer_buf(0) + SS.o_ssa));
+        else emit_input<WT>(S, nullptr, nullptr, (float *)(layer_buf(0) + SS.o_ssa));
+        signal_phase();
+    }
+    return true;
+}
+
+__device__ __forceinline__ void final_phase(SrLds &S, unsigned p) {
+    const int ch = SS.ch, c0 = blockIdx.x * ch, H = SS.H, b = SS.b;
+    if (!wait_rinv(S, p)) return;
+    for (int i = threadIdx.x; i < 16 * ch; i += SR_CW * 64) {
+        const int r = i / ch, c = i - r * ch;
+        if (r < b) SS.out[(size_t)r * H + c0 + c] = SS.g_norm[c0 + c] * (S.xown[r][c] * S.rinv[r]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+template <int WT, int D, bool C>
+__device__ __forceinline__ bool compute_main(SrLds &S) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    unsigned E = 0;
+    if (wave == 0) E = __builtin_amdgcn_readfirstlane(ldc_u(SS.ctr + SR_CTR_EPOCH));
+    Cons cs{0u, 0u};
+    const int nl = SS.nl, np = npl();
+    if (!init_phase<WT>(S)) return false;
+    unsigned p = 1;
+    for (int l = 0; l < nl; ++l) {
+        for (int i = 0; i < np; ++i, ++p) {
+            if (!wait_phase(S, p, E)) return false;
+            const int k = kind_at(i);
+            char *lb = layer_buf(l);
+            if (wave == 0 && (k == K_Q || k == K_G || k == K_DA || k == K_DM))
+                compute_rinv(S, (const float *)(lb + ((k == K_Q || k == K_DA) ? SS.o_ssa : SS.o_ssm)), p, SS.H);
+            bool ok;
+            if (k == K_A) ok = attn_phase<WT, D>(S, cs, l, p);
+            else if (k == K_M) ok = merge_phase<WT, D>(S, l, p);
+            else {
+                cs.seq = gemm_phase<WT, D, C>(k, l, p, cs.seq);
+                ok = cs.seq != ~0u;
+            }
+            if (!ok) return false;
+        }
+    }
+    if (SS.last) {
+        if (!wait_phase(S, p, E)) return false;
+        if (wave == 0) compute_rinv(S, (const float *)(layer_buf(nl) + SS.o_ssa), p, SS.H);
+        final_phase(S, p);
+    }
+    return lds_ld(&S.abort_) == 0;
+}
+
+template <int WT, int D, bool C>
+__global__ __launch_bounds__(SR_THREADS, 1) void sround_kernel(SrArgs) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (threadIdx.x < 64) {
+        if (lane < SR_CW) S.cons[lane] = 0;
+        if (lane == 0) { S.pub = 0; S.phase = 0; S.rphase = 0; S.done = 0; S.abort_ = 0; }
+    }
+    __syncthreads();
+    if (wave == SR_CW) {
+        loader_main<WT, D>(S);
+        if (lds_ld_nodep(&S.abort_)) stc_u(SS.ctr + SR_CTR_ERR, 1u);
+        return;
+    }
+    // compute waves
+    if (!compute_main<WT, D, C>(S)) stc_u(SS.ctr + SR_CTR_ERR, 1u);
+}
+
+template <int WT, bool C>
+hipError_t launch_d(const SrArgs &a, int nwg, hipStream_t s) {
+    if (a.s.d == 64) hipLaunchKernelGGL((sround_kernel<WT, 64, C>), dim3(nwg), dim3(SR_THREADS), 0, s, a);
+    else if constexpr (WT != WT_F32) hipLaunchKernelGGL((sround_kernel<WT, 128, C>), dim3(nwg), dim3(SR_THREADS), 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+template <int WT>
+hipError_t launch_c(const SrArgs &a, int nwg, hipStream_t s) {
+    return a.s.d2 ? launch_d<WT, true>(a, nwg, s) : launch_d<WT, false>(a, nwg, s);
+}
+
+}  // namespace
+
+SrLayout sround_layout(int H, int I, int qd, int kvd, int nkv, int G, int d, int wt, int nwg, int d2) {
+    const long long AB = wt == WT_F32 ? 4 : 2;
+    long long off = 0;
+    auto take = [&](long long bytes) { const long long o = off; off += (bytes + 255) / 256 * 256; return o; };
+    SrLayout L;
+    L.xa = take(16 * H * AB);
+    L.ssa = take(16LL * nwg * 4);
+    L.qkv = take(16LL * (qd + 2 * kvd) * AB);
+    L.po = take((long long)nkv * SR_MAX_SPLITS * G * 16 * d * AB);
+    L.pml = take((long long)nkv * SR_MAX_SPLITS * G * 16 * 2 * 4);
+    L.of = take(16LL * qd * AB);
+    L.xm = take(16LL * H * AB);
+    L.ssm = take(16LL * nwg * 4);
+    L.zf = take(16LL * I * AB);
+    L.da = take(16LL * 4 * (d2 > 0 ? d2 : 1) * 4);
+    L.dm = take(16LL * 4 * (d2 > 0 ? d2 : 1) * 4);
+    L.stride = off;
+    return L;
+}
+
+// tiles of 16 columns that workgroup w gets of the concatenated q|k|v outputs
+static int q_tiles(int w, int cq, int qd, int kvd) {
+    const int c0 = w * cq, c1 = c0 + cq;
+    const int a[3] = {0, qd, qd + kvd}, e[3] = {qd, qd + kvd, qd + 2 * kvd};
+    int nt = 0;
+    for (int s = 0; s < 3; ++s) {
+        const int lo = c0 > a[s] ? c0 : a[s], hi = c1 < e[s] ? c1 : e[s];
+        if (hi > lo) nt += (hi - lo + 15) / 16;
+    }
+    return nt;
+}
+
+int sround_nwg(int H, int I, int qd, int kvd, int wt, int d2, int cus) {
+    const int nqkv = qd + 2 * kvd;
+    const int kw = wt == WT_BF16 ? 32 : wt == WT_FP8 ? 64 : 16;
+    const int nf = wt == WT_FP8 ? 4 : 8;
+    for (const int K : {H, I, qd}) {
+        if (K % kw) return 0;
+        const int nkw = (K / kw + SR_CW - 1) / SR_CW;
+        if ((nkw + nf - 1) / nf > 3) return 0;      // passes built per GEMM
+    }
+    for (int n = cus < 256 ? cus : 256; n >= 1; --n) {
+        if (H % n || I % n || nqkv % n) continue;
+        const int ch = H / n, ci = I / n, cq = nqkv / n;
+        if (ch % 4 || ci % 4 || cq % 4 || ch > SR_MAXCH) continue;
+        if ((ch + 15) / 16 > SR_MAXT || 2 * ((ci + 15) / 16) > SR_MAXT) continue;
+        bool ok = true;
+        for (int w = 0; w < n && ok; ++w) ok = q_tiles(w, cq, qd, kvd) <= SR_MAXT;
+        if (!ok) continue;
+        if (d2 > 0 && 4 * d2 > 16 * n) continue;
+        return n;
+    }
+    return 0;
+}
+
+hipError_t sround_launch(const SrArgs &a, int wt, int nwg, hipStream_t s) {
+    switch (wt) {
+        case WT_F32: return launch_c<WT_F32>(a, nwg, s);
+        case WT_BF16: return launch_c<WT_BF16>(a, nwg, s);
+        default: return launch_c<WT_FP8>(a, nwg, s);
+    }
+}
+
+}  // namespace dfl

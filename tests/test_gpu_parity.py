@@ -19,8 +19,8 @@ SMALL_BF16 = synth.DraftConfig(
     name="small_bf16", n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64,
     intermediate=768, n_taps=2, weight_dtype="bf16", kv_dtype="bf16", path="round",
     ctx=100, block=16, seed=21)
-# head_dim 128 with 16 q heads on one kv head: 256 queries per kv head, two attention passes
-SMALL_BF16_D128 = SMALL_BF16.replace(name="small_bf16_d128", hidden=1024, n_q_heads=16, n_kv_heads=1,
+# head_dim 128 with 8 q heads on one kv head (128 queries per kv head)
+SMALL_BF16_D128 = SMALL_BF16.replace(name="small_bf16_d128", hidden=1024, n_q_heads=8, n_kv_heads=1,
                                      head_dim=128, seed=22)
 # fp8 e4m3fn weights with per-row f32 scales
 SMALL_FP8 = SMALL_BF16.replace(name="small_fp8", weight_dtype="fp8", seed=23)
@@ -149,10 +149,11 @@ def test_d2_identity_taps_equal_backbone():
     """DFlash2 special case: with zero dynamic projections and static taps
     [0, 1] the wrap is the identity, so the output equals the same weights
     without the wrap (the conv path and the plain path run different code).
-    The two agree to rounding only: the conv path splits the normalised rows
-    x*g/rms into bf16 hi + lo halves (about 16 significant bits, ~1e-5
-    relative) before the GEMM, the plain path splits x*g and scales after, so
-    they round different values; 1e-4 bounds that over two layers."""
+    The two agree to rounding only: GEMM inputs are bf16 (8 significant
+    bits, 2^-9 relative), and the conv path rounds the normalised rows
+    x*g/rms after the conv while the plain path rounds x*g and applies 1/rms
+    to the GEMM output, so they round different values.  Over two layers that
+    stays within a few times 2^-9; 2e-3 is the bound used."""
     from block_diffusion_drafter_round_amd import dflash as D
     cfg = SMALL_D2
     sw = synth.make_weights(cfg)
@@ -168,7 +169,7 @@ def test_d2_identity_taps_equal_backbone():
     taps, noise, pos = synth.make_taps(cfg, n), synth.make_noise(cfg), synth.positions(0, n + b)
     o_d2 = host(D.Drafter(sw, max_rows=n).forward_full(dev(taps), dev(noise), dev(pos)))
     o_plain = host(D.Drafter(plain, max_rows=n).forward_full(dev(taps), dev(noise), dev(pos)))
-    check("d2 identity taps vs plain backbone", o_d2, o_plain, 1e-4)
+    check("d2 identity taps vs plain backbone", o_d2, o_plain, 2e-3)
 
 
 def test_errors_leave_state_unchanged():
