@@ -10,13 +10,13 @@ constexpr int SR_THREADS = 64 * (SR_CW + 1);  // plus one loader wave
 constexpr int SR_PART = 1024;                 // one wave-wide load: 64 lanes x 16 bytes
 constexpr int SR_SLOT = SR_CW * SR_PART;      // a ring slot holds one part per compute wave
 constexpr int SR_NSLOT = 15;                  // ring slots (120 KiB of LDS)
-constexpr int SR_DEPTH = 7;                   // slots the loader keeps in flight (7 x 8 loads <= vmcnt 63)
+constexpr int SR_DEPTH = 3;                   // slots the loader keeps in flight (3 x 8 loads)
 constexpr int SR_MAXT = 4;                    // output tiles of 16 columns per workgroup and GEMM
 constexpr int SR_MAXSTEP = 24;                // k steps of one wave per GEMM
 constexpr int SR_ACTREG = 12;                 // 16-byte activation fragments a lane holds at once
 constexpr int SR_MAXL = 8;                    // layers per launch
 constexpr int SR_MAX_SPLITS = 64;             // attention key splits per kv head
-constexpr int SR_MAXCH = 64;                  // residual columns owned by one workgroup
+constexpr int SR_MAXCH = 48;                  // residual columns owned by one workgroup
 constexpr int SR_MAXG = 8;                    // q heads per kv head
 constexpr int SR_MAX_D2 = 64;                 // DFlash2 conv groups
 constexpr int SR_TRACE = 4096;                // phase time stamps

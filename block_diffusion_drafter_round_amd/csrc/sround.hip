@@ -172,11 +172,13 @@ __device__ __forceinline__ void put4(void *buf, int r, int c, float x0, float x1
 // ---------------------------------------------------------------------------
 // LDS
 // ---------------------------------------------------------------------------
+static_assert(64 + SR_MAXCH <= 128, "aux holds 64 scales then the gains");
 struct SrLds {
     u32x4 ring[SR_NSLOT][SR_CW][64];
     f32x4 red[SR_CW][SR_MAXT][64];
     float xown[16][SR_MAXCH];
     float rinv[16];
+    float aux[128];            // epilogue constants of the phase: fp8 scales [tile][16], gains [64..)
     unsigned cons[SR_CW];      // slots each compute wave has released
     unsigned pub;              // slots the loader has published
     unsigned phase;            // global phases known complete
@@ -237,25 +239,40 @@ __device__ __forceinline__ int gemm_K(int kind) {
     return kind == K_O ? SS.qd : kind == K_D ? SS.I : SS.H;
 }
 
+// Tiles of a run of m columns (m a multiple of 4): 16-wide tiles, then the
+// remainder as an 8-wide and/or a 4-wide tile, so every tile is 16, 8 or 4
+// columns wide (a narrow tile packs 2 or 4 k steps into one ring part).
+__device__ __forceinline__ int run_tiles(int m) {
+    const int r = m & 15;
+    return (m >> 4) + (r == 12 ? 2 : r ? 1 : 0);
+}
+// first column (relative to the run) and width of tile t of a run of m
+__device__ __forceinline__ void run_tile(int m, int t, int &c, int &n) {
+    const int full = m >> 4, r = m & 15;
+    if (t < full) { c = 16 * t; n = 16; return; }
+    c = 16 * full;
+    if (r == 12) { if (t == full) n = 8; else { c += 8; n = 4; } }
+    else n = r;
+}
+
 // number of tiles of this workgroup for a GEMM phase
 __device__ __forceinline__ int gemm_nt(int kind) {
     const int w = blockIdx.x;
     switch (kind) {
         case K_Q: {
             const int c0 = w * SS.cq, c1 = c0 + SS.cq;
-            const int b1 = SS.qd, b2 = SS.qd + SS.kvd, b3 = SS.qd + 2 * SS.kvd;
+            const int a[3] = {0, SS.qd, SS.qd + SS.kvd}, e[3] = {SS.qd, SS.qd + SS.kvd, SS.qd + 2 * SS.kvd};
             int nt = 0;
-            const int a[3] = {0, b1, b2}, e[3] = {b1, b2, b3};
 #pragma unroll
             for (int s = 0; s < 3; ++s) {
                 const int lo = max(c0, a[s]), hi = min(c1, e[s]);
-                if (hi > lo) nt += (hi - lo + 15) / 16;
+                if (hi > lo) nt += run_tiles(hi - lo);
             }
             return nt;
         }
-        case K_O: case K_D: return (SS.ch + 15) / 16;
-        case K_G: return 2 * ((SS.ci + 15) / 16);
-        default: return 16 * w < 4 * SS.d2 ? 1 : 0;     // K_DA, K_DM
+        case K_O: case K_D: return run_tiles(SS.ch);
+        case K_G: return 2 * run_tiles(SS.ci);
+        default: return 16 * w < 4 * SS.d2 ? run_tiles(min(16, 4 * SS.d2 - 16 * w)) : 0;     // K_DA, K_DM
     }
 }
 
@@ -279,11 +296,12 @@ __device__ __forceinline__ GT gemm_tile(int kind, int l, int t) {
             for (int s = 0; s < 3; ++s) {
                 const int lo = max(c0, a[s]), hi = min(c1, e[s]);
                 if (hi > lo) {
-                    const int n = (hi - lo + 15) / 16;
+                    const int n = run_tiles(hi - lo);
                     if (t >= base && t < base + n) {
-                        const int cl = lo - a[s] + 16 * (t - base);
+                        int c, nn;
+                        run_tile(hi - lo, t - base, c, nn);
                         const SrMat m = s == 0 ? kmat(ka()->L[l].q) : s == 1 ? kmat(ka()->L[l].k) : kmat(ka()->L[l].v);
-                        mk(m, cl, min(16, hi - a[s] - cl), s);
+                        mk(m, lo - a[s] + c, nn, s);
                     }
                     base += n;
                 }
@@ -291,20 +309,23 @@ __device__ __forceinline__ GT gemm_tile(int kind, int l, int t) {
             break;
         }
         case K_O: case K_D: {
-            const int c = w * SS.ch + 16 * t;
-            mk(kind == K_O ? kmat(ka()->L[l].o) : kmat(ka()->L[l].d), c, min(16, (w + 1) * SS.ch - c), 0);
+            int c, nn;
+            run_tile(SS.ch, t, c, nn);
+            mk(kind == K_O ? kmat(ka()->L[l].o) : kmat(ka()->L[l].d), w * SS.ch + c, nn, 0);
             break;
         }
         case K_G: {
-            const int ntg = (SS.ci + 15) / 16;
-            const int s = t < ntg ? 0 : 1, tt = t - s * ntg;
-            const int c = w * SS.ci + 16 * tt;
-            mk(s == 0 ? kmat(ka()->L[l].g) : kmat(ka()->L[l].u), c, min(16, (w + 1) * SS.ci - c), s);
+            const int ntg = run_tiles(SS.ci);
+            const int s = t < ntg ? 0 : 1;
+            int c, nn;
+            run_tile(SS.ci, t - s * ntg, c, nn);
+            mk(s == 0 ? kmat(ka()->L[l].g) : kmat(ka()->L[l].u), w * SS.ci + c, nn, s);
             break;
         }
         default: {   // K_DA, K_DM
-            const int c = 16 * w;
-            mk(kind == K_DA ? kmat(ka()->L[l].aw) : kmat(ka()->L[l].mw), c, min(16, 4 * SS.d2 - c), 0);
+            int c, nn;
+            run_tile(min(16, 4 * SS.d2 - 16 * w), t, c, nn);
+            mk(kind == K_DA ? kmat(ka()->L[l].aw) : kmat(ka()->L[l].mw), 16 * w + c, nn, 0);
             break;
         }
     }
@@ -393,8 +414,8 @@ __device__ __forceinline__ bool loader_wait_free(SrLds &S, Loader &ld) {
 __device__ __forceinline__ void loader_commit(SrLds &S, Loader &ld) {
     ++ld.seq;
     if (ld.seq > SR_DEPTH) {
-        static_assert(8 * SR_DEPTH == 56, "wait immediate");
-        __builtin_amdgcn_s_waitcnt(0xCF78);                  // vmcnt(56): 8 * SR_DEPTH loads may stay in flight
+        static_assert(8 * SR_DEPTH == 24, "wait immediate");
+        __builtin_amdgcn_s_waitcnt(0x4F78);                  // vmcnt(24): 8 * SR_DEPTH loads may stay in flight
         cbar();
         lds_st_nodep(&S.pub, ld.seq - SR_DEPTH);
     }
@@ -404,36 +425,72 @@ __device__ __forceinline__ void dma16(const void *g, u32x4 *ldsdst) {
     __builtin_amdgcn_global_load_lds(g, (lds_void *)ldsdst, 16, 0, 0);
 }
 
+// Slot layout of a group of 4 k steps: for each step, the tiles in order; a
+// tile of width n takes one slot per 16 / n steps (its part holds that many
+// steps).  off[t][j] is the slot (within the group) holding tile t's step j,
+// cnt[j] the slots of steps 0..j.
+struct Grp {
+    int n[SR_MAXT], off[SR_MAXT][4], cnt[4], slots;
+};
+template <int WT>
+__device__ __forceinline__ Grp grp_layout(int kind, int l, int nt) {
+    Grp G;
+#pragma unroll
+    for (int t = 0; t < SR_MAXT; ++t) G.n[t] = t < nt ? gemm_tile<WT>(kind, l, t).n : 16;
+    // part of tile t that holds step j of a group: a new part every 16/n steps
+    int c = 0, cur[SR_MAXT];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int t = 0; t < SR_MAXT; ++t) {
+            const int spi = 16 / G.n[t];
+            if (t < nt && (j & (spi - 1)) == 0) cur[t] = c++;
+            G.off[t][j] = t < nt ? cur[t] : 0;
+        }
+        G.cnt[j] = c;
+    }
+    G.slots = c;
+    return G;
+}
+
 template <int WT>
 __device__ __forceinline__ bool load_gemm(SrLds &S, Loader &ld, int kind, int l) {
     constexpr int KW = TR<WT>::KW, ES = TR<WT>::ES, P = TR<WT>::P;
-    const int lane = lane_id(), n16 = lane & 15, g = lane >> 4;
+    const int lane = lane_id();
     const int nt = gemm_nt(kind);
     if (nt == 0) return true;
     const int K = gemm_K(kind), nst = K / KW, nkw = gemm_npass<WT>(nst) * PassCfg<WT>::NF;
-    // this lane's row of each tile (rows past a tile's width repeat its last row)
+    // lane L of a part of tile t (width n) loads row L % n, lane group
+    // (L / n) % 4, of step L / (4 n) of the part's steps
     const char *row[SR_MAXT];
+    int sofs[SR_MAXT], spi[SR_MAXT];
 #pragma unroll
     for (int t = 0; t < SR_MAXT; ++t) {
-        row[t] = nullptr;
+        row[t] = nullptr; sofs[t] = 0; spi[t] = 1;
         if (t < nt) {
             const GT tl = gemm_tile<WT>(kind, l, t);
-            row[t] = tl.w + (size_t)min(n16, tl.n - 1) * K * ES + (size_t)g * P * ES;
+            const int n = tl.n;
+            row[t] = tl.w + (size_t)(lane & (n - 1)) * K * ES + (size_t)((lane / n) & 3) * P * ES;
+            sofs[t] = lane / (4 * n);
+            spi[t] = 16 / n;
         }
     }
-    for (int j = 0; j < nkw; ++j) {
+    for (int j = 0; j < nkw; j += 4) {
 #pragma unroll
-        for (int t = 0; t < SR_MAXT; ++t) {
-            if (t < nt) {
-                if (!loader_wait_free(S, ld)) return false;
-                u32x4 *dst = &S.ring[ld.seq % SR_NSLOT][0][0];
+        for (int j4 = 0; j4 < 4; ++j4) {
 #pragma unroll
-                for (int v = 0; v < SR_CW; ++v) {
-                    int ks = v * nkw + j;
-                    ks = ks < nst ? ks : 0;
-                    dma16(row[t] + (size_t)ks * KW * ES, dst + v * 64);
+            for (int t = 0; t < SR_MAXT; ++t) {
+                if (t < nt && (j4 & (spi[t] - 1)) == 0) {
+                    if (!loader_wait_free(S, ld)) return false;
+                    u32x4 *dst = &S.ring[ld.seq % SR_NSLOT][0][0];
+#pragma unroll
+                    for (int v = 0; v < SR_CW; ++v) {
+                        int ks = v * nkw + j + j4 + sofs[t];
+                        ks = ks < nst ? ks : 0;
+                        dma16(row[t] + (size_t)ks * KW * ES, dst + v * 64);
+                    }
+                    loader_commit(S, ld);
                 }
-                loader_commit(S, ld);
             }
         }
     }
@@ -613,7 +670,8 @@ __device__ __forceinline__ void trace_all(unsigned p) {
 
 // ---------------------------------------------------------------------------
 // residual slice -> next GEMM input (X * gain in fragment order) and partial
-// sums of squares; with gain == nullptr only the sums (final norm)
+// sums of squares; with gain == nullptr only the sums (final norm).  gain
+// points at the gain of this workgroup's first column.
 // ---------------------------------------------------------------------------
 template <int WT>
 __device__ __forceinline__ void emit_input(SrLds &S, const float *gain, char *frag, float *ssq) {
@@ -622,7 +680,7 @@ __device__ __forceinline__ void emit_input(SrLds &S, const float *gain, char *fr
     if (frag && gain) {
         for (int i = lane; i < 16 * nq; i += 64) {
             const int r = i / nq, q = i - r * nq, c = 4 * q;
-            const float4 gg = *reinterpret_cast<const float4 *>(gain + c0 + c);
+            const float4 gg = *reinterpret_cast<const float4 *>(gain + c);
             put4<WT>(frag, r, c0 + c, S.xown[r][c] * gg.x, S.xown[r][c + 1] * gg.y, S.xown[r][c + 2] * gg.z,
                      S.xown[r][c + 3] * gg.w);
         }
@@ -739,7 +797,7 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
             if (cl >= tl.n) continue;
             float y[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = sum[i] * (d2 ? 1.f : rs) * (tl.sc ? tl.sc[cl + i] : 1.f);
+            for (int i = 0; i < 4; ++i) y[i] = sum[i] * (d2 ? 1.f : rs) * (tl.sc ? S.aux[16 * t + cl + i] : 1.f);
             const int col = tl.col + cl;
             if (tl.seg < 2) {
                 const int hh = col / D, dd = col - hh * D;
@@ -778,7 +836,7 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
             const int cl = 4 * g;
             float y[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = sum[i] * (tl.sc && cl < tl.n ? tl.sc[cl + i] : 1.f);
+            for (int i = 0; i < 4; ++i) y[i] = sum[i] * (tl.sc && cl < tl.n ? S.aux[16 * t + cl + i] : 1.f);
             if constexpr (C) d2_finish(y, r, tl.col + cl, base, Dc);
             if (cl < tl.n) {
                 const int xc = tl.col - c0 + cl;
@@ -789,10 +847,10 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
         cbar();
         __builtin_amdgcn_wave_barrier();
         if (kind == K_O) {
-            emit_input<WT>(S, ka()->L[l].g_post, lb + SS.o_xm, (float *)(lb + SS.o_ssm));
+            emit_input<WT>(S, S.aux + 64, lb + SS.o_xm, (float *)(lb + SS.o_ssm));
         } else {
             const bool more = l + 1 < SS.nl;
-            emit_input<WT>(S, more ? ka()->L[l + 1].g_in : nullptr, more ? ln + SS.o_xa : nullptr, (float *)(ln + SS.o_ssa));
+            emit_input<WT>(S, more ? S.aux + 64 : nullptr, more ? ln + SS.o_xa : nullptr, (float *)(ln + SS.o_ssa));
             if (!more && !SS.last) {
                 for (int i = lane; i < 16 * SS.ch; i += 64) {
                     const int rr = i / SS.ch, c = i - rr * SS.ch;
@@ -811,8 +869,8 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
             float z[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float gv = sg[i] * (d2 ? 1.f : rs) * (tg.sc ? tg.sc[cl + i] : 1.f);
-                const float uv = su[i] * (d2 ? 1.f : rs) * (tu.sc ? tu.sc[cl + i] : 1.f);
+                const float gv = sg[i] * (d2 ? 1.f : rs) * (tg.sc ? S.aux[16 * t + cl + i] : 1.f);
+                const float uv = su[i] * (d2 ? 1.f : rs) * (tu.sc ? S.aux[16 * (t + ntg) + cl + i] : 1.f);
                 z[i] = r < b ? gv / (1.f + __expf(-gv)) * uv : 0.f;
             }
             put4<WT>(zf, r, tg.col + cl, z[0], z[1], z[2], z[3]);
@@ -827,36 +885,45 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     st4(Dc, ((size_t)r * 4 * SS.d2 + tl.col + cl + i) * 4,
-                        __float_as_uint(sum[i] * rs * (tl.sc ? tl.sc[cl + i] : 1.f)));
+                        __float_as_uint(sum[i] * rs * (tl.sc ? S.aux[cl + i] : 1.f)));
             }
         }
     }
 }
 
-// One pass of NF k steps with the pass's activations in registers.
+// One pass of NF k steps (groups of 4) with the pass's activations in registers.
 template <int WT, bool C>
-__device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, unsigned &slot, u32x4 *a, int ks, int nst, int nt, bool conv,
+__device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, const Grp &G, u32x4 *a, int ks, int nst, int nt, bool conv,
                                           const float *cbase, const float *cD, f32x4 (&acc)[SR_MAXT]) {
     constexpr int AFR = TR<WT>::AFR, NF = PassCfg<WT>::NF;
-    const int lane = lane_id(), v = wave_id();
-    const u32x4 *ringv = &S.ring[0][v][lane];
+    const int v = wave_id();
+    const u32x4 *ringv = &S.ring[0][v][0];
 #pragma unroll
-    for (int j = 0; j < NF; ++j) {
-        u32x4 *aj = &a[j * AFR];
-        const bool live = ks + j < nst;
-        if constexpr (C) {
-            if (conv && live) d2_prepare<WT>(S, aj, ks + j, cbase, cD);
-        }
-        if (!ring_wait(S, cs, cs.seq + nt)) return false;
+    for (int q = 0; q < NF / 4; ++q) {
+        const unsigned g0 = cs.seq;
 #pragma unroll
-        for (int t = 0; t < SR_MAXT; ++t) {
-            if (t < nt) {
-                const u32x4 wv = ringv[(size_t)slot * (SR_SLOT / 16)];
-                slot = __builtin_amdgcn_readfirstlane(slot + 1 == SR_NSLOT ? 0 : slot + 1);
-                if (live) mac<WT>(acc[t], wv, aj);
+        for (int j4 = 0; j4 < 4; ++j4) {
+            const int j = 4 * q + j4;
+            u32x4 *aj = &a[j * AFR];
+            const bool live = ks + j < nst;
+            if constexpr (C) {
+                if (conv && live) d2_prepare<WT>(S, aj, ks + j, cbase, cD);
+            }
+            if (!ring_wait(S, cs, g0 + G.cnt[j4])) return false;
+#pragma unroll
+            for (int t = 0; t < SR_MAXT; ++t) {
+                if (t < nt) {
+                    const int n = G.n[t];
+                    const unsigned slot = __builtin_amdgcn_readfirstlane((g0 + G.off[t][j4]) % SR_NSLOT);
+                    // lane index taken afresh so the 16 (tile, step) offsets are not all held live
+                    const int ln = lane_id();
+                    const int L = (j4 & (16 / n - 1)) * 4 * n + (ln >> 4) * n + (ln & (n - 1));
+                    const u32x4 wv = ringv[(size_t)slot * (SR_SLOT / 16) + L];
+                    if (live) mac<WT>(acc[t], wv, aj);
+                }
             }
         }
-        cs.seq = __builtin_amdgcn_readfirstlane(cs.seq + nt);
+        cs.seq = __builtin_amdgcn_readfirstlane(g0 + G.slots);
         ring_release(S, cs.seq);
     }
     return true;
@@ -864,8 +931,8 @@ __device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, unsigned &slot, u3
 
 // all k steps of one wave: up to SR_MAXPASS passes, activations double-buffered
 template <int WT, bool C>
-__device__ __forceinline__ bool gemm_steps(SrLds &S, Cons &cs, const char *act, int ks0, int nst, int nt, int npass, bool conv,
-                                           const float *cbase, const float *cD, f32x4 (&acc)[SR_MAXT], unsigned p) {
+__device__ __forceinline__ bool gemm_steps(SrLds &S, Cons &cs, const Grp &G, const char *act, int ks0, int nst, int nt, int npass,
+                                           bool conv, const float *cbase, const float *cD, f32x4 (&acc)[SR_MAXT], unsigned p) {
     constexpr int AFR = TR<WT>::AFR, NF = PassCfg<WT>::NF;
     u32x4 a0[NF * AFR], a1[NF * AFR];
     auto load_pass = [&](int ps, u32x4 *dst) {
@@ -878,21 +945,20 @@ __device__ __forceinline__ bool gemm_steps(SrLds &S, Cons &cs, const char *act, 
                 dst[j * AFR + f] = *reinterpret_cast<const u32x4 *>(act + (size_t)ks * 64 * 16 * AFR + 16 * f);
         }
     };
-    unsigned slot = __builtin_amdgcn_readfirstlane(cs.seq % SR_NSLOT);
     load_pass(0, a0);
     if (npass > 1) load_pass(1, a1);
     if (blockIdx.x == 0 && (threadIdx.x >> 6) == 1 && SS.trace) {
         vm_wait();
         dbg_at(p, 1);
-        if (!ring_wait(S, cs, cs.seq + nt)) return false;
+        if (!ring_wait(S, cs, cs.seq + G.cnt[0])) return false;
         dbg_at(p, 4);
     }
-    if (!gemm_pass<WT, C>(S, cs, slot, a0, ks0, nst, nt, conv, cbase, cD, acc)) return false;
+    if (!gemm_pass<WT, C>(S, cs, G, a0, ks0, nst, nt, conv, cbase, cD, acc)) return false;
     if (npass > 1) {
         if (npass > 2) load_pass(2, a0);
-        if (!gemm_pass<WT, C>(S, cs, slot, a1, ks0 + NF, nst, nt, conv, cbase, cD, acc)) return false;
+        if (!gemm_pass<WT, C>(S, cs, G, a1, ks0 + NF, nst, nt, conv, cbase, cD, acc)) return false;
         if (npass > 2) {
-            if (!gemm_pass<WT, C>(S, cs, slot, a0, ks0 + 2 * NF, nst, nt, conv, cbase, cD, acc)) return false;
+            if (!gemm_pass<WT, C>(S, cs, G, a0, ks0 + 2 * NF, nst, nt, conv, cbase, cD, acc)) return false;
         }
     }
     return true;
@@ -934,7 +1000,17 @@ __device__ __attribute__((noinline)) unsigned gemm_phase(int kind, int l, unsign
 #pragma unroll
         for (int t = 0; t < SR_MAXT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         dbg_at(p, 0);
-        const bool ok = gemm_steps<WT, C>(S, cs, act, ks0, nst, nt, npass, conv, cbase, cD, acc, p);
+        if (v == SR_CW - 1) {
+            // epilogue constants into LDS: fp8 scales of the tiles, the next norm's gains
+            if (lane < 16 * nt) {
+                const GT tl = gemm_tile<WT>(kind, l, lane >> 4);
+                if (tl.sc && (lane & 15) < tl.n) S.aux[lane] = tl.sc[lane & 15];
+            }
+            const float *gn = kind == K_O ? ka()->L[l].g_post : (kind == K_D && l + 1 < SS.nl) ? ka()->L[l + 1].g_in : nullptr;
+            if (gn && lane < SS.ch) S.aux[64 + lane] = gn[blockIdx.x * SS.ch + lane];
+        }
+        const Grp G = grp_layout<WT>(kind, l, nt);
+        const bool ok = gemm_steps<WT, C>(S, cs, G, act, ks0, nst, nt, npass, conv, cbase, cD, acc, p);
         dbg_at(p, 2);
         if (!ok) return ~0u;
 #pragma unroll
@@ -1327,7 +1403,7 @@ __device__ __forceinline__ bool init_phase(SrLds &S) {
     }
     vm_wait();
     if (arrive(S)) {
-        if (SS.nl > 0) emit_input<WT>(S, ka()->L[0].g_in, layer_buf(0) + SS.o_xa, (float *)(layer_buf(0) + SS.o_ssa));
+        if (SS.nl > 0) emit_input<WT>(S, ka()->L[0].g_in + c0, layer_buf(0) + SS.o_xa, (float *)(layer_buf(0) + SS.o_ssa));
         else emit_input<WT>(S, nullptr, nullptr, (float *)(layer_buf(0) + SS.o_ssa));
         signal_phase();
     }
@@ -1432,14 +1508,20 @@ SrLayout sround_layout(int H, int I, int qd, int kvd, int nkv, int G, int d, int
     return L;
 }
 
-// tiles of 16 columns that workgroup w gets of the concatenated q|k|v outputs
+// tiles of a run of m columns: 16-wide tiles plus an 8- and/or 4-wide rest
+static int host_run_tiles(int m) {
+    const int r = m & 15;
+    return (m >> 4) + (r == 12 ? 2 : r ? 1 : 0);
+}
+
+// tiles that workgroup w gets of the concatenated q|k|v outputs
 static int q_tiles(int w, int cq, int qd, int kvd) {
     const int c0 = w * cq, c1 = c0 + cq;
     const int a[3] = {0, qd, qd + kvd}, e[3] = {qd, qd + kvd, qd + 2 * kvd};
     int nt = 0;
     for (int s = 0; s < 3; ++s) {
         const int lo = c0 > a[s] ? c0 : a[s], hi = c1 < e[s] ? c1 : e[s];
-        if (hi > lo) nt += (hi - lo + 15) / 16;
+        if (hi > lo) nt += host_run_tiles(hi - lo);
     }
     return nt;
 }
@@ -1453,11 +1535,15 @@ int sround_nwg(int H, int I, int qd, int kvd, int wt, int d2, int cus) {
         const int nkw = (K / kw + SR_CW - 1) / SR_CW;
         if ((nkw + nf - 1) / nf > 3) return 0;      // passes built per GEMM
     }
+    // a group of 4 k steps of all of a workgroup's columns (one ring slot per
+    // 4 columns) must fit in the ring beside the loader's in-flight slots
+    const int max_cols = 4 * (SR_NSLOT - SR_DEPTH);
     for (int n = cus < 256 ? cus : 256; n >= 1; --n) {
         if (H % n || I % n || nqkv % n) continue;
         const int ch = H / n, ci = I / n, cq = nqkv / n;
         if (ch % 4 || ci % 4 || cq % 4 || ch > SR_MAXCH) continue;
-        if ((ch + 15) / 16 > SR_MAXT || 2 * ((ci + 15) / 16) > SR_MAXT) continue;
+        if (ch > max_cols || 2 * ci > max_cols || cq > max_cols) continue;
+        if (host_run_tiles(ch) > SR_MAXT || 2 * host_run_tiles(ci) > SR_MAXT) continue;
         bool ok = true;
         for (int w = 0; w < n && ok; ++w) ok = q_tiles(w, cq, qd, kvd) <= SR_MAXT;
         if (!ok) continue;
