@@ -169,6 +169,17 @@ __device__ __forceinline__ void put4(void *buf, int r, int c, float x0, float x1
     else st8(buf, e * 2, u32x2{bf2(x0, x1), bf2(x2, x3)});
 }
 
+// Two-plane bf16 activations (used with the DFlash2 wrap): the plane at buf
+// holds bf16(x), the plane lo_off bytes further the rounding residual
+// bf16(x - bf16(x)), so a GEMM over both planes sees x to about 16 bits.
+__device__ __forceinline__ float bf_round(float x) { return bf16_bits_to_f32(f32_to_bf16_bits(x)); }
+template <int WT, bool HL>
+__device__ __forceinline__ void put4x(void *buf, size_t lo_off, int r, int c, float x0, float x1, float x2, float x3) {
+    put4<WT>(buf, r, c, x0, x1, x2, x3);
+    if constexpr (HL)
+        put4<WT>((char *)buf + lo_off, r, c, x0 - bf_round(x0), x1 - bf_round(x1), x2 - bf_round(x2), x3 - bf_round(x3));
+}
+
 // ---------------------------------------------------------------------------
 // LDS
 // ---------------------------------------------------------------------------
@@ -434,22 +445,23 @@ struct Grp {
 };
 template <int WT>
 __device__ __forceinline__ Grp grp_layout(int kind, int l, int nt) {
+    // every field is wave-uniform and kept in scalar registers
     Grp G;
 #pragma unroll
-    for (int t = 0; t < SR_MAXT; ++t) G.n[t] = t < nt ? gemm_tile<WT>(kind, l, t).n : 16;
+    for (int t = 0; t < SR_MAXT; ++t) G.n[t] = __builtin_amdgcn_readfirstlane(t < nt ? gemm_tile<WT>(kind, l, t).n : 16);
     // part of tile t that holds step j of a group: a new part every 16/n steps
     int c = 0, cur[SR_MAXT];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
         for (int t = 0; t < SR_MAXT; ++t) {
-            const int spi = 16 / G.n[t];
-            if (t < nt && (j & (spi - 1)) == 0) cur[t] = c++;
-            G.off[t][j] = t < nt ? cur[t] : 0;
+            const int m = G.n[t] == 16 ? 0 : G.n[t] == 8 ? 1 : 3;     // 16 / n - 1
+            if (t < nt && (j & m) == 0) cur[t] = c++;
+            G.off[t][j] = __builtin_amdgcn_readfirstlane(t < nt ? cur[t] : 0);
         }
-        G.cnt[j] = c;
+        G.cnt[j] = __builtin_amdgcn_readfirstlane(c);
     }
-    G.slots = c;
+    G.slots = __builtin_amdgcn_readfirstlane(c);
     return G;
 }
 
@@ -576,7 +588,10 @@ __device__ __forceinline__ bool ring_wait(SrLds &S, Cons &c, unsigned upto) {   
 }
 __device__ __forceinline__ void ring_release(SrLds &S, unsigned upto) {
     cbar();
-    lds_st(&S.cons[threadIdx.x >> 6], upto);
+    // kept scalar up to the store, so no vector copy of it lives across the step loop
+    unsigned u = __builtin_amdgcn_readfirstlane(upto);
+    asm volatile("" : "+s"(u));
+    lds_st(&S.cons[threadIdx.x >> 6], u);
 }
 
 // wait until `p` global phases are complete (wave 0 polls, the others read LDS)
@@ -673,7 +688,7 @@ __device__ __forceinline__ void trace_all(unsigned p) {
 // sums of squares; with gain == nullptr only the sums (final norm).  gain
 // points at the gain of this workgroup's first column.
 // ---------------------------------------------------------------------------
-template <int WT>
+template <int WT, bool HL>
 __device__ __forceinline__ void emit_input(SrLds &S, const float *gain, char *frag, float *ssq) {
     const int lane = lane_id();
     const int ch = SS.ch, c0 = blockIdx.x * SS.ch, nq = ch / 4;
@@ -681,7 +696,7 @@ __device__ __forceinline__ void emit_input(SrLds &S, const float *gain, char *fr
         for (int i = lane; i < 16 * nq; i += 64) {
             const int r = i / nq, q = i - r * nq, c = 4 * q;
             const float4 gg = *reinterpret_cast<const float4 *>(gain + c);
-            put4<WT>(frag, r, c0 + c, S.xown[r][c] * gg.x, S.xown[r][c + 1] * gg.y, S.xown[r][c + 2] * gg.z,
+            put4x<WT, HL>(frag, (size_t)16 * SS.H * 2, r, c0 + c, S.xown[r][c] * gg.x, S.xown[r][c + 1] * gg.y, S.xown[r][c + 2] * gg.z,
                      S.xown[r][c + 3] * gg.w);
         }
     }
@@ -713,8 +728,8 @@ __device__ __forceinline__ void mac(f32x4 &acc, const u32x4 &w, const u32x4 *a) 
 // DFlash2 prepare conv on the staged activations of one k step ([DflashDraft]
 // "d2_conv_prepare"): xc[r,c] = (b[c,0] + D[r,g(c),0]) xn[r-1,c] + (b[c,1] +
 // D[r,g(c),1]) xn[r,c], xn = (X * gain) / rms, xn[-1] = 0.
-template <int WT>
-__device__ __forceinline__ void d2_prepare(SrLds &S, u32x4 *a, int kstep, const float *base, const float *Dc) {
+template <int WT, bool HL>
+__device__ __forceinline__ void d2_prepare(SrLds &S, u32x4 *a, u32x4 *alo, int kstep, const float *base, const float *Dc) {
     constexpr int KW = TR<WT>::KW, P = TR<WT>::P, AFR = TR<WT>::AFR;
     const int lane = lane_id(), r = lane & 15, g = lane >> 4;
     const int c0 = kstep * KW + g * P;
@@ -732,6 +747,10 @@ __device__ __forceinline__ void d2_prepare(SrLds &S, u32x4 *a, int kstep, const 
             for (int i = 0; i < 4; ++i) {
                 x[8 * f + 2 * i] = bf16_bits_to_f32(a[f][i] & 0xFFFFu);
                 x[8 * f + 2 * i + 1] = __uint_as_float(a[f][i] & 0xFFFF0000u);
+                if constexpr (HL) {
+                    x[8 * f + 2 * i] += bf16_bits_to_f32(alo[f][i] & 0xFFFFu);
+                    x[8 * f + 2 * i + 1] += __uint_as_float(alo[f][i] & 0xFFFF0000u);
+                }
             }
     }
     float y[P];
@@ -748,6 +767,14 @@ __device__ __forceinline__ void d2_prepare(SrLds &S, u32x4 *a, int kstep, const 
         for (int f = 0; f < AFR; ++f)
             a[f] = u32x4{bf2(y[8 * f], y[8 * f + 1]), bf2(y[8 * f + 2], y[8 * f + 3]), bf2(y[8 * f + 4], y[8 * f + 5]),
                          bf2(y[8 * f + 6], y[8 * f + 7])};
+        if constexpr (HL) {
+#pragma unroll
+            for (int i = 0; i < P; ++i) y[i] -= bf_round(y[i]);
+#pragma unroll
+            for (int f = 0; f < AFR; ++f)
+                alo[f] = u32x4{bf2(y[8 * f], y[8 * f + 1]), bf2(y[8 * f + 2], y[8 * f + 3]), bf2(y[8 * f + 4], y[8 * f + 5]),
+                               bf2(y[8 * f + 6], y[8 * f + 7])};
+        }
     }
 }
 
@@ -778,6 +805,7 @@ __device__ __forceinline__ void d2_finish(float (&y)[4], int r, int c, const flo
 
 template <int WT, int D, bool C>
 __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigned p, int nt) {
+    constexpr bool HL = C && TR<WT>::AB == 2;      // two-plane activations with the DFlash2 wrap
     const int lane = lane_id(), r = lane & 15, g = lane >> 4;
     char *lb = layer_buf(l), *ln = layer_buf(l + 1);
     constexpr bool d2 = C;
@@ -847,10 +875,10 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
         cbar();
         __builtin_amdgcn_wave_barrier();
         if (kind == K_O) {
-            emit_input<WT>(S, S.aux + 64, lb + SS.o_xm, (float *)(lb + SS.o_ssm));
+            emit_input<WT, HL>(S, S.aux + 64, lb + SS.o_xm, (float *)(lb + SS.o_ssm));
         } else {
             const bool more = l + 1 < SS.nl;
-            emit_input<WT>(S, more ? S.aux + 64 : nullptr, more ? ln + SS.o_xa : nullptr, (float *)(ln + SS.o_ssa));
+            emit_input<WT, HL>(S, more ? S.aux + 64 : nullptr, more ? ln + SS.o_xa : nullptr, (float *)(ln + SS.o_ssa));
             if (!more && !SS.last) {
                 for (int i = lane; i < 16 * SS.ch; i += 64) {
                     const int rr = i / SS.ch, c = i - rr * SS.ch;
@@ -873,7 +901,7 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
                 const float uv = su[i] * (d2 ? 1.f : rs) * (tu.sc ? S.aux[16 * (t + ntg) + cl + i] : 1.f);
                 z[i] = r < b ? gv / (1.f + __expf(-gv)) * uv : 0.f;
             }
-            put4<WT>(zf, r, tg.col + cl, z[0], z[1], z[2], z[3]);
+            put4x<WT, HL>(zf, (size_t)16 * SS.I * 2, r, tg.col + cl, z[0], z[1], z[2], z[3]);
         }
     } else {   // K_DA, K_DM: dynamic conv coefficients D[r][j] = rinv[r] * s_j * (X * g)[r] . W_dyn[j]
         if (nt > 0) {
@@ -893,9 +921,10 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
 
 // One pass of NF k steps (groups of 4) with the pass's activations in registers.
 template <int WT, bool C>
-__device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, const Grp &G, u32x4 *a, int ks, int nst, int nt, bool conv,
-                                          const float *cbase, const float *cD, f32x4 (&acc)[SR_MAXT]) {
+__device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, const Grp &G, u32x4 *a, u32x4 *alo, int ks, int nst, int nt,
+                                          bool conv, const float *cbase, const float *cD, f32x4 (&acc)[SR_MAXT]) {
     constexpr int AFR = TR<WT>::AFR, NF = PassCfg<WT>::NF;
+    constexpr bool HL = C && TR<WT>::AB == 2;       // alo != a: the activations' low plane
     const int v = wave_id();
     const u32x4 *ringv = &S.ring[0][v][0];
 #pragma unroll
@@ -904,10 +933,10 @@ __device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, const Grp &G, u32x
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) {
             const int j = 4 * q + j4;
-            u32x4 *aj = &a[j * AFR];
+            u32x4 *aj = &a[j * AFR], *alj = &alo[j * AFR];
             const bool live = ks + j < nst;
             if constexpr (C) {
-                if (conv && live) d2_prepare<WT>(S, aj, ks + j, cbase, cD);
+                if (conv && live) d2_prepare<WT, HL>(S, aj, alj, ks + j, cbase, cD);
             }
             if (!ring_wait(S, cs, g0 + G.cnt[j4])) return false;
 #pragma unroll
@@ -917,9 +946,13 @@ __device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, const Grp &G, u32x
                     const unsigned slot = __builtin_amdgcn_readfirstlane((g0 + G.off[t][j4]) % SR_NSLOT);
                     // lane index taken afresh so the 16 (tile, step) offsets are not all held live
                     const int ln = lane_id();
-                    const int L = (j4 & (16 / n - 1)) * 4 * n + (ln >> 4) * n + (ln & (n - 1));
+                    const int m = n == 16 ? 0 : n == 8 ? 1 : 3;          // 16 / n - 1
+                    const int L = (j4 & m) * 4 * n + (ln >> 4) * n + (ln & (n - 1));
                     const u32x4 wv = ringv[(size_t)slot * (SR_SLOT / 16) + L];
-                    if (live) mac<WT>(acc[t], wv, aj);
+                    if (live) {
+                        mac<WT>(acc[t], wv, aj);
+                        if constexpr (HL) { if (alo != a) mac<WT>(acc[t], wv, alj); }
+                    }
                 }
             }
         }
@@ -932,33 +965,50 @@ __device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, const Grp &G, u32x
 // all k steps of one wave: up to SR_MAXPASS passes, activations double-buffered
 template <int WT, bool C>
 __device__ __forceinline__ bool gemm_steps(SrLds &S, Cons &cs, const Grp &G, const char *act, int ks0, int nst, int nt, int npass,
-                                           bool conv, const float *cbase, const float *cD, f32x4 (&acc)[SR_MAXT], unsigned p) {
+                                           bool conv, bool hl, const float *cbase, const float *cD, f32x4 (&acc)[SR_MAXT],
+                                           unsigned p) {
     constexpr int AFR = TR<WT>::AFR, NF = PassCfg<WT>::NF;
     u32x4 a0[NF * AFR], a1[NF * AFR];
-    auto load_pass = [&](int ps, u32x4 *dst) {
+    auto load_pass = [&](int ps, u32x4 *dst, size_t off) {
 #pragma unroll
         for (int j = 0; j < NF; ++j) {
             int ks = ks0 + ps * NF + j;
             ks = ks < nst ? ks : 0;                   // dead steps reread step 0
 #pragma unroll
             for (int f = 0; f < AFR; ++f)
-                dst[j * AFR + f] = *reinterpret_cast<const u32x4 *>(act + (size_t)ks * 64 * 16 * AFR + 16 * f);
+                dst[j * AFR + f] = *reinterpret_cast<const u32x4 *>(act + off + (size_t)ks * 64 * 16 * AFR + 16 * f);
         }
     };
-    load_pass(0, a0);
-    if (npass > 1) load_pass(1, a1);
+    if constexpr (C && TR<WT>::AB == 2) {
+        if (hl) {
+            // two-plane activations: a pass holds both planes of its steps
+            // (a0 high, a1 low), so the next pass is not prefetched
+            const size_t lo_off = (size_t)16 * nst * TR<WT>::KW * 2;
+#pragma unroll
+            for (int ps = 0; ps < SR_MAXPASS; ++ps) {
+                if (ps < npass) {
+                    load_pass(ps, a0, 0);
+                    load_pass(ps, a1, lo_off);
+                    if (!gemm_pass<WT, C>(S, cs, G, a0, a1, ks0 + ps * NF, nst, nt, conv, cbase, cD, acc)) return false;
+                }
+            }
+            return true;
+        }
+    }
+    load_pass(0, a0, 0);
+    if (npass > 1) load_pass(1, a1, 0);
     if (blockIdx.x == 0 && (threadIdx.x >> 6) == 1 && SS.trace) {
         vm_wait();
         dbg_at(p, 1);
         if (!ring_wait(S, cs, cs.seq + G.cnt[0])) return false;
         dbg_at(p, 4);
     }
-    if (!gemm_pass<WT, C>(S, cs, G, a0, ks0, nst, nt, conv, cbase, cD, acc)) return false;
+    if (!gemm_pass<WT, C>(S, cs, G, a0, a0, ks0, nst, nt, conv, cbase, cD, acc)) return false;
     if (npass > 1) {
-        if (npass > 2) load_pass(2, a0);
-        if (!gemm_pass<WT, C>(S, cs, G, a1, ks0 + NF, nst, nt, conv, cbase, cD, acc)) return false;
+        if (npass > 2) load_pass(2, a0, 0);
+        if (!gemm_pass<WT, C>(S, cs, G, a1, a1, ks0 + NF, nst, nt, conv, cbase, cD, acc)) return false;
         if (npass > 2) {
-            if (!gemm_pass<WT, C>(S, cs, G, a0, ks0 + 2 * NF, nst, nt, conv, cbase, cD, acc)) return false;
+            if (!gemm_pass<WT, C>(S, cs, G, a0, a0, ks0 + 2 * NF, nst, nt, conv, cbase, cD, acc)) return false;
         }
     }
     return true;
@@ -1010,7 +1060,9 @@ __device__ __attribute__((noinline)) unsigned gemm_phase(int kind, int l, unsign
             if (gn && lane < SS.ch) S.aux[64 + lane] = gn[blockIdx.x * SS.ch + lane];
         }
         const Grp G = grp_layout<WT>(kind, l, nt);
-        const bool ok = gemm_steps<WT, C>(S, cs, G, act, ks0, nst, nt, npass, conv, cbase, cD, acc, p);
+        // with the DFlash2 wrap every GEMM input but o_proj's has two planes
+        const bool hl = C && TR<WT>::AB == 2 && kind != K_O;
+        const bool ok = gemm_steps<WT, C>(S, cs, G, act, ks0, nst, nt, npass, conv, hl, cbase, cD, acc, p);
         dbg_at(p, 2);
         if (!ok) return ~0u;
 #pragma unroll
@@ -1381,8 +1433,9 @@ __device__ __forceinline__ bool merge_phase(SrLds &S, int l, unsigned p) {
 // ---------------------------------------------------------------------------
 // init and final phases
 // ---------------------------------------------------------------------------
-template <int WT>
+template <int WT, bool C>
 __device__ __forceinline__ bool init_phase(SrLds &S) {
+    constexpr bool HL = C && TR<WT>::AB == 2;
     const int lane = lane_id(), v = wave_id();
     const int ch = SS.ch, c0 = blockIdx.x * ch, H = SS.H, b = SS.b;
     for (int i = threadIdx.x; i < 16 * ch; i += SR_CW * 64) {
@@ -1403,8 +1456,8 @@ __device__ __forceinline__ bool init_phase(SrLds &S) {
     }
     vm_wait();
     if (arrive(S)) {
-        if (SS.nl > 0) emit_input<WT>(S, ka()->L[0].g_in + c0, layer_buf(0) + SS.o_xa, (float *)(layer_buf(0) + SS.o_ssa));
-        else emit_input<WT>(S, nullptr, nullptr, (float *)(layer_buf(0) + SS.o_ssa));
+        if (SS.nl > 0) emit_input<WT, HL>(S, ka()->L[0].g_in + c0, layer_buf(0) + SS.o_xa, (float *)(layer_buf(0) + SS.o_ssa));
+        else emit_input<WT, HL>(S, nullptr, nullptr, (float *)(layer_buf(0) + SS.o_ssa));
         signal_phase();
     }
     return true;
@@ -1429,7 +1482,7 @@ __device__ __forceinline__ bool compute_main(SrLds &S) {
     if (wave == 0) E = __builtin_amdgcn_readfirstlane(ldc_u(SS.ctr + SR_CTR_EPOCH));
     Cons cs{0u, 0u};
     const int nl = SS.nl, np = npl();
-    if (!init_phase<WT>(S)) return false;
+    if (!init_phase<WT, C>(S)) return false;
     unsigned p = 1;
     for (int l = 0; l < nl; ++l) {
         for (int i = 0; i < np; ++i, ++p) {
@@ -1493,15 +1546,16 @@ SrLayout sround_layout(int H, int I, int qd, int kvd, int nkv, int G, int d, int
     long long off = 0;
     auto take = [&](long long bytes) { const long long o = off; off += (bytes + 255) / 256 * 256; return o; };
     SrLayout L;
-    L.xa = take(16 * H * AB);
+    const int planes = d2 > 0 && AB == 2 ? 2 : 1;      // DFlash2: two-plane GEMM inputs
+    L.xa = take(16LL * H * AB * planes);
     L.ssa = take(16LL * nwg * 4);
     L.qkv = take(16LL * (qd + 2 * kvd) * AB);
     L.po = take((long long)nkv * SR_MAX_SPLITS * G * 16 * d * AB);
     L.pml = take((long long)nkv * SR_MAX_SPLITS * G * 16 * 2 * 4);
     L.of = take(16LL * qd * AB);
-    L.xm = take(16LL * H * AB);
+    L.xm = take(16LL * H * AB * planes);
     L.ssm = take(16LL * nwg * 4);
-    L.zf = take(16LL * I * AB);
+    L.zf = take(16LL * I * AB * planes);
     L.da = take(16LL * 4 * (d2 > 0 ? d2 : 1) * 4);
     L.dm = take(16LL * 4 * (d2 > 0 ? d2 : 1) * 4);
     L.stride = off;
