@@ -18,8 +18,16 @@ Printed as one JSON line:
 * roofline: the persistent forward_round kernel's algorithmic bytes per
   launch over its average launch time, timed live with HIP events on its
   stream;
+* roofline.traffic: the kernel's measured HBM bytes per launch, from the
+  rocprofv3 FETCH_SIZE / WRITE_SIZE record committed under profiles/
+  (each counter scaled by what it reads for a plain device copy of known
+  size); null when the kernel's sources no longer match that record;
 * cpu_baseline: the fp64 CPU oracle running the same round on a bounded
   sample.
+
+``python bench.py --copy-calibration`` only copies 256 MiB on the device five
+times: run under ``rocprofv3 --pmc FETCH_SIZE`` (then WRITE_SIZE) it gives the
+counters' scale factors.
 """
 from __future__ import annotations
 
@@ -38,6 +46,47 @@ import synth  # noqa: E402
 
 METRIC = "drafter 16-token rounds/sec at ctx 4096 + achieved HBM GB/s fraction"
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, vendor figure
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "sround_kernel_c3_ctx4096_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "block_diffusion_drafter_round_amd", "csrc", f) for f in ("sround.hip", "sround.h")]
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic() -> dict | None:
+    """HBM bytes per launch of the round kernel from the committed counter
+    record, or None if the record is missing or was taken on other sources.
+    The record holds one line ``traffic-record: key=value; ...``."""
+    try:
+        with open(TRAFFIC_RECORD) as fh:
+            line = next(l for l in fh if l.startswith("traffic-record:"))
+    except (OSError, StopIteration):
+        return None
+    kv = dict(x.strip().split("=", 1) for x in line.split(":", 1)[1].split(";") if "=" in x)
+    if kv.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    fetch = float(kv["fetch_kib"]) * 1024 * float(kv["fetch_scale"])
+    write = float(kv["write_kib"]) * 1024 * float(kv["write_scale"])
+    return {"fetch": int(fetch), "write": int(write), "total": int(fetch + write)}
+
+
+def copy_calibration() -> int:
+    """256 MiB device-to-device copy, five times (counter calibration)."""
+    import torch
+    n = 256 << 20
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied {n} bytes 5 times", flush=True)
+    return 0
 
 
 def round_bytes(cfg, ctx: int, t: int = 16, b: int = 16) -> dict:
@@ -119,7 +168,10 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prof", action="store_true", help="skip the live per-kernel timing")
+    ap.add_argument("--copy-calibration", action="store_true", help="only run the 256 MiB copy used to scale counters")
     args = ap.parse_args(argv)
+    if args.copy_calibration:
+        return copy_calibration()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the drafter path has no "
               f"cross-GPU work; sequences shard by data parallelism).", file=sys.stderr)
@@ -193,8 +245,11 @@ def main(argv=None) -> int:
         avg_s = tot_ms / 1e3 / max(nl, 1)
         gb = round_kernel_bytes(cfg, ctx, b)
         ach = gb / avg_s / 1e9
+        tr = measured_traffic()
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": tr["total"] if tr else None,
+                    "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                    "traffic_fetch": tr["fetch"] if tr else None, "traffic_write": tr["write"] if tr else None,
                     "kernel": "persistent forward_round kernel (8 layers, b=16, 4112 keys)",
                     "bytes_per_launch": gb, "avg_launch_us": round(avg_s * 1e6, 2), "launches": nl,
                     "ms_per_step_while_timed": round(max(gpu_p, wall_p) * 1e3 / args.steps, 4)}
