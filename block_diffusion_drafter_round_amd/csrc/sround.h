@@ -20,8 +20,11 @@ constexpr int SR_MAXCH = 48;                  // residual columns owned by one w
 constexpr int SR_MAXG = 8;                    // q heads per kv head
 constexpr int SR_MAX_D2 = 64;                 // DFlash2 conv groups
 constexpr int SR_TRACE = 4096;                // phase time stamps
-// counter words: 8 per-XCD-slot counters (32 words apart), then the epoch and the error word
-constexpr int SR_CTR_EPOCH = 256, SR_CTR_ERR = 288, SR_CTR_WORDS = 320;
+// counter words: SR_NCTR phase counters 32 words (128 bytes) apart, workgroup w
+// signalling counter w % SR_NCTR, then the epoch and the error word.  Few
+// workgroups per counter keep the same-line atomics of a phase end short.
+constexpr int SR_NCTR = 64;
+constexpr int SR_CTR_EPOCH = SR_NCTR * 32, SR_CTR_ERR = SR_CTR_EPOCH + 32, SR_CTR_WORDS = SR_CTR_ERR + 32;
 
 struct SrMat {
     const void *w;    // [n][K], torch Linear layout, in the weight dtype

@@ -38,8 +38,10 @@
 // Synchronisation.  Inside a workgroup: LDS words only (no s_barrier; the
 // loader never waits for compute waves except for free ring slots).  The last
 // compute wave to finish a phase runs the epilogue, waits for its stores and
-// bumps the counter of its XCD slot (blockIdx % 8).  Wave 0 polls the eight
-// counters with device-coherent loads and publishes the phase in LDS.  Each
+// bumps phase counter blockIdx % 64 (four workgroups share one, so the
+// same-line atomics at a phase end stay short).  Wave 0 polls the 64
+// counters, one per lane, with device-coherent loads and publishes the phase
+// in LDS.  Each
 // (layer, phase) output has its own workspace buffer, written with
 // device-coherent (sc1) stores and first read after the counter says it is
 // complete, so plain loads can use the L2 of each XCD.  Counters are never
@@ -599,9 +601,10 @@ __device__ __forceinline__ bool wait_phase(SrLds &S, unsigned p, unsigned E) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     int spins = 0;
     if (wave == 0) {
-        const int x = lane & 7;
+        static_assert(SR_NCTR <= 64 && 64 % SR_NCTR == 0, "one counter per lane group");
+        const int x = lane % SR_NCTR;
         const unsigned nwg = gridDim.x;
-        const unsigned per = nwg > (unsigned)x ? (nwg - x + 7) / 8 : 0u;
+        const unsigned per = nwg > (unsigned)x ? (nwg - x + SR_NCTR - 1) / SR_NCTR : 0u;
         const unsigned want = (E + p) * per;
         unsigned *ctr = SS.ctr + x * 32;
         while (true) {
@@ -671,7 +674,7 @@ __device__ __forceinline__ bool arrive(SrLds &S) {
 }
 __device__ __forceinline__ void signal_phase() {
     vm_wait();
-    if ((threadIdx.x & 63) == 0) add_u(SS.ctr + (blockIdx.x & 7) * 32, 1u);
+    if ((threadIdx.x & 63) == 0) add_u(SS.ctr + (blockIdx.x % SR_NCTR) * 32, 1u);
 }
 // wave 1 of workgroup 0: stamp k of phase p at trace word 512 + 8p + k
 __device__ __forceinline__ void dbg_at(unsigned p, int k) {
