@@ -197,6 +197,7 @@ struct SrLds {
     unsigned phase;            // global phases known complete
     unsigned rphase;           // phase whose row scales rinv holds (+1)
     unsigned done;             // compute-wave arrivals (8 per phase)
+    unsigned stg;              // compute-wave arrivals at the attention staging (8 per layer)
     unsigned abort_;
 };
 
@@ -1088,10 +1089,10 @@ __device__ __attribute__((noinline)) unsigned gemm_phase(int kind, int l, unsign
 // attention phase (compute waves)
 // ---------------------------------------------------------------------------
 // q / k head vector of one lane: values (s, j) at d = KSA s + PQ g + j.
-// RMSNorm over head_dim (gain gk), NeoX rope at position pos (pairs s, s + NS/2),
-// times scale.
+// RMSNorm over head_dim (gain gk), NeoX rope with the row's cos/sin pairs
+// cs[d/2][2] (pairs s, s + NS/2), times scale.  gk and cs point into LDS.
 template <int WT, int D>
-__device__ __forceinline__ void norm_rope(float (&x)[D / 4], const float *gk, int r, float scale) {
+__device__ __forceinline__ void norm_rope(float (&x)[D / 4], const float *gk, const float *cs, float scale) {
     constexpr int PQ = AT<WT, D>::PQ, KSA = 4 * PQ, NS = D / KSA, NQV = AT<WT, D>::NQV;
     const int g = lane_id() >> 4;
     float ss = 0.f;
@@ -1104,7 +1105,6 @@ __device__ __forceinline__ void norm_rope(float (&x)[D / 4], const float *gk, in
     for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int j = 0; j < PQ; ++j) x[s * PQ + j] *= inv * gk[KSA * s + PQ * g + j];
-    const float *cs = SS.cs + (size_t)r * D;      // [r][d/2][2]
 #pragma unroll
     for (int s = 0; s < NS / 2; ++s)
 #pragma unroll
@@ -1115,6 +1115,33 @@ __device__ __forceinline__ void norm_rope(float (&x)[D / 4], const float *gk, in
             x[s * PQ + j] = (y0 * csv.x - y1 * csv.y) * scale;
             x[(s + NS / 2) * PQ + j] = (y1 * csv.x + y0 * csv.y) * scale;
         }
+}
+
+template <int WT, int D>
+__device__ __forceinline__ void load_head(float (&x)[D / 4], const char *src);
+
+// a lane's q / k head values as raw 16-byte words, then decoded: split so a
+// caller can issue several heads' loads before the first use
+template <int WT, int D> struct HeadWords { static constexpr int N = (D / 4) / (WT == WT_F32 ? 4 : 8); };
+template <int WT, int D>
+__device__ __forceinline__ void load_head_raw(u32x4 *u, const char *src) {
+#pragma unroll
+    for (int i = 0; i < HeadWords<WT, D>::N; ++i) u[i] = *reinterpret_cast<const u32x4 *>(src + 16 * i);
+}
+template <int WT, int D>
+__device__ __forceinline__ void decode_head(float (&x)[D / 4], const u32x4 *u) {
+#pragma unroll
+    for (int i = 0; i < HeadWords<WT, D>::N; ++i) {
+        if constexpr (WT == WT_F32) {
+            x[4 * i] = f_of(u[i].x); x[4 * i + 1] = f_of(u[i].y); x[4 * i + 2] = f_of(u[i].z); x[4 * i + 3] = f_of(u[i].w);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                x[8 * i + 2 * k] = bf16_bits_to_f32(u[i][k] & 0xFFFFu);
+                x[8 * i + 2 * k + 1] = __uint_as_float(u[i][k] & 0xFFFF0000u);
+            }
+        }
+    }
 }
 
 template <int WT, int D>
@@ -1228,12 +1255,44 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
         const size_t koff = (size_t)16 * SS.qd * AB, voff = (size_t)16 * (SS.qd + SS.kvd) * AB;
         const bool actw = v < SS.G;
         const int hq = it.h * SS.G + (actw ? v : 0);
+        // The layer's q/k head-norm gains and the block rows' cos/sin go to
+        // LDS (the GEMM reduction area is idle during attention), loaded in
+        // the same round trip as this wave's q head: [0, D) g_q, [D, 2D) g_k,
+        // [2D, 18D) cos/sin [16][D/2][2].
+        float *stg = reinterpret_cast<float *>(&S.red[0][0][0]);
+        static_assert(sizeof(S.red) >= 18 * D * sizeof(float), "staging fits the reduction area");
+        constexpr int HW = HeadWords<WT, D>::N, NV = 18 * D / 4;
+        u32x4 qraw[HW];
+        load_head_raw<WT, D>(qraw, qkv + (((size_t)(hq * 16 + r16) * 4 + g) * (D / 4)) * AB);
+        {
+            float4 sv[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int i = (int)threadIdx.x + k * SR_CW * 64;
+                const float *src = i < D / 4 ? ka()->L[l].g_q + 4 * i
+                                 : i < D / 2 ? ka()->L[l].g_k + 4 * (i - D / 4) : SS.cs + 4 * (i - D / 2);
+                if (i < NV) sv[k] = *reinterpret_cast<const float4 *>(src);
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int i = (int)threadIdx.x + k * SR_CW * 64;
+                if (i < NV) *reinterpret_cast<float4 *>(stg + 4 * i) = sv[k];
+            }
+            cbar();
+            if (lane == 0) lds_add(&S.stg, 1u);
+            int spins = 0;
+            while (lds_ld(&S.stg) < (unsigned)(SR_CW * (l + 1))) {
+                if (lds_ld(&S.abort_)) return false;
+                if (++spins > SPIN_LIMIT) { set_error(S); return false; }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
         // query fragments of q head hq, rows r16
         u32x4 qf[NC];
         {
             float x[NQV];
-            load_head<WT, D>(x, qkv + (((size_t)(hq * 16 + r16) * 4 + g) * (D / 4)) * AB);
-            norm_rope<WT, D>(x, ka()->L[l].g_q, r16, SS.mscale * SS.qscale);
+            decode_head<WT, D>(x, qraw);
+            norm_rope<WT, D>(x, stg, stg + 2 * D + r16 * D, SS.mscale * SS.qscale);
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 if constexpr (WT == WT_F32) {
@@ -1253,19 +1312,31 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
 #pragma unroll
         for (int t = 0; t < NDT; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (it.last && actw) {
-            // the block's own keys: normed + roped k and raw v of the b block rows
+            // the block's own keys: normed + roped k and raw v of the b block
+            // rows.  Every load is issued before the first use, so the block
+            // costs one memory round trip rather than one per operand.
+            const char *vT = qkv + voff;
+            constexpr int HW = HeadWords<WT, D>::N;
+            u32x4 kraw[2][HW], vraw[NDT][A::VH];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const int key = 8 * (r16 >> 2) + 4 * kt + (r16 & 3);      // < 16 always
+                load_head_raw<WT, D>(kraw[kt], qkv + koff + (((size_t)(it.h * 16 + key) * 4 + g) * (D / 4)) * AB);
+            }
+#pragma unroll
+            for (int t = 0; t < NDT; ++t)
+#pragma unroll
+                for (int hv = 0; hv < A::VH; ++hv) {
+                    const size_t e = ((size_t)it.h * D + 16 * t + r16) * 16 + 8 * (g & 1) + 4 * hv;
+                    vraw[t][hv] = *reinterpret_cast<const u32x4 *>(vT + e * AB);
+                }
             u32x4 kb[2][NC];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
                 const int key = 8 * (r16 >> 2) + 4 * kt + (r16 & 3);
                 float x[NQV];
-                if (key < 16) {
-                    load_head<WT, D>(x, qkv + koff + (((size_t)(it.h * 16 + key) * 4 + g) * (D / 4)) * AB);
-                    norm_rope<WT, D>(x, ka()->L[l].g_k, key, SS.mscale);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < NQV; ++i) x[i] = 0.f;
-                }
+                decode_head<WT, D>(x, kraw[kt]);
+                norm_rope<WT, D>(x, stg + D, stg + 2 * D + key * D, SS.mscale);
                 if (v == 0 && key < SS.b) {   // block K row to the cache (rows len + key)
                     constexpr int PQ = A::PQ;
                     char *kcache = SS.kc + (size_t)l * SS.kv_lstride;
@@ -1292,13 +1363,8 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
                     }
                 }
             }
-            const char *vT = qkv + voff;
             auto kf = [&](int kt, int c) -> u32x4 { return kb[kt][c]; };
-            auto vf = [&](int t, int hv) -> u32x4 {
-                if (g >= 2) return u32x4{0, 0, 0, 0};
-                const size_t e = ((size_t)it.h * D + 16 * t + r16) * 16 + 8 * g + 4 * hv;
-                return *reinterpret_cast<const u32x4 *>(vT + e * AB);
-            };
+            auto vf = [&](int t, int hv) -> u32x4 { return g >= 2 ? u32x4{0, 0, 0, 0} : vraw[t][hv]; };
             const int kend = SS.b - 8 * g;
             auto valid = [&](int i) { return i < kend; };
             attn_block<WT, D>(st, qf, kf, vf, valid);
@@ -1517,7 +1583,7 @@ __global__ __launch_bounds__(SR_THREADS, 1) void sround_kernel(SrArgs) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if (threadIdx.x < 64) {
         if (lane < SR_CW) S.cons[lane] = 0;
-        if (lane == 0) { S.pub = 0; S.phase = 0; S.rphase = 0; S.done = 0; S.abort_ = 0; }
+        if (lane == 0) { S.pub = 0; S.phase = 0; S.rphase = 0; S.done = 0; S.stg = 0; S.abort_ = 0; }
     }
     __syncthreads();
     if (wave == SR_CW) {
