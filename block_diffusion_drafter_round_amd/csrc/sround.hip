@@ -1421,7 +1421,10 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
 template <int WT, int D>
 __device__ __forceinline__ bool merge_phase(SrLds &S, int l, unsigned p) {
     constexpr int AB = TR<WT>::AB;
-    constexpr int NDG = D / 8, NSG = 64 / NDG;      // d groups of 8, split groups
+    // one unit of work: a (row, q head) query and a 32-wide part of head_dim,
+    // so every compute wave of the grid takes a share; lane (dg, sg) holds
+    // 8 dims (group dg) of the splits sg, sg + NSG, ...
+    constexpr int DP = 32, DQ = D / DP, NDG = DP / 8, NSG = 64 / NDG, NPS = SR_MAX_SPLITS / NSG;
     const int lane = lane_id(), v = wave_id();
     const int dg = lane % NDG, sg = lane / NDG;
     char *lb = layer_buf(l);
@@ -1429,36 +1432,33 @@ __device__ __forceinline__ bool merge_phase(SrLds &S, int l, unsigned p) {
     const float *pml = (const float *)(lb + SS.o_pml);
     char *of = lb + SS.o_of;
     const int GQ = SS.G * 16, ns = SS.nsplit;
-    const int nqry = SS.nkv * GQ;
-    for (int qq = blockIdx.x * SR_CW + v; qq < nqry; qq += gridDim.x * SR_CW) {
+    const int nu = SS.nkv * GQ * DQ;
+    for (int u = blockIdx.x * SR_CW + v; u < nu; u += gridDim.x * SR_CW) {
+        const int qq = u / DQ, dq = u - qq * DQ;
         const int h = qq / GQ, qi = qq - h * GQ;
         const int j = qi >> 4, r = qi & 15;
         const int hq = h * SS.G + j;
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         float L = 1.f;
         if (r < SS.b) {
-            float m = -1e30f, lv = 0.f;
-            if (lane < ns) {
-                const float2 ml = *reinterpret_cast<const float2 *>(pml + ((size_t)(h * ns + lane) * GQ + qi) * 2);
-                m = ml.x;
-                lv = ml.y;
-            }
-            float M = m;
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-            const float w = lane < ns ? __builtin_amdgcn_exp2f(m - M) : 0.f;
-            L = wave_sum(w * lv);
-            // every split's partial is loaded before the first add
-            constexpr int NPS = SR_MAX_SPLITS / NSG;       // splits per lane at most
+            // every load (the splits' m, l and partial O) before the first use
+            float2 ml = make_float2(-1e30f, 0.f);
+            if (lane < ns) ml = *reinterpret_cast<const float2 *>(pml + ((size_t)(h * ns + lane) * GQ + qi) * 2);
             u32x4 raw[NPS][AB == 4 ? 2 : 1];
 #pragma unroll
             for (int i = 0; i < NPS; ++i) {
                 int sp = sg + NSG * i;
                 sp = sp < ns ? sp : 0;
-                const size_t e = ((size_t)(h * ns + sp) * GQ + qi) * D + 8 * dg;
+                const size_t e = ((size_t)(h * ns + sp) * GQ + qi) * D + DP * dq + 8 * dg;
                 raw[i][0] = *reinterpret_cast<const u32x4 *>(po + e * AB);
                 if constexpr (AB == 4) raw[i][AB == 4 ? 1 : 0] = *reinterpret_cast<const u32x4 *>(po + e * AB + 16);
             }
+            const float m = ml.x, lv = ml.y;
+            float M = m;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+            const float w = lane < ns ? __builtin_amdgcn_exp2f(m - M) : 0.f;
+            L = wave_sum(w * lv);
 #pragma unroll
             for (int i = 0; i < NPS; ++i) {
                 const int sp = sg + NSG * i;
@@ -1469,11 +1469,11 @@ __device__ __forceinline__ bool merge_phase(SrLds &S, int l, unsigned p) {
                     acc[0] += ws * f_of(a0.x); acc[1] += ws * f_of(a0.y); acc[2] += ws * f_of(a0.z); acc[3] += ws * f_of(a0.w);
                     acc[4] += ws * f_of(a1.x); acc[5] += ws * f_of(a1.y); acc[6] += ws * f_of(a1.z); acc[7] += ws * f_of(a1.w);
                 } else {
-                    const u32x4 u = raw[i][0];
+                    const u32x4 uu = raw[i][0];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        acc[2 * k] += ws * bf16_bits_to_f32(u[k] & 0xFFFFu);
-                        acc[2 * k + 1] += ws * __uint_as_float(u[k] & 0xFFFF0000u);
+                        acc[2 * k] += ws * bf16_bits_to_f32(uu[k] & 0xFFFFu);
+                        acc[2 * k + 1] += ws * __uint_as_float(uu[k] & 0xFFFF0000u);
                     }
                 }
             }
@@ -1484,7 +1484,7 @@ __device__ __forceinline__ bool merge_phase(SrLds &S, int l, unsigned p) {
             for (int k = 0; k < 8; ++k) acc[k] += __shfl_xor(acc[k], o, 64);
         if (sg == 0) {
             const float il = 1.f / L;
-            const int c = hq * D + 8 * dg;
+            const int c = hq * D + DP * dq + 8 * dg;
             put4<WT>(of, r, c, acc[0] * il, acc[1] * il, acc[2] * il, acc[3] * il);
             put4<WT>(of, r, c + 4, acc[4] * il, acc[5] * il, acc[6] * il, acc[7] * il);
         }
