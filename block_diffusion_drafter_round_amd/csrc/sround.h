@@ -6,7 +6,7 @@
 namespace dfl {
 
 constexpr int SR_CW = 8;                      // compute waves per workgroup
-constexpr int SR_THREADS = 64 * (SR_CW + 1);  // plus one loader wave
+constexpr int SR_THREADS = 64 * (SR_CW + 2);  // plus one loader and one service wave
 constexpr int SR_PART = 1024;                 // one wave-wide load: 64 lanes x 16 bytes
 constexpr int SR_SLOT = SR_CW * SR_PART;      // a ring slot holds one part per compute wave
 constexpr int SR_NSLOT = 15;                  // ring slots (120 KiB of LDS)

@@ -4,7 +4,9 @@
 // attention is full and non-causal over all len + b keys; [atlas dflash_head]
 // overview: pre-norm Qwen3 layers with GQA and a SwiGLU MLP).
 //
-// One workgroup per CU: one loader wave and eight compute waves.
+// One workgroup per CU: one loader wave, eight compute waves and one service
+// wave (it computes the rows' 1/rms for the norm-consuming phases as soon as
+// they open).
 //
 // Loader wave.  Weights and the committed K/V rows do not depend on the
 // round's activations, so the loader streams them, in the exact order the
@@ -1557,9 +1559,6 @@ __device__ __forceinline__ bool compute_main(SrLds &S) {
         for (int i = 0; i < np; ++i, ++p) {
             if (!wait_phase(S, p, E)) return false;
             const int k = kind_at(i);
-            char *lb = layer_buf(l);
-            if (wave == 0 && (k == K_Q || k == K_G || k == K_DA || k == K_DM))
-                compute_rinv(S, (const float *)(lb + ((k == K_Q || k == K_DA) ? SS.o_ssa : SS.o_ssm)), p, SS.H);
             bool ok;
             if (k == K_A) ok = attn_phase<WT, D>(S, cs, l, p);
             else if (k == K_M) ok = merge_phase<WT, D>(S, l, p);
@@ -1572,10 +1571,27 @@ __device__ __forceinline__ bool compute_main(SrLds &S) {
     }
     if (SS.last) {
         if (!wait_phase(S, p, E)) return false;
-        if (wave == 0) compute_rinv(S, (const float *)(layer_buf(nl) + SS.o_ssa), p, SS.H);
         final_phase(S, p);
     }
     return lds_ld(&S.abort_) == 0;
+}
+
+// Service wave: the rows' 1/rms of every norm-consuming phase (and of the
+// final norm) as soon as the phase opens, from the producers' partial sums
+// of squares, so no GEMM wave starts its share late.
+__device__ __forceinline__ void service_main(SrLds &S) {
+    const int nl = SS.nl, np = npl();
+    unsigned p = 1;
+    for (int l = 0; l < nl; ++l) {
+        for (int i = 0; i < np; ++i, ++p) {
+            const int k = kind_at(i);
+            if (k == K_Q || k == K_G || k == K_DA || k == K_DM) {
+                if (!wait_phase(S, p, 0u)) return;
+                compute_rinv(S, (const float *)(layer_buf(l) + ((k == K_Q || k == K_DA) ? SS.o_ssa : SS.o_ssm)), p, SS.H);
+            }
+        }
+    }
+    if (SS.last && wait_phase(S, p, 0u)) compute_rinv(S, (const float *)(layer_buf(nl) + SS.o_ssa), p, SS.H);
 }
 
 template <int WT, int D, bool C>
@@ -1589,6 +1605,10 @@ __global__ __launch_bounds__(SR_THREADS, 1) void sround_kernel(SrArgs) {
     if (wave == SR_CW) {
         loader_main<WT, D>(S);
         if (lds_ld_nodep(&S.abort_)) stc_u(SS.ctr + SR_CTR_ERR, 1u);
+        return;
+    }
+    if (wave == SR_CW + 1) {
+        service_main(S);
         return;
     }
     // compute waves
