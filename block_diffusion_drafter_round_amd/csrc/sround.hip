@@ -610,9 +610,10 @@ __device__ __forceinline__ bool wait_phase(SrLds &S, unsigned p, unsigned E) {
         const unsigned per = nwg > (unsigned)x ? (nwg - x + SR_NCTR - 1) / SR_NCTR : 0u;
         const unsigned want = (E + p) * per;
         unsigned *ctr = SS.ctr + x * 32;
+        bool seen = per == 0;       // counters are monotonic: a lane stops reading once its group is done
         while (true) {
-            const unsigned v = ldc_u(ctr);
-            if (__all((int)(v - want) >= 0)) break;
+            if (!seen) seen = (int)(ldc_u(ctr) - want) >= 0;
+            if (__all(seen)) break;
             if (lds_ld(&S.abort_)) return false;
             if (++spins > SPIN_LIMIT / 8) { set_error(S); return false; }
             // about 1.7 us between polls: each poll reads 64 lines device-wide
