@@ -145,6 +145,34 @@ def test_multi_round_append_then_round(cfg):
         check(f"{cfg.name} round {rnd} len={p}", out, O.forward_round(m, okv, noise, bpos), tol_for(cfg))
 
 
+@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_FP8_D128, SMALL_D2], ids=lambda c: c.name)
+@pytest.mark.parametrize("n,b", [(37, 16), (40, 5), (41, 7)])
+def test_round_writes_block_kv_rows(cfg, n, b):
+    """[DflashDraft] forward_round: the block's K (normed + roped) and V land
+    transiently at cache rows [len, len + b) while len stays.  Layer 0's
+    block rows are checked against the oracle's k/v of the block input
+    (with the DFlash2 wrap, of its prepared rows).  len = 37 and 41 are not
+    multiples of 4 and b = 5, 7 end inside a row quad, so the kernel's
+    partial-quad stores are covered next to the whole-quad ones."""
+    sw, m, dr, D = _setup(cfg, max_rows=64)
+    kv = D.KVCache(cfg, 128)
+    taps = synth.make_taps(cfg, n)
+    dr.ingest_ctx(kv, dr.ctx_features(dev(taps)), dev(synth.positions(0, n)))
+    noise = synth.make_noise(cfg, rows=b)
+    bpos = synth.positions(n, b)
+    dr.forward_round(kv, dev(noise), dev(bpos))
+    assert kv.len == n
+    L = m.layers[0]
+    xn = O.rms_norm(noise, L["g_in"], m.eps)
+    if cfg.d2_groups:
+        xn, _ = O.d2_prepare(xn, L["attn.w_dyn"], L["attn.base"], cfg.d2_groups)
+    ok, ov = O.ctx_kv(m, 0, xn, bpos)
+    k, v = kv_rows_f64(kv, 0, n, n + b)
+    tol = 1e-5 if cfg.kv_dtype == "f32" else 1e-2
+    check(f"{cfg.name} block K rows len={n} b={b}", k, ok, tol)
+    check(f"{cfg.name} block V rows len={n} b={b}", v, ov, tol)
+
+
 def test_d2_identity_taps_equal_backbone():
     """DFlash2 special case: with zero dynamic projections and static taps
     [0, 1] the wrap is the identity, so the output equals the same weights
