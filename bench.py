@@ -22,8 +22,11 @@ Printed as one JSON line:
   rocprofv3 FETCH_SIZE / WRITE_SIZE record committed under profiles/
   (each counter scaled by what it reads for a plain device copy of known
   size); null when the kernel's sources no longer match that record;
+* roofline.copy_gbs / frac_of_copy: the rate of a plain 1 GiB device copy
+  measured in the same run, and the kernel's achieved rate against it;
+* spread: p10 / p50 / p90 of 100 rounds timed one by one;
 * cpu_baseline: the fp64 CPU oracle running the same round on a bounded
-  sample.
+  sample, on all host threads and on one (value_1thread).
 
 ``python bench.py --copy-calibration`` only copies 256 MiB on the device five
 times: run under ``rocprofv3 --pmc FETCH_SIZE`` (then WRITE_SIZE) it gives the
@@ -144,20 +147,52 @@ def cpu_baseline(cfg, ctx: int, seconds: float) -> dict:
     noise = synth.make_noise(cfg)
     pos_new = synth.positions(base, 16)
     pos_blk = synth.positions(ctx, 16)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        feats = O.ctx_features(m, taps)
-        O.ingest_ctx(m, kv, feats, pos_new)
-        O.forward_round(m, kv, noise, pos_blk)
-        kv.truncate(base)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": n / el, "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} full rounds (ctx_features 16 + ingest 16 + forward_round b=16 at ctx {ctx}, "
-                      f"cache prefilled directly to {base} rows), {el:.1f} s, numpy fp64"}
+    def rounds(budget: float):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            feats = O.ctx_features(m, taps)
+            O.ingest_ctx(m, kv, feats, pos_new)
+            O.forward_round(m, kv, noise, pos_blk)
+            kv.truncate(base)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return n, el
+
+    n, el = rounds(seconds)
+    rec = {"value": n / el, "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{n} full rounds (ctx_features 16 + ingest 16 + forward_round b=16 at ctx {ctx}, "
+                     f"cache prefilled directly to {base} rows), {el:.1f} s, numpy fp64"}
+    try:  # the same rounds on one host thread (BLAS limited to 1)
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            n1, el1 = rounds(seconds / 2)
+        rec["value_1thread"] = n1 / el1
+        rec["sample_1thread"] = f"{n1} rounds, {el1:.1f} s, BLAS limited to 1 thread"
+    except Exception:  # pragma: no cover
+        pass
+    return rec
+
+
+def copy_reference(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """Device-to-device copy of `nbytes`: the HBM rate a plain streaming
+    kernel reaches on this GPU (it reads and writes nbytes per copy)."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return {"gbs": round(2 * nbytes / sec / 1e9, 1), "bytes_per_copy": 2 * nbytes,
+            "what": f"torch device copy of {nbytes >> 20} MiB (read + write), mean of {reps}"}
 
 
 def main(argv=None) -> int:
@@ -254,6 +289,22 @@ def main(argv=None) -> int:
                     "bytes_per_launch": gb, "avg_launch_us": round(avg_s * 1e6, 2), "launches": nl,
                     "ms_per_step_while_timed": round(max(gpu_p, wall_p) * 1e3 / args.steps, 4)}
 
+    # per-round spread: each of 100 rounds between its own pair of events
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
+    torch.cuda.synchronize()
+    for a, z in evs:
+        a.record(stream)
+        step()
+        z.record(stream)
+    torch.cuda.synchronize()
+    per = np.sort(np.array([a.elapsed_time(z) for a, z in evs]))
+    spread = {"round_ms_p10": round(float(np.percentile(per, 10)), 4), "round_ms_p50": round(float(np.median(per)), 4),
+              "round_ms_p90": round(float(np.percentile(per, 90)), 4), "rounds": len(per)}
+    copy = copy_reference(torch, dev)
+    if roofline is not None:
+        roofline["copy_gbs"] = copy["gbs"]
+        roofline["frac_of_copy"] = round(roofline["achieved"] / copy["gbs"], 4)
+
     cpu = None
     if not args.no_cpu:
         print(f"[bench] cpu oracle baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
@@ -271,6 +322,8 @@ def main(argv=None) -> int:
                    "ctx": ctx, "block": b, "weights": "bf16", "kv": "bf16"},
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "round_bytes": rb["total"],
+        "spread": spread,
+        "copy_reference": copy,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
