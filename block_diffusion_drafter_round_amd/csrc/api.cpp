@@ -81,6 +81,16 @@ struct WsLayout {
     dfl::SrLayout sl;
 };
 
+// ingest_ctx projects up to INGEST_FUSE_ROWS / t layers' k|v in one GEMM
+// (at most GEMM_MAX_SEG / 2 and ROPE_MAX_LAYERS): few new rows make a skinny,
+// latency-bound GEMM per layer, so the layers share one launch instead
+constexpr size_t INGEST_FUSE_ROWS = 128;
+
+int ingest_layers_per_launch(int t) {
+    const int n = t > 0 ? (int)(INGEST_FUSE_ROWS / (size_t)t) : 1;
+    return std::max(1, std::min({n, dfl::GEMM_MAX_SEG / 2, dfl::ROPE_MAX_LAYERS}));
+}
+
 // workgroups the round kernel is laid out for at most (partial sums of
 // squares are stored per workgroup)
 constexpr int WS_MAX_NWG = 256;
@@ -103,7 +113,7 @@ WsLayout ws_layout(const dflash_cfg &c, int max_rows) {
     L.lay_stride = (size_t)L.sl.stride;
     L.lay = take(L.lay_stride * (dfl::SR_MAXL + 1));
     // row-dependent regions
-    L.qkv = take(4 * rows * 2 * kvd);
+    L.qkv = take(4 * std::max<size_t>(rows, INGEST_FUSE_ROWS) * 2 * kvd);
     L.feats = take(4 * rows * H);
     L.total = off;
     return L;
@@ -238,13 +248,20 @@ hipError_t run_ingest(const dflash_model *m, dflash_kv *kv, const float *feats, 
                       const WsLayout &L, hipStream_t s) {
     const dflash_cfg &c = m->cfg;
     const int kvd = c.n_kv_heads * c.head_dim;
+    const int per = ingest_layers_per_launch(t);
     float *kvbuf = at<float>(ws, L.qkv);
-    for (int l = 0; l < c.n_layers; ++l) {
-        const dflash_layer_weights &W = m->layers[l];
+    for (int l0 = 0; l0 < c.n_layers; l0 += per) {
+        const int nl = std::min(per, c.n_layers - l0);
+        // k|v of layers l0 .. l0 + nl - 1 side by side: [t][nl * 2 * kvd]
         dfl::GemmArgs g{};
         g.A = feats; g.lda = c.hidden; g.M = t; g.K = c.hidden;
-        g.seg[0] = seg(W.wk, kvd); g.seg[1] = seg(W.wv, kvd); g.nseg = 2;
-        g.Y = kvbuf; g.ldy = 2 * kvd; g.epi = dfl::EPI_STORE; g.wtype = wtype(c);
+        for (int i = 0; i < nl; ++i) {
+            const dflash_layer_weights &W = m->layers[l0 + i];
+            g.seg[2 * i] = seg(W.wk, kvd);
+            g.seg[2 * i + 1] = seg(W.wv, kvd);
+        }
+        g.nseg = 2 * nl;
+        g.Y = kvbuf; g.ldy = nl * 2 * kvd; g.epi = dfl::EPI_STORE; g.wtype = wtype(c);
         hipError_t e;
         {
             ProfScope p(DFLASH_K_GEMM_KV, s);
@@ -252,15 +269,18 @@ hipError_t run_ingest(const dflash_model *m, dflash_kv *kv, const float *feats, 
         }
         if (e != hipSuccess) return e;
         dfl::RopeArgs r{};
-        r.src = kvbuf; r.ld = 2 * kvd; r.q_off = -1; r.k_off = 0; r.v_off = kvd;
-        r.g_q = nullptr; r.g_k = W.g_k; r.pos = pos; r.rows = t;
-        r.nq = c.n_q_heads; r.nkv = c.n_kv_heads; r.d = c.head_dim; r.eps = c.rms_eps; r.mscale = (float)m->mscale;
-        r.q_out = nullptr; r.kc = layer_ptr(kv->k, c, kv->capacity, l); r.vc = layer_ptr(kv->v, c, kv->capacity, l);
-        r.cap = kv->capacity; r.row0 = kv->len; r.kv_f32 = c.kv_dtype == DFLASH_F32;
+        r.src = kvbuf; r.ld = nl * 2 * kvd; r.lstride = 2 * kvd; r.nl = nl;
+        for (int i = 0; i < nl; ++i) {
+            r.g_k[i] = m->layers[l0 + i].g_k;
+            r.kc[i] = layer_ptr(kv->k, c, kv->capacity, l0 + i);
+            r.vc[i] = layer_ptr(kv->v, c, kv->capacity, l0 + i);
+        }
+        r.pos = pos; r.rows = t; r.nkv = c.n_kv_heads; r.d = c.head_dim; r.eps = c.rms_eps;
+        r.mscale = (float)m->mscale; r.cap = kv->capacity; r.row0 = kv->len; r.kv_f32 = c.kv_dtype == DFLASH_F32;
         memcpy(r.inv_freq, m->inv_freq, sizeof r.inv_freq);
         {
             ProfScope p(DFLASH_K_ROPE, s);
-            e = dfl::qk_norm_rope(r, s);
+            e = dfl::kv_norm_rope(r, s);
         }
         if (e != hipSuccess) return e;
     }

@@ -15,10 +15,12 @@ struct GemmSeg {
     int          n;      // output columns of this segment (multiple of 16)
 };
 
+constexpr int GEMM_MAX_SEG = 16;
+
 struct GemmArgs {
     const float *A; int lda; int M; int K;
-    GemmSeg seg[3]; int nseg;     // the output columns are the segments side by side
-                                  // (EPI_SWIGLU: seg[0] = gate, seg[1] = up, same n)
+    GemmSeg seg[GEMM_MAX_SEG]; int nseg;  // the output columns are the segments side by side
+                                          // (EPI_SWIGLU: seg[0] = gate, seg[1] = up, same n)
     float *Y; int ldy;
     int epi;
     int wtype;
@@ -42,22 +44,24 @@ int gemm_plan(GemmArgs &a);
 hipError_t rmsnorm(const float *x, int ldx, const float *g, float *y, int ldy,
                    float *xcopy, int rows, int H, float eps, hipStream_t s);
 
-// ---- q/k head norm + rope (+ mscale) and KV stores --------------------------
+// ---- k head norm + rope (+ mscale) and KV stores, several layers at once ----
 constexpr int MAX_HALF_DIM = 64;
+constexpr int ROPE_MAX_LAYERS = 8;
 struct RopeArgs {
-    const float *src; int ld;     // [rows, ld] projection output
-    int q_off, k_off, v_off;      // column offsets; q_off < 0: no q heads
-    const float *g_q, *g_k;
+    const float *src; int ld;     // [rows, ld] projection output; layer i's k heads start at
+    int lstride;                  // column i * lstride, its v heads kvd = nkv * d further on
+    int nl;                       // layers in this launch (<= ROPE_MAX_LAYERS)
+    const float *g_k[ROPE_MAX_LAYERS];
+    void *kc[ROPE_MAX_LAYERS];    // layer i's K [nkv][cap][d] and V [nkv][d][cap]
+    void *vc[ROPE_MAX_LAYERS];
     const int32_t *pos;
-    int rows, nq, nkv, d;
+    int rows, nkv, d;
     float eps; float mscale;
-    float *q_out;                 // [rows][nq][d] f32
-    void *kc; void *vc;           // this layer's K [nkv][cap][d] and V [nkv][d][cap]
     int cap; int row0;            // cache rows row0 .. row0 + rows - 1
     int kv_f32;                   // 1: f32 cache, 0: bf16 cache
     double inv_freq[MAX_HALF_DIM];
 };
-hipError_t qk_norm_rope(const RopeArgs &a, hipStream_t s);
+hipError_t kv_norm_rope(const RopeArgs &a, hipStream_t s);
 
 
 }  // namespace dfl

@@ -3,17 +3,18 @@
 // RMSNorm ([DflashDraft] "ctx_features": hidden_norm; the layer norms and the
 // final norm): y = g * x / sqrt(mean(x^2) + eps).  One workgroup per row.
 //
-// Head norm + rope ([memra dflash module] "DflashKv": cached K is
+// K head norm + rope ([memra dflash module] "DflashKv": cached K is
 // normed+roped, V raw; [DflashDraft] "rope_yarn": rope_neox_ff with
 // per-dimension inverse frequencies, then the q/k scale mscale).
-// * One workgroup per row.  It first builds the row's cos/sin table.  The
-//   angle pos * inv_freq[j] and its sin/cos are evaluated in f64, so long
-//   positions keep full accuracy.
+// * One workgroup per (row, layer), so one launch covers every layer whose
+//   k|v projections one GEMM produced side by side.  It first builds the
+//   row's cos/sin table.  The angle pos * inv_freq[j] and its sin/cos are
+//   evaluated in f64, so long positions keep full accuracy.
 // * Each wave then takes heads in turn.  Lane j < d/2 holds the rope pair
 //   (j, j + d/2) of one head: one wave-wide sum of squares gives the head's
 //   RMS, and the rotation is lane-local.
-// * q goes to a f32 buffer.  k and v go to the layer's cache at rows
-//   row0 + r: K [nkv][cap][d], V transposed [nkv][d][cap].
+// * k and v go to the layer's cache at rows row0 + r: K [nkv][cap][d],
+//   V transposed [nkv][d][cap].
 #include "common.h"
 #include "kernels.h"
 
@@ -56,8 +57,8 @@ __device__ __forceinline__ void store_kv(void *base, size_t idx, float v, int kv
     else reinterpret_cast<uint16_t *>(base)[idx] = (uint16_t)f32_to_bf16_bits(v);
 }
 
-__global__ __launch_bounds__(256) void qk_norm_rope_kernel(RopeArgs a) {
-    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(256) void kv_norm_rope_kernel(RopeArgs a) {
+    const int r = blockIdx.x, l = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = a.d >> 1;
     __shared__ float cs[MAX_HALF_DIM], sn[MAX_HALF_DIM];
     if (tid < half) {
@@ -69,20 +70,17 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(RopeArgs a) {
     }
     __syncthreads();
 
-    const float *row = a.src + (size_t)r * a.ld;
-    const int nqh = a.q_off >= 0 ? a.nq : 0;
-    const int nnorm = nqh + a.nkv;          // heads that get norm + rope
-    const int nheads = nnorm + a.nkv;       // + raw v heads
+    const float *row = a.src + (size_t)r * a.ld + (size_t)l * a.lstride;
+    const float *gain = a.g_k[l];
+    void *kc = a.kc[l], *vc = a.vc[l];
+    const int kvd = a.nkv * a.d;
     const bool act = lane < half;
     const float c = act ? cs[lane] : 0.f, s = act ? sn[lane] : 0.f;
     const size_t crow = (size_t)(a.row0 + r);
 
-    for (int h = wave; h < nheads; h += 4) {
-        if (h < nnorm) {
-            const bool isq = h < nqh;
-            const int hh = isq ? h : h - nqh;
-            const float *src = row + (isq ? a.q_off : a.k_off) + hh * a.d;
-            const float *gain = isq ? a.g_q : a.g_k;
+    for (int h = wave; h < 2 * a.nkv; h += 4) {
+        if (h < a.nkv) {
+            const float *src = row + h * a.d;
             const float x0 = act ? src[lane] : 0.f, x1 = act ? src[lane + half] : 0.f;
             const float ss = wave_sum(x0 * x0 + x1 * x1);
             const float inv = 1.f / sqrtf(ss / (float)a.d + a.eps);
@@ -90,28 +88,23 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(RopeArgs a) {
                 const float y0 = gain[lane] * (x0 * inv), y1 = gain[lane + half] * (x1 * inv);
                 const float o0 = (y0 * c - y1 * s) * a.mscale;
                 const float o1 = (y1 * c + y0 * s) * a.mscale;
-                if (isq) {
-                    float *q = a.q_out + ((size_t)r * a.nq + hh) * a.d;
-                    q[lane] = o0;
-                    q[lane + half] = o1;
-                } else {
-                    const size_t base = ((size_t)hh * a.cap + crow) * a.d;
-                    store_kv(a.kc, base + lane, o0, a.kv_f32);
-                    store_kv(a.kc, base + lane + half, o1, a.kv_f32);
-                }
+                const size_t base = ((size_t)h * a.cap + crow) * a.d;
+                store_kv(kc, base + lane, o0, a.kv_f32);
+                store_kv(kc, base + lane + half, o1, a.kv_f32);
             }
         } else if (act) {
-            const int hh = h - nnorm;
-            const float *src = row + a.v_off + hh * a.d;
-            store_kv(a.vc, ((size_t)hh * a.d + lane) * a.cap + crow, src[lane], a.kv_f32);
-            store_kv(a.vc, ((size_t)hh * a.d + lane + half) * a.cap + crow, src[lane + half], a.kv_f32);
+            const int hh = h - a.nkv;
+            const float *src = row + kvd + hh * a.d;
+            store_kv(vc, ((size_t)hh * a.d + lane) * a.cap + crow, src[lane], a.kv_f32);
+            store_kv(vc, ((size_t)hh * a.d + lane + half) * a.cap + crow, src[lane + half], a.kv_f32);
         }
     }
 }
 
-hipError_t qk_norm_rope(const RopeArgs &a, hipStream_t s) {
-    if (a.rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(qk_norm_rope_kernel, dim3(a.rows), dim3(256), 0, s, a);
+hipError_t kv_norm_rope(const RopeArgs &a, hipStream_t s) {
+    if (a.rows <= 0 || a.nl <= 0) return hipSuccess;
+    if (a.nl > ROPE_MAX_LAYERS || a.d > 2 * MAX_HALF_DIM) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kv_norm_rope_kernel, dim3(a.rows, a.nl), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -89,6 +89,33 @@ def test_ingest_cache_rows(cfg):
         check(f"{cfg.name} layer {l} cached V", v, okv.v[l], tol)
 
 
+@pytest.mark.parametrize("n_layers", [5, 10])
+def test_ingest_layer_groups(n_layers):
+    """ingest_ctx projects several layers' k|v in one launch when few rows come
+    in (up to 8 layers at 16 rows or fewer, 3 at 40, 2 at 64, 1 at 129), with a
+    ragged last group when the layer count does not divide: every layer's
+    cache rows must still match the oracle."""
+    cfg = SMALL_BF16.replace(name=f"small_bf16_l{n_layers}", n_layers=n_layers, seed=40 + n_layers)
+    sw, m, dr, D = _setup(cfg, max_rows=129)
+    sizes = (1, 16, 40, 64, 129)
+    n = sum(sizes)
+    taps = synth.make_taps(cfg, n)
+    pos = synth.positions(500, n)
+    kv = D.KVCache(cfg, 256)
+    lo = 0
+    for t in sizes:
+        feats = dr.ctx_features(dev(taps[lo:lo + t]))
+        dr.ingest_ctx(kv, feats, dev(pos[lo:lo + t]))
+        lo += t
+        assert kv.len == lo
+    okv = O.OracleKV(cfg)
+    O.ingest_ctx(m, okv, O.ctx_features(m, taps), pos)
+    for l in range(cfg.n_layers):
+        k, v = kv_rows_f64(kv, l, 0, n)
+        check(f"{cfg.name} layer {l} cached K", k, okv.k[l], 1e-2)
+        check(f"{cfg.name} layer {l} cached V", v, okv.v[l], 1e-2)
+
+
 @pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_BF16_D128, SMALL_FP8, SMALL_FP8_D128] + D2_CFGS,
                          ids=lambda c: c.name)
 @pytest.mark.parametrize("b", [16, 5, 1])
