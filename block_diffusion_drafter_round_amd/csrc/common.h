@@ -31,12 +31,16 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c) {
 // bf16 bit patterns <-> float
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// round-to-nearest-even f32 -> bf16 bits (finite inputs)
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// round-to-nearest-even f32 pair -> packed bf16 bits, a in the low half
+// (one v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t bf16_pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
+// round-to-nearest-even f32 -> bf16 bits
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return bf16_pack(f, 0.f) & 0xFFFFu; }
 
 // Split 8 floats into bf16 hi + lo parts, hi = rne(x), lo = rne(x - hi).
 // hi + lo carries about 16 significant bits, so a bf16 MFMA over (hi, lo)
@@ -45,10 +49,9 @@ __device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8 &hi, bf
     uint32_t h[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        uint32_t h0 = f32_to_bf16_bits(x[2 * i]), h1 = f32_to_bf16_bits(x[2 * i + 1]);
-        float r0 = x[2 * i] - bf16_bits_to_f32(h0), r1 = x[2 * i + 1] - bf16_bits_to_f32(h1);
-        h[i] = h0 | (h1 << 16);
-        l[i] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
+        h[i] = bf16_pack(x[2 * i], x[2 * i + 1]);
+        const float r0 = x[2 * i] - __uint_as_float(h[i] << 16), r1 = x[2 * i + 1] - __uint_as_float(h[i] & 0xFFFF0000u);
+        l[i] = bf16_pack(r0, r1);
     }
     u32x4 hv = {h[0], h[1], h[2], h[3]};
     u32x4 lv = {l[0], l[1], l[2], l[3]};
@@ -59,7 +62,7 @@ __device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8 &hi, bf
 __device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
     uint32_t h[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = f32_to_bf16_bits(x[2 * i]) | (f32_to_bf16_bits(x[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) h[i] = bf16_pack(x[2 * i], x[2 * i + 1]);
     u32x4 v = {h[0], h[1], h[2], h[3]};
     return __builtin_bit_cast(bf16x8, v);
 }

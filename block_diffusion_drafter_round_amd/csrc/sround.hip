@@ -120,7 +120,7 @@ __device__ __forceinline__ void lds_st_nodep(unsigned *p, unsigned v) {
     asm volatile("ds_write_b32 %0, %1" : : "v"(lds_off(p)), "v"(v) : "memory");
 }
 __device__ __forceinline__ float f_of(uint32_t u) { return __uint_as_float(u); }
-__device__ __forceinline__ uint32_t bf2(float a, float b) { return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16); }
+__device__ __forceinline__ uint32_t bf2(float a, float b) { return bf16_pack(a, b); }
 
 // Lane and wave index behind an opaque copy: values derived from them are
 // recomputed inside each phase rather than hoisted out of the layer loop
@@ -176,12 +176,20 @@ __device__ __forceinline__ void put4(void *buf, int r, int c, float x0, float x1
 // Two-plane bf16 activations (used with the DFlash2 wrap): the plane at buf
 // holds bf16(x), the plane lo_off bytes further the rounding residual
 // bf16(x - bf16(x)), so a GEMM over both planes sees x to about 16 bits.
-__device__ __forceinline__ float bf_round(float x) { return bf16_bits_to_f32(f32_to_bf16_bits(x)); }
+__device__ __forceinline__ float bf_round(float x) { return __uint_as_float(bf16_pack(x, 0.f) << 16); }
 template <int WT, bool HL>
 __device__ __forceinline__ void put4x(void *buf, size_t lo_off, int r, int c, float x0, float x1, float x2, float x3) {
-    put4<WT>(buf, r, c, x0, x1, x2, x3);
-    if constexpr (HL)
-        put4<WT>((char *)buf + lo_off, r, c, x0 - bf_round(x0), x1 - bf_round(x1), x2 - bf_round(x2), x3 - bf_round(x3));
+    if constexpr (HL) {
+        static_assert(TR<WT>::AB == 2, "two planes hold bf16 activations");
+        const uint32_t h01 = bf16_pack(x0, x1), h23 = bf16_pack(x2, x3);
+        const size_t e = frag_idx<WT>(r, c);
+        st8(buf, e * 2, u32x2{h01, h23});
+        st8((char *)buf + lo_off, e * 2,
+            u32x2{bf16_pack(x0 - __uint_as_float(h01 << 16), x1 - __uint_as_float(h01 & 0xFFFF0000u)),
+                  bf16_pack(x2 - __uint_as_float(h23 << 16), x3 - __uint_as_float(h23 & 0xFFFF0000u))});
+    } else {
+        put4<WT>(buf, r, c, x0, x1, x2, x3);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1266,10 +1274,32 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
         // The layer's q/k head-norm gains and the block rows' cos/sin go to
         // LDS (the GEMM reduction area is idle during attention), loaded in
         // the same round trip as this wave's q head: [0, D) g_q, [D, 2D) g_k,
-        // [2D, 18D) cos/sin [16][D/2][2].
+        // then the cos/sin rows [16][D/2][2], CSR floats apart.  Lanes of one
+        // head read the same pair of 16 different rows; the 4-float pad puts
+        // those rows in different LDS banks.
+        constexpr int CSR = D + 4, CS0 = 2 * D, STG = CS0 + 16 * CSR;
         float *stg = reinterpret_cast<float *>(&S.red[0][0][0]);
-        static_assert(sizeof(S.red) >= 18 * D * sizeof(float), "staging fits the reduction area");
         constexpr int HW = HeadWords<WT, D>::N, NV = 18 * D / 4;
+        // The last split also attends the block's own keys.  Their raw k rows
+        // [16][D] (KRS bytes apart, padded like the cos/sin rows) and v^T
+        // [D][16] of kv head h go to LDS after the staging area, 1 KB per wave
+        // and load, in the same round trip as the q head.  Every wave then
+        // reads them from LDS instead of loading them itself once q is done.
+        constexpr int KRB = 16 * D * AB, RB = D * AB, KRS = RB + 16, NCH = 2 * KRB / 1024;
+        static_assert(KRB % 1024 == 0 && NCH <= 2 * SR_CW, "block k / v rows fill at most two 1 KB loads per wave");
+        static_assert(sizeof(S.red) >= 4 * STG + 16 * KRS + KRB, "staging and block rows fit the reduction area");
+        char *bk = reinterpret_cast<char *>(stg + STG), *bv = bk + 16 * KRS;
+        u32x4 braw[2];
+        if (it.last) {
+            const char *ksrc = qkv + koff + (size_t)it.h * KRB, *vsrc = qkv + voff + (size_t)it.h * KRB;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c = v + SR_CW * j;
+                if (c < NCH)
+                    braw[j] = *reinterpret_cast<const u32x4 *>((c < NCH / 2 ? ksrc + 1024 * c : vsrc + 1024 * (c - NCH / 2)) +
+                                                               16 * lane);
+            }
+        }
         u32x4 qraw[HW];
         load_head_raw<WT, D>(qraw, qkv + (((size_t)(hq * 16 + r16) * 4 + g) * (D / 4)) * AB);
         {
@@ -1284,7 +1314,20 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int i = (int)threadIdx.x + k * SR_CW * 64;
-                if (i < NV) *reinterpret_cast<float4 *>(stg + 4 * i) = sv[k];
+                const int f = 4 * (i - D / 2);      // cos/sin float index
+                float *dst = i < D / 2 ? stg + 4 * i : stg + CS0 + (f / D) * CSR + f % D;
+                if (i < NV) *reinterpret_cast<float4 *>(dst) = sv[k];
+            }
+            if (it.last) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int c = v + SR_CW * j;
+                    if (c < NCH) {
+                        const int o = 1024 * c + 16 * lane;
+                        char *dst = c < NCH / 2 ? bk + (o / RB) * KRS + o % RB : bv + (o - KRB);
+                        *reinterpret_cast<u32x4 *>(dst) = braw[j];
+                    }
+                }
             }
             cbar();
             if (lane == 0) lds_add(&S.stg, 1u);
@@ -1300,7 +1343,7 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
         {
             float x[NQV];
             decode_head<WT, D>(x, qraw);
-            norm_rope<WT, D>(x, stg, stg + 2 * D + r16 * D, SS.mscale * SS.qscale);
+            norm_rope<WT, D>(x, stg, stg + CS0 + r16 * CSR, SS.mscale * SS.qscale);
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 if constexpr (WT == WT_F32) {
@@ -1321,22 +1364,22 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
         for (int t = 0; t < NDT; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (it.last && actw) {
             // the block's own keys: normed + roped k and raw v of the b block
-            // rows.  Every load is issued before the first use, so the block
-            // costs one memory round trip rather than one per operand.
-            const char *vT = qkv + voff;
-            constexpr int HW = HeadWords<WT, D>::N;
+            // rows, read from the LDS copy.  Lanes of tile keys 16..31 (no
+            // such rows) take zeros; their scores are masked anyway.
             u32x4 kraw[2][HW], vraw[NDT][A::VH];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                const int key = 8 * (r16 >> 2) + 4 * kt + (r16 & 3);      // < 16 always
-                load_head_raw<WT, D>(kraw[kt], qkv + koff + (((size_t)(it.h * 16 + key) * 4 + g) * (D / 4)) * AB);
+                const int key = 8 * (r16 >> 2) + 4 * kt + (r16 & 3);
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(bk + key * KRS + g * (D / 4) * AB);
+#pragma unroll
+                for (int i = 0; i < HW; ++i) kraw[kt][i] = key < 16 ? src[i] : u32x4{0, 0, 0, 0};
             }
 #pragma unroll
             for (int t = 0; t < NDT; ++t)
 #pragma unroll
                 for (int hv = 0; hv < A::VH; ++hv) {
-                    const size_t e = ((size_t)it.h * D + 16 * t + r16) * 16 + 8 * (g & 1) + 4 * hv;
-                    vraw[t][hv] = *reinterpret_cast<const u32x4 *>(vT + e * AB);
+                    const int e = (16 * t + r16) * 16 + 8 * (g & 1) + 4 * hv;
+                    vraw[t][hv] = *reinterpret_cast<const u32x4 *>(bv + (size_t)e * AB);
                 }
             u32x4 kb[2][NC];
 #pragma unroll
@@ -1344,7 +1387,7 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
                 const int key = 8 * (r16 >> 2) + 4 * kt + (r16 & 3);
                 float x[NQV];
                 decode_head<WT, D>(x, kraw[kt]);
-                norm_rope<WT, D>(x, stg + D, stg + 2 * D + key * D, SS.mscale);
+                norm_rope<WT, D>(x, stg + D, stg + CS0 + key * CSR, SS.mscale);
                 if (v == 0 && key < SS.b) {   // block K row to the cache (rows len + key)
                     constexpr int PQ = A::PQ;
                     char *kcache = SS.kc + (size_t)l * SS.kv_lstride;
