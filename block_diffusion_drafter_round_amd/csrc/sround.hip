@@ -1286,48 +1286,43 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
         // and load, in the same round trip as the q head.  Every wave then
         // reads them from LDS instead of loading them itself once q is done.
         constexpr int KRB = 16 * D * AB, RB = D * AB, KRS = RB + 16, NCH = 2 * KRB / 1024;
-        static_assert(KRB % 1024 == 0 && NCH <= 2 * SR_CW, "block k / v rows fill at most two 1 KB loads per wave");
+        static_assert(KRB % 1024 == 0 && NCH <= SR_CW, "block k / v rows fill at most one 1 KB load per wave");
         static_assert(sizeof(S.red) >= 4 * STG + 16 * KRS + KRB, "staging and block rows fit the reduction area");
         char *bk = reinterpret_cast<char *>(stg + STG), *bv = bk + 16 * KRS;
-        u32x4 braw[2];
+        // Loads below are unconditional (indices clamped into range; only the
+        // LDS stores are guarded), so their values stay in registers and every
+        // load of the round trip is in flight at once.
+        u32x4 braw = u32x4{0, 0, 0, 0};
         if (it.last) {
             const char *ksrc = qkv + koff + (size_t)it.h * KRB, *vsrc = qkv + voff + (size_t)it.h * KRB;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int c = v + SR_CW * j;
-                if (c < NCH)
-                    braw[j] = *reinterpret_cast<const u32x4 *>((c < NCH / 2 ? ksrc + 1024 * c : vsrc + 1024 * (c - NCH / 2)) +
-                                                               16 * lane);
-            }
+            const int c = min(v, NCH - 1);
+            braw = *reinterpret_cast<const u32x4 *>((c < NCH / 2 ? ksrc + 1024 * c : vsrc + 1024 * (c - NCH / 2)) + 16 * lane);
         }
         u32x4 qraw[HW];
         load_head_raw<WT, D>(qraw, qkv + (((size_t)(hq * 16 + r16) * 4 + g) * (D / 4)) * AB);
         {
-            float4 sv[2];
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int i = (int)threadIdx.x + k * SR_CW * 64;
+            constexpr int NK = (NV + SR_CW * 64 - 1) / (SR_CW * 64);
+            static_assert(NK <= 2, "staging takes at most two float4 per thread");
+            auto src_of = [&](int i) -> const float4 * {
                 const float *src = i < D / 4 ? ka()->L[l].g_q + 4 * i
                                  : i < D / 2 ? ka()->L[l].g_k + 4 * (i - D / 4) : SS.cs + 4 * (i - D / 2);
-                if (i < NV) sv[k] = *reinterpret_cast<const float4 *>(src);
-            }
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int i = (int)threadIdx.x + k * SR_CW * 64;
+                return reinterpret_cast<const float4 *>(src);
+            };
+            auto put = [&](int i, float4 x) {
                 const int f = 4 * (i - D / 2);      // cos/sin float index
                 float *dst = i < D / 2 ? stg + 4 * i : stg + CS0 + (f / D) * CSR + f % D;
-                if (i < NV) *reinterpret_cast<float4 *>(dst) = sv[k];
-            }
-            if (it.last) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int c = v + SR_CW * j;
-                    if (c < NCH) {
-                        const int o = 1024 * c + 16 * lane;
-                        char *dst = c < NCH / 2 ? bk + (o / RB) * KRS + o % RB : bv + (o - KRB);
-                        *reinterpret_cast<u32x4 *>(dst) = braw[j];
-                    }
-                }
+                if (i < NV) *reinterpret_cast<float4 *>(dst) = x;
+            };
+            const int i0 = (int)threadIdx.x, i1 = i0 + SR_CW * 64;
+            const float4 sv0 = *src_of(min(i0, NV - 1));
+            float4 sv1 = float4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (NK == 2) sv1 = *src_of(min(i1, NV - 1));
+            put(i0, sv0);
+            if constexpr (NK == 2) put(i1, sv1);
+            if (it.last && v < NCH) {
+                const int o = 1024 * v + 16 * lane;
+                char *dst = v < NCH / 2 ? bk + (o / RB) * KRS + o % RB : bv + (o - KRB);
+                *reinterpret_cast<u32x4 *>(dst) = braw;
             }
             cbar();
             if (lane == 0) lds_add(&S.stg, 1u);
