@@ -9,11 +9,12 @@
 // * A workgroup of 4 waves takes one item.  Wave w owns the 16 columns
 //   [16w, 16w + 16) of the group (with SwiGLU, also the matching 16 up
 //   columns).
-// * Per K chunk, every wave first issues all of its weight loads.  Each lane
-//   loads one 16-byte piece per step and weight row: bf16 8 values (K step
-//   32), fp8 16 codes (K step 64), f32 4 values (K step 16).
-// * Meanwhile the workgroup stages the activation chunk in LDS once, in MFMA
-//   fragment order.  bf16/fp8 weights use the activations split into bf16
+// * Per K chunk, every thread first issues its activation loads, then every
+//   wave all of its weight loads.  Each lane loads one 16-byte piece per
+//   step and weight row: bf16 8 values (K step 32), fp8 16 codes (K step
+//   64), f32 4 values (K step 16).
+// * While the weight loads are in flight, the workgroup stages the
+//   activations in LDS once, in MFMA fragment order.  bf16/fp8 weights use the activations split into bf16
 //   hi + lo parts (two MFMAs 16x16x32 per step, ~16-bit activation
 //   precision).  f32 weights use MFMA 16x16x4 f32 on the f32 values.
 // * The MFMAs then read A from LDS (one 16-byte read per fragment) and W
@@ -43,25 +44,45 @@ __device__ __forceinline__ float ld_coherent(const float *p) {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Stage A[m0 .. m0+16*MT)[k0 .. k0 + NSTEP*KS) into LDS fragments.
+// Stage A[m0 .. m0+16*MT)[k0 .. k0 + NSTEP*KS) into LDS fragments, in two
+// halves: load_a issues every load of the chunk at once (addresses clamped
+// into range, so the values stay in registers), put_a converts them and
+// writes the fragments; the caller issues the weight loads in between.
 // Layout: lds[((mt * NSTEP + s) * FR + f) * 64 + lane] (16 bytes each).
+template <int WT, int MT, int NSTEP> struct AStage {
+    static constexpr int GROUPS = NSTEP * WCfg<WT>::KS / 8;   // 8-float groups per row
+    static constexpr int TOTAL = MT * 16 * GROUPS;
+    static constexpr int IT = (TOTAL + 255) / 256;            // groups per thread
+    float4 v[IT][2];
+};
+
 template <int WT, int MT, int NSTEP>
-__device__ __forceinline__ void stage_a(u32x4 *lds, const GemmArgs &p, int m0, int k0, int kvalid) {
-    constexpr int KS = WCfg<WT>::KS;
-    constexpr int GROUPS = NSTEP * KS / 8;          // 8-float groups per row
-    constexpr int TOTAL = MT * 16 * GROUPS;
-    for (int idx = threadIdx.x; idx < TOTAL; idx += 256) {
-        const int rowl = idx / GROUPS, j = idx - rowl * GROUPS;   // row in item, 8-float group
-        const int row = m0 + rowl;
-        float x[8];
-        if (row < p.M && 8 * j < kvalid) {
-            const float *src = p.A + (size_t)row * p.lda + k0 + 8 * j;
-            float4 a = ld_f4(src), b = ld_f4(src + 4);
-            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-        } else {
+__device__ __forceinline__ void load_a(AStage<WT, MT, NSTEP> &st, const GemmArgs &p, int m0, int k0, int kvalid) {
+    using S = AStage<WT, MT, NSTEP>;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = 0.f;
-        }
+    for (int it = 0; it < S::IT; ++it) {
+        const int idx = min((int)threadIdx.x + 256 * it, S::TOTAL - 1);
+        const int rowl = idx / S::GROUPS, j = idx - rowl * S::GROUPS;
+        const int row = min(m0 + rowl, p.M - 1), kk = min(8 * j, kvalid - 8);
+        const float *src = p.A + (size_t)row * p.lda + k0 + kk;
+        st.v[it][0] = ld_f4(src);
+        st.v[it][1] = ld_f4(src + 4);
+    }
+}
+
+template <int WT, int MT, int NSTEP>
+__device__ __forceinline__ void put_a(u32x4 *lds, const AStage<WT, MT, NSTEP> &st, const GemmArgs &p, int m0, int kvalid) {
+    using S = AStage<WT, MT, NSTEP>;
+#pragma unroll
+    for (int it = 0; it < S::IT; ++it) {
+        const int idx = (int)threadIdx.x + 256 * it;
+        if (idx >= S::TOTAL) break;
+        const int rowl = idx / S::GROUPS, j = idx - rowl * S::GROUPS;   // row in item, 8-float group
+        const bool ok = m0 + rowl < p.M && 8 * j < kvalid;
+        const float4 a = st.v[it][0], b = st.v[it][1];
+        float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = ok ? x[i] : 0.f;
         const int mt = rowl >> 4, r16 = rowl & 15;
         if constexpr (WT == WT_F32) {
             // step s covers 16 K: lane group g holds K 4g..4g+3 -> two fragments per 8 floats
@@ -126,8 +147,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
         wbase[0] = (const char *)p.seg[0].w; wscale[0] = p.seg[0].scale;
         wbase[1] = (const char *)p.seg[1].w; wscale[1] = p.seg[1].scale;
     } else {
-        int s = 0;
-        while (s + 1 < p.nseg && ncol >= p.seg[s].n) { ncol -= p.seg[s].n; ++s; }
+        // walked with the group's first column, which is uniform over the
+        // workgroup, so the segment table is read with scalar loads
+        int gcol = group * 64, s = 0;
+        while (s + 1 < p.nseg && gcol >= p.seg[s].n) { gcol -= p.seg[s].n; ++s; }
+        ncol = gcol + wave * 16;
         wbase[0] = (const char *)p.seg[s].w; wscale[0] = p.seg[s].scale;
     }
     const size_t K = p.K;
@@ -144,18 +168,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     for (int k0 = kbeg; k0 < kend; k0 += KCH) {
         const int kvalid = min(KCH, kend - k0);          // a multiple of KS
         const int nst = kvalid / KS;
-        // 1. all weight loads of this chunk
+        // 1. the chunk's activation loads, then all of its weight loads
+        AStage<WT, MT, NSTEP> ast;
+        load_a<WT, MT, NSTEP>(ast, p, m0, k0, kvalid);
+        asm volatile("" ::: "memory");                   // keep the activation loads ahead of the weights'
         u32x4 wv[NSTEP][NACC];
 #pragma unroll
         for (int a = 0; a < NACC; ++a) {
             const char *wr = wbase[a] + ((size_t)(ncol + r16) * K + k0 + lane_koff) * ES;
+            // unconditional (steps past the chunk reload its last one), so the
+            // compiler counts them and waits for the activations alone first
 #pragma unroll
-            for (int s = 0; s < NSTEP; ++s)
-                if (s < nst) wv[s][a] = ld_stream16(wr + (size_t)s * KS * ES);
+            for (int s = 0; s < NSTEP; ++s) wv[s][a] = ld_stream16(wr + (size_t)min(s, nst - 1) * KS * ES);
         }
-        // 2. activations -> LDS fragments
+        // 2. activations -> LDS fragments (the weight loads stay in flight)
         if (k0 != kbeg) __syncthreads();
-        stage_a<WT, MT, NSTEP>(lds, p, m0, k0, kvalid);
+        put_a<WT, MT, NSTEP>(lds, ast, p, m0, kvalid);
         __syncthreads();
         // 3. MFMAs
 #pragma unroll
