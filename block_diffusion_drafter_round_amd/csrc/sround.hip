@@ -21,8 +21,9 @@
 // workgroup has signalled the previous one:
 //   Q  q|k|v projection: columns split over workgroups, K split over waves
 //   A  attention: (kv head, key split) items; q/k head RMSNorm + NeoX rope
-//      in registers; online softmax over the ring's K/V blocks and the
-//      block's own K/V; partial (m, l, O) per split
+//      in registers from gains and cos/sin staged in LDS; online softmax over
+//      the ring's K/V blocks and (last split) the block's own K/V, staged in
+//      LDS in the same round trip as q; partial (m, l, O) per split
 //   M  merge of the splits -> O, written as o_proj input fragments
 //   O  o_proj + residual -> post-attention-norm input fragments
 //   G  gate|up + SwiGLU -> down input fragments
@@ -43,8 +44,7 @@
 // bumps phase counter blockIdx % 64 (four workgroups share one, so the
 // same-line atomics at a phase end stay short).  Wave 0 polls the 64
 // counters, one per lane, with device-coherent loads and publishes the phase
-// in LDS.  Each
-// (layer, phase) output has its own workspace buffer, written with
+// in LDS.  Each (layer, phase) output has its own workspace buffer, written with
 // device-coherent (sc1) stores and first read after the counter says it is
 // complete, so plain loads can use the L2 of each XCD.  Counters are never
 // reset: the workspace's epoch word counts the phases of earlier launches.
