@@ -826,6 +826,8 @@ __device__ __forceinline__ void d2_finish(float (&y)[4], int r, int c, const flo
 template <int WT, int D, bool C>
 __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigned p, int nt) {
     constexpr bool HL = C && TR<WT>::AB == 2;      // two-plane activations with the DFlash2 wrap
+    // fp8 weights always carry row scales (staged in S.aux); the others never
+    constexpr bool FP8 = WT == WT_FP8;
     const int lane = lane_id(), r = lane & 15, g = lane >> 4;
     char *lb = layer_buf(l), *ln = layer_buf(l + 1);
     constexpr bool d2 = C;
@@ -845,7 +847,7 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
             if (cl >= tl.n) continue;
             float y[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = sum[i] * (d2 ? 1.f : rs) * (tl.sc ? S.aux[16 * t + cl + i] : 1.f);
+            for (int i = 0; i < 4; ++i) y[i] = sum[i] * (d2 ? 1.f : rs) * (FP8 ? S.aux[16 * t + cl + i] : 1.f);
             const int col = tl.col + cl;
             if (tl.seg < 2) {
                 const int hh = col / D, dd = col - hh * D;
@@ -884,7 +886,7 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
             const int cl = 4 * g;
             float y[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = sum[i] * (tl.sc && cl < tl.n ? S.aux[16 * t + cl + i] : 1.f);
+            for (int i = 0; i < 4; ++i) y[i] = sum[i] * (FP8 && cl < tl.n ? S.aux[16 * t + cl + i] : 1.f);
             if constexpr (C) d2_finish(y, r, tl.col + cl, base, Dc);
             if (cl < tl.n) {
                 const int xc = tl.col - c0 + cl;
@@ -917,8 +919,8 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
             float z[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float gv = sg[i] * (d2 ? 1.f : rs) * (tg.sc ? S.aux[16 * t + cl + i] : 1.f);
-                const float uv = su[i] * (d2 ? 1.f : rs) * (tu.sc ? S.aux[16 * (t + ntg) + cl + i] : 1.f);
+                const float gv = sg[i] * (d2 ? 1.f : rs) * (FP8 ? S.aux[16 * t + cl + i] : 1.f);
+                const float uv = su[i] * (d2 ? 1.f : rs) * (FP8 ? S.aux[16 * (t + ntg) + cl + i] : 1.f);
                 z[i] = r < b ? gv / (1.f + __expf(-gv)) * uv : 0.f;
             }
             put4x<WT, HL>(zf, (size_t)16 * SS.I * 2, r, tg.col + cl, z[0], z[1], z[2], z[3]);
@@ -933,7 +935,7 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     st4(Dc, ((size_t)r * 4 * SS.d2 + tl.col + cl + i) * 4,
-                        __float_as_uint(sum[i] * rs * (tl.sc ? S.aux[cl + i] : 1.f)));
+                        __float_as_uint(sum[i] * rs * (FP8 ? S.aux[cl + i] : 1.f)));
             }
         }
     }
