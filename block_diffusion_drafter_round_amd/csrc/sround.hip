@@ -721,8 +721,14 @@ __device__ __forceinline__ void emit_input(SrLds &S, const float *gain, char *fr
         }
     }
     if (lane < 16) {
+        // every LDS read of the row issued before the first add (ch is a multiple of 4)
         float s = 0.f;
-        for (int c = 0; c < ch; ++c) s += S.xown[lane][c] * S.xown[lane][c];
+#pragma unroll
+        for (int c = 0; c < SR_MAXCH; c += 4) {
+            if (c >= ch) break;
+            const float4 x = *reinterpret_cast<const float4 *>(&S.xown[lane][c]);
+            s += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+        }
         st4(ssq, ((size_t)lane * gridDim.x + blockIdx.x) * 4, __float_as_uint(s));
     }
 }
@@ -840,7 +846,9 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
         char *qkv = lb + SS.o_qkv;
         const size_t koff = (size_t)16 * SS.qd * AB, voff = (size_t)16 * (SS.qd + SS.kvd) * AB;
         char *vcache = SS.vc + (size_t)l * SS.kv_lstride;
-        for (int t = 0; t < nt; ++t) {
+#pragma unroll
+        for (int t = 0; t < SR_MAXT; ++t) {
+            if (t >= nt) break;
             const GT tl = gemm_tile<WT>(K_Q, l, t);
             const f32x4 sum = tile_sum<WT>(S, t);
             const int cl = 4 * g;
@@ -911,7 +919,9 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
     } else if (kind == K_G) {
         const int ntg = nt / 2;
         char *zf = lb + SS.o_zf;
-        for (int t = 0; t < ntg; ++t) {
+#pragma unroll
+        for (int t = 0; t < SR_MAXT / 2; ++t) {
+            if (t >= ntg) break;
             const GT tg = gemm_tile<WT>(K_G, l, t), tu = gemm_tile<WT>(K_G, l, t + ntg);
             const f32x4 sg = tile_sum<WT>(S, t), su = tile_sum<WT>(S, t + ntg);
             const int cl = 4 * g;
