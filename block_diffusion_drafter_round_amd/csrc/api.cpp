@@ -25,6 +25,9 @@ struct dflash_model {
     std::vector<dflash_layer_weights> layers;
     double inv_freq[dfl::MAX_HALF_DIM];
     double mscale;
+    char *pk;            // packed GEMM weight stream (dflash_pack_weights), borrowed
+    int pk_nwg;          // round-kernel workgroups the stream was packed for
+    long long pk_layer;  // bytes of one layer's stream
 };
 
 namespace {
@@ -301,20 +304,60 @@ int device_cus() {
 
 dfl::SrMat smat(const dflash_matrix &m) { return dfl::SrMat{m.data, m.scale}; }
 
+// round-kernel workgroups on the current device, or <= 0
+int round_nwg(const dflash_cfg &c) {
+    return dfl::sround_nwg(c.hidden, c.intermediate, c.n_q_heads * c.head_dim, c.n_kv_heads * c.head_dim, c.weight_dtype,
+                           c.d2_groups, std::min(device_cus(), WS_MAX_NWG));
+}
+
+long long pack_layer_bytes(const dflash_cfg &c, int nwg) {
+    return dfl::sround_pack_layer_bytes(c.hidden, c.intermediate, c.n_q_heads * c.head_dim, c.n_kv_heads * c.head_dim,
+                                        c.weight_dtype, c.d2_groups, nwg);
+}
+
+// the round kernel's dimensions and the pointers of layers [l0, l0 + nl)
+void fill_round_args(const dflash_model *m, int nwg, int l0, int nl, dfl::SrArgs &ra) {
+    const dflash_cfg &c = m->cfg;
+    dfl::SrScalars &a = ra.s;
+    const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+    a.H = c.hidden; a.I = c.intermediate; a.nq = c.n_q_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim;
+    a.qd = qd; a.kvd = kvd; a.G = c.n_q_heads / c.n_kv_heads; a.d2 = c.d2_groups;
+    a.nwg = nwg; a.cq = (qd + 2 * kvd) / nwg; a.ch = c.hidden / nwg; a.ci = c.intermediate / nwg;
+    a.nl = nl;
+    a.first = l0 == 0;
+    a.last = l0 + nl == c.n_layers;
+    for (int i = 0; i < nl; ++i) {
+        const dflash_layer_weights &W = m->layers[l0 + i];
+        dfl::SrLayer &R = ra.L[i];
+        R.q = smat(W.wq); R.k = smat(W.wk); R.v = smat(W.wv); R.o = smat(W.wo);
+        R.g = smat(W.wg); R.u = smat(W.wu); R.d = smat(W.wd);
+        R.g_in = W.g_in; R.g_post = W.g_post; R.g_q = W.g_q; R.g_k = W.g_k;
+        if (c.d2_groups > 0) {
+            R.aw = smat(W.attn_w_dyn); R.mw = smat(W.mlp_w_dyn);
+            R.abase = W.attn_base; R.mbase = W.mlp_base;
+        }
+        R.pk = m->pk ? m->pk + (long long)(l0 + i) * m->pk_layer : nullptr;
+    }
+}
+
+// the packed stream must exist and match the current device's launch shape
+int check_packed(const dflash_model *m) {
+    if (!m->pk) return fail(DFLASH_E_INVAL, "weights not packed: call dflash_pack_weights first");
+    const int nwg = round_nwg(m->cfg);
+    if (nwg != m->pk_nwg)
+        return fail(DFLASH_E_INVAL, "weights packed for %d workgroups, this device runs %d: pack again", m->pk_nwg, nwg);
+    return DFLASH_OK;
+}
+
 // forward_round: the streamed round kernel, one launch per SR_MAXL layers
 hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *noise, const int32_t *pos, int b, float *out,
                      void *ws, const WsLayout &L, hipStream_t s) {
     const dflash_cfg &c = m->cfg;
-    const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
-    const int nwg = dfl::sround_nwg(c.hidden, c.intermediate, qd, kvd, c.weight_dtype, c.d2_groups,
-                                    std::min(device_cus(), WS_MAX_NWG));
-    if (nwg <= 0) return hipErrorInvalidDevice;
+    const int nwg = round_nwg(c);
+    if (nwg <= 0 || nwg != m->pk_nwg) return hipErrorInvalidDevice;
     dfl::SrArgs ra{};
     dfl::SrScalars &a = ra.s;
-    a.H = c.hidden; a.I = c.intermediate; a.nq = c.n_q_heads; a.nkv = c.n_kv_heads; a.d = c.head_dim;
-    a.qd = qd; a.kvd = kvd; a.G = c.n_q_heads / c.n_kv_heads;
-    a.b = b; a.len = kv->len; a.cap = kv->capacity; a.d2 = c.d2_groups;
-    a.nwg = nwg; a.cq = (qd + 2 * kvd) / nwg; a.ch = c.hidden / nwg; a.ci = c.intermediate / nwg;
+    a.b = b; a.len = kv->len; a.cap = kv->capacity;
     // attention key splits: at most one item per workgroup, keys per split a multiple of 32
     int ns = std::max(1, std::min({dfl::SR_MAX_SPLITS, nwg / c.n_kv_heads, (kv->len + 31) / 32}));
     int kps = kv->len > 0 ? (kv->len + ns - 1) / ns : 32;
@@ -337,22 +380,9 @@ hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *no
     int l0 = 0;
     do {
         const int nl = std::min(dfl::SR_MAXL, c.n_layers - l0);
-        a.nl = nl;
-        a.first = l0 == 0;
-        a.last = l0 + nl == c.n_layers;
+        fill_round_args(m, nwg, l0, nl, ra);
         a.kc = static_cast<char *>(layer_ptr(kv->k, c, kv->capacity, l0));
         a.vc = static_cast<char *>(layer_ptr(kv->v, c, kv->capacity, l0));
-        for (int i = 0; i < nl; ++i) {
-            const dflash_layer_weights &W = m->layers[l0 + i];
-            dfl::SrLayer &R = ra.L[i];
-            R.q = smat(W.wq); R.k = smat(W.wk); R.v = smat(W.wv); R.o = smat(W.wo);
-            R.g = smat(W.wg); R.u = smat(W.wu); R.d = smat(W.wd);
-            R.g_in = W.g_in; R.g_post = W.g_post; R.g_q = W.g_q; R.g_k = W.g_k;
-            if (c.d2_groups > 0) {
-                R.aw = smat(W.attn_w_dyn); R.mw = smat(W.mlp_w_dyn);
-                R.abase = W.attn_base; R.mbase = W.mlp_base;
-            }
-        }
         hipError_t e;
         {
             ProfScope p(DFLASH_K_ROUND, s);
@@ -406,6 +436,35 @@ int dflash_load_weights(const dflash_cfg *cfg, const dflash_weights *w, dflash_m
 }
 
 void dflash_free(dflash_model *m) { delete m; }
+
+size_t dflash_packed_bytes(const dflash_model *m) {
+    g_err.clear();
+    if (!m) { fail(DFLASH_E_INVAL, "model is null"); return 0; }
+    const int nwg = round_nwg(m->cfg);
+    if (nwg <= 0) { fail(DFLASH_E_HIP, "no usable device for the round kernel"); return 0; }
+    return (size_t)pack_layer_bytes(m->cfg, nwg) * m->cfg.n_layers;
+}
+
+int dflash_pack_weights(dflash_model *m, void *dst, size_t bytes, void *stream) {
+    g_err.clear();
+    if (!m) return fail(DFLASH_E_INVAL, "model is null");
+    if (!aligned(dst, 256)) return fail(DFLASH_E_INVAL, "dst null or not 256-byte aligned");
+    const int nwg = round_nwg(m->cfg);
+    if (nwg <= 0) return fail(DFLASH_E_HIP, "no usable device for the round kernel");
+    const long long per = pack_layer_bytes(m->cfg, nwg);
+    if (bytes < (size_t)per * m->cfg.n_layers)
+        return fail(DFLASH_E_INVAL, "dst holds %zu bytes, the packed weights need %lld", bytes, per * m->cfg.n_layers);
+    m->pk = static_cast<char *>(dst);
+    m->pk_nwg = nwg;
+    m->pk_layer = per;
+    for (int l0 = 0; l0 < m->cfg.n_layers; l0 += dfl::SR_MAXL) {
+        dfl::SrArgs ra{};
+        fill_round_args(m, nwg, l0, std::min(dfl::SR_MAXL, m->cfg.n_layers - l0), ra);
+        const hipError_t e = dfl::sround_pack_launch(ra, m->cfg.weight_dtype, nwg, (hipStream_t)stream);
+        if (e != hipSuccess) { m->pk = nullptr; return hip_fail(e, "pack_weights"); }
+    }
+    return DFLASH_OK;
+}
 
 size_t dflash_workspace_bytes(const dflash_model *m, int32_t max_rows) {
     if (!m || max_rows < 0) return 0;
@@ -463,7 +522,7 @@ int dflash_forward_round(const dflash_model *m, dflash_kv *kv, const float *nois
         return fail(DFLASH_E_CAPACITY, "len %d + b %d exceeds capacity %d", kv->len, b, kv->capacity);
     if (!aligned(noise_emb, 16) || !aligned(out, 16) || !aligned(pos_block, 4))
         return fail(DFLASH_E_INVAL, "noise_emb / out / pos_block null or misaligned");
-    if ((rc = check_ws(m, ws, ws_bytes, 0))) return rc;
+    if ((rc = check_ws(m, ws, ws_bytes, 0)) || (rc = check_packed(m))) return rc;
     hipError_t e = run_round(m, kv, noise_emb, pos_block, b, out, ws, ws_layout(m->cfg, 0), (hipStream_t)stream);
     return e == hipSuccess ? DFLASH_OK : hip_fail(e, "forward_round");
 }
@@ -480,7 +539,7 @@ int dflash_forward_full(const dflash_model *m, const float *taps, const float *n
         return fail(DFLASH_E_CAPACITY, "n %d + b %d exceeds scratch capacity %d", n, b, scratch->capacity);
     if ((n > 0 && !aligned(taps, 16)) || !aligned(noise_emb, 16) || !aligned(out, 16) || !aligned(pos, 4))
         return fail(DFLASH_E_INVAL, "taps / noise_emb / out / pos null or misaligned");
-    if ((rc = check_ws(m, ws, ws_bytes, n))) return rc;
+    if ((rc = check_ws(m, ws, ws_bytes, n)) || (rc = check_packed(m))) return rc;
     const WsLayout L = ws_layout(m->cfg, n);
     hipStream_t s = (hipStream_t)stream;
     float *feats = at<float>(ws, L.feats);

@@ -36,6 +36,7 @@ struct SrLayer {
     SrMat aw, mw;                          // DFlash2 dynamic-coefficient projections [4G][H]
     const float *g_in, *g_post, *g_q, *g_k;
     const float *abase, *mbase;            // DFlash2 static taps [2][H][2] (attention, MLP)
+    char *pk;                              // the layer's packed GEMM weight stream (sround_pack_layer_bytes)
 };
 
 struct SrScalars {
@@ -77,5 +78,10 @@ SrLayout sround_layout(int H, int I, int qd, int kvd, int nkv, int G, int d, int
 int sround_nwg(int H, int I, int qd, int kvd, int wt, int d2, int cus);
 
 hipError_t sround_launch(const SrArgs &a, int wt, int nwg, hipStream_t s);
+
+// Packed weight stream: bytes per layer for a launch of nwg workgroups, and
+// the kernel that writes the stream of every layer of `a` (L[i].pk).
+long long sround_pack_layer_bytes(int H, int I, int qd, int kvd, int wt, int d2, int nwg);
+hipError_t sround_pack_launch(const SrArgs &a, int wt, int nwg, hipStream_t s);
 
 }  // namespace dfl

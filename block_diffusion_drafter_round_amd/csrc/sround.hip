@@ -478,15 +478,59 @@ __device__ __forceinline__ Grp grp_layout(int kind, int l, int nt) {
     return G;
 }
 
+// Packed weight stream.  The GEMM weights do not depend on the round, so
+// they are rearranged once (sround_pack_kernel) into the exact order the
+// loader wave moves them: per layer and GEMM phase, per workgroup, a run of
+// ring slots, each slot SR_CW parts of 64 lanes x 16 bytes, contiguous.  The
+// loader then streams 8 KiB runs; read in place, a part is 16 weight rows of
+// 64 bytes each, which one wave moves at about half the contiguous rate.
+// Slots per workgroup of one phase: groups of 4 k steps times one slot per 4
+// of its columns (a 16-wide tile fills 4 slots per group, an 8-wide 2, a
+// 4-wide 1); cols is the most columns any workgroup has in the phase.
+__host__ __device__ inline long long pk_wg_slots(int wt, int K, int cols) {
+    const int kw = wt == WT_BF16 ? 32 : wt == WT_FP8 ? 64 : 16;
+    const int nf = wt == WT_FP8 ? 4 : 8;
+    const int nkw = ((K / kw + SR_CW - 1) / SR_CW + nf - 1) / nf * nf;
+    return (long long)(nkw / 4) * (cols / 4);
+}
+__host__ __device__ inline long long pk_wg_bytes(int wt, int kind, int H, int I, int qd, int cq, int ch, int ci) {
+    const int K = kind == K_O ? qd : kind == K_D ? I : H;
+    const int cols = kind == K_Q ? cq : (kind == K_O || kind == K_D) ? ch : kind == K_G ? 2 * ci : 16;
+    return pk_wg_slots(wt, K, cols) * SR_SLOT;
+}
+// byte offset of a phase's runs in the layer's stream (phases in the order
+// DA, Q, O, DM, G, D; DA and DM only with the DFlash2 wrap); any other kind
+// gives the layer's total
+__host__ __device__ inline long long pk_layer_off(int wt, int kind, int H, int I, int qd, int cq, int ch, int ci, int nwg, int d2) {
+    long long off = 0;
+    for (int i = 0; i < 6; ++i) {
+        const int k = i == 0 ? K_DA : i == 1 ? K_Q : i == 2 ? K_O : i == 3 ? K_DM : i == 4 ? K_G : K_D;
+        if (k == kind) return off;
+        if (d2 == 0 && (k == K_DA || k == K_DM)) continue;
+        off += (long long)nwg * pk_wg_bytes(wt, k, H, I, qd, cq, ch, ci);
+    }
+    return off;
+}
+// this workgroup's slot run of one GEMM phase of local layer l
 template <int WT>
-__device__ __forceinline__ bool load_gemm(SrLds &S, Loader &ld, int kind, int l) {
+__device__ __forceinline__ char *pk_run(int kind, int l) {
+    const long long off = pk_layer_off(WT, kind, SS.H, SS.I, SS.qd, SS.cq, SS.ch, SS.ci, SS.nwg, SS.d2) +
+                          (long long)blockIdx.x * pk_wg_bytes(WT, kind, SS.H, SS.I, SS.qd, SS.cq, SS.ch, SS.ci);
+    return ka()->L[l].pk + off;
+}
+
+// Writes this workgroup's slot run of one GEMM phase: slot by slot in the
+// loader's order, part v of a slot holding what compute wave v consumes.
+// Lane L of a part of tile t (width n) takes row L % n, lane group
+// (L / n) % 4, of step L / (4 n) of the part's steps; steps past the end of
+// K (dead steps) repeat step 0 and are never used.
+template <int WT>
+__device__ __forceinline__ void pack_gemm(int kind, int l) {
     constexpr int KW = TR<WT>::KW, ES = TR<WT>::ES, P = TR<WT>::P;
     const int lane = lane_id();
     const int nt = gemm_nt(kind);
-    if (nt == 0) return true;
+    if (nt == 0) return;
     const int K = gemm_K(kind), nst = K / KW, nkw = gemm_npass<WT>(nst) * PassCfg<WT>::NF;
-    // lane L of a part of tile t (width n) loads row L % n, lane group
-    // (L / n) % 4, of step L / (4 n) of the part's steps
     const char *row[SR_MAXT];
     int sofs[SR_MAXT], spi[SR_MAXT];
 #pragma unroll
@@ -500,24 +544,49 @@ __device__ __forceinline__ bool load_gemm(SrLds &S, Loader &ld, int kind, int l)
             spi[t] = 16 / n;
         }
     }
+    char *run = pk_run<WT>(kind, l);
+    size_t si = 0;
     for (int j = 0; j < nkw; j += 4) {
-#pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) {
 #pragma unroll
             for (int t = 0; t < SR_MAXT; ++t) {
                 if (t < nt && (j4 & (spi[t] - 1)) == 0) {
-                    if (!loader_wait_free(S, ld)) return false;
-                    u32x4 *dst = &S.ring[ld.seq % SR_NSLOT][0][0];
+                    u32x4 val[SR_CW];
 #pragma unroll
                     for (int v = 0; v < SR_CW; ++v) {
                         int ks = v * nkw + j + j4 + sofs[t];
                         ks = ks < nst ? ks : 0;
-                        dma16(row[t] + (size_t)ks * KW * ES, dst + v * 64);
+                        val[v] = *reinterpret_cast<const u32x4 *>(row[t] + (size_t)ks * KW * ES);
                     }
-                    loader_commit(S, ld);
+#pragma unroll
+                    for (int v = 0; v < SR_CW; ++v)
+                        *reinterpret_cast<u32x4 *>(run + (si * SR_CW + v) * SR_PART + 16 * lane) = val[v];
+                    ++si;
                 }
             }
         }
+    }
+}
+
+// Streams this workgroup's slot run of one GEMM phase into the ring: slot by
+// slot, each lane moving 16 contiguous bytes per part.
+template <int WT>
+__device__ __forceinline__ bool load_gemm(SrLds &S, Loader &ld, int kind, int l) {
+    const int nt = gemm_nt(kind);
+    if (nt == 0) return true;
+    const int nst = gemm_K(kind) / TR<WT>::KW, nkw = gemm_npass<WT>(nst) * PassCfg<WT>::NF;
+    int cols = 0;
+#pragma unroll
+    for (int t = 0; t < SR_MAXT; ++t)
+        if (t < nt) cols += gemm_tile<WT>(kind, l, t).n;
+    const int nslot = __builtin_amdgcn_readfirstlane(nkw / 4 * (cols / 4));
+    const char *src = pk_run<WT>(kind, l) + 16 * lane_id();
+    for (int si = 0; si < nslot; ++si) {
+        if (!loader_wait_free(S, ld)) return false;
+        u32x4 *dst = &S.ring[ld.seq % SR_NSLOT][0][0];
+#pragma unroll
+        for (int v = 0; v < SR_CW; ++v) dma16(src + ((size_t)si * SR_CW + v) * SR_PART, dst + v * 64);
+        loader_commit(S, ld);
     }
     return true;
 }
@@ -1671,6 +1740,17 @@ __global__ __launch_bounds__(SR_THREADS, 1) void sround_kernel(SrArgs) {
     if (!compute_main<WT, D, C>(S)) stc_u(SS.ctr + SR_CTR_ERR, 1u);
 }
 
+// one wave per workgroup writes that workgroup's slot runs of every layer
+template <int WT>
+__global__ __launch_bounds__(64) void sround_pack_kernel(SrArgs) {
+    const int nl = SS.nl, np = npl();
+    for (int l = 0; l < nl; ++l)
+        for (int i = 0; i < np; ++i) {
+            const int k = kind_at(i);
+            if (k != K_A && k != K_M) pack_gemm<WT>(k, l);
+        }
+}
+
 template <int WT, bool C>
 hipError_t launch_d(const SrArgs &a, int nwg, hipStream_t s) {
     if (a.s.d == 64) hipLaunchKernelGGL((sround_kernel<WT, 64, C>), dim3(nwg), dim3(SR_THREADS), 0, s, a);
@@ -1750,6 +1830,20 @@ int sround_nwg(int H, int I, int qd, int kvd, int wt, int d2, int cus) {
         return n;
     }
     return 0;
+}
+
+long long sround_pack_layer_bytes(int H, int I, int qd, int kvd, int wt, int d2, int nwg) {
+    if (nwg <= 0) return 0;
+    return pk_layer_off(wt, -1, H, I, qd, (qd + 2 * kvd) / nwg, H / nwg, I / nwg, nwg, d2);
+}
+
+hipError_t sround_pack_launch(const SrArgs &a, int wt, int nwg, hipStream_t s) {
+    switch (wt) {
+        case WT_F32: hipLaunchKernelGGL(sround_pack_kernel<WT_F32>, dim3(nwg), dim3(64), 0, s, a); break;
+        case WT_BF16: hipLaunchKernelGGL(sround_pack_kernel<WT_BF16>, dim3(nwg), dim3(64), 0, s, a); break;
+        default: hipLaunchKernelGGL(sround_pack_kernel<WT_FP8>, dim3(nwg), dim3(64), 0, s, a); break;
+    }
+    return hipGetLastError();
 }
 
 hipError_t sround_launch(const SrArgs &a, int wt, int nwg, hipStream_t s) {

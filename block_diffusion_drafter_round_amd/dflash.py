@@ -61,7 +61,7 @@ _lib = None
 EXPORTS = ("dflash_load_weights", "dflash_free", "dflash_workspace_bytes", "dflash_ctx_features",
            "dflash_ingest_ctx", "dflash_forward_round", "dflash_forward_full", "dflash_last_error",
            "dflash_rope_table", "dflash_prof_start", "dflash_prof_stop", "dflash_workspace_status",
-           "dflash_prof_trace", "dflash_prof_trace_read")
+           "dflash_prof_trace", "dflash_prof_trace_read", "dflash_packed_bytes", "dflash_pack_weights")
 
 # kernel classes of the measurement hook (include/dflash_prof.h)
 K_GEMM_FC, K_GEMM_KV, K_GEMM_QKV, K_GEMM_O, K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN, K_ROPE, K_NORM, K_ROUND = range(1, 11)
@@ -81,6 +81,9 @@ def lib():
     L.dflash_free.restype = None
     L.dflash_workspace_bytes.argtypes = [vp, i32]
     L.dflash_workspace_bytes.restype = sz
+    L.dflash_packed_bytes.argtypes = [vp]
+    L.dflash_packed_bytes.restype = sz
+    L.dflash_pack_weights.argtypes = [vp, vp, sz, vp]
     L.dflash_ctx_features.argtypes = [vp, vp, i32, vp, vp, sz, vp]
     L.dflash_ingest_ctx.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, i32, vp, sz, vp]
     L.dflash_forward_round.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, i32, vp, vp, sz, vp]
@@ -93,7 +96,7 @@ def lib():
     L.dflash_prof_trace.argtypes = [i32]
     L.dflash_prof_trace_read.argtypes = [vp, vp, sz, C.POINTER(C.c_uint64), i32, vp]
     for name in EXPORTS:
-        if name not in ("dflash_free", "dflash_workspace_bytes", "dflash_last_error"):
+        if name not in ("dflash_free", "dflash_workspace_bytes", "dflash_last_error", "dflash_packed_bytes"):
             getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -132,6 +135,17 @@ def dflash_load_weights(cfg: dflash_cfg, weights: dflash_weights) -> int:
 
 def dflash_free(model: int) -> None:
     lib().dflash_free(model)
+
+
+def dflash_packed_bytes(model: int) -> int:
+    n = int(lib().dflash_packed_bytes(model))
+    if n == 0 and lib().dflash_last_error():
+        raise DflashError(DFLASH_E_HIP, lib().dflash_last_error().decode())
+    return n
+
+
+def dflash_pack_weights(model: int, dst, nbytes: int, stream=None) -> None:
+    _check(lib().dflash_pack_weights(model, _ptr(dst), nbytes, _stream(stream)))
 
 
 def dflash_workspace_bytes(model: int, max_rows: int) -> int:
@@ -299,6 +313,9 @@ class Drafter:
         self.weights = DeviceWeights(stored, device)
         self.ccfg = make_cfg(self.cfg)
         self.model = dflash_load_weights(self.ccfg, self.weights.struct)
+        self.packed_bytes = dflash_packed_bytes(self.model)
+        self.packed = torch.empty(max(self.packed_bytes, 256), dtype=torch.uint8, device=self.device)
+        dflash_pack_weights(self.model, self.packed, self.packed_bytes)
         self.max_rows = 0
         self.ws = None
         self.ensure_rows(max_rows)

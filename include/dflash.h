@@ -156,6 +156,28 @@ int dflash_load_weights(const dflash_cfg *cfg, const dflash_weights *w, dflash_m
 /* Release a handle from dflash_load_weights (NULL is allowed). */
 void dflash_free(dflash_model *m);
 
+/* Bytes of device memory that dflash_pack_weights needs for this model on
+ * the current device (the layout depends on the device's CU count).
+ * Returns 0 for a model without layers, and 0 with dflash_last_error set if
+ * m is NULL or no device is usable.  Makes no allocation. */
+size_t dflash_packed_bytes(const dflash_model *m);
+
+/* Rearrange the layer GEMM weights (the [DflashDraft] layer fields wq, wk,
+ * wv, wo, wg, wu, wd and, with the DFlash2 wrap, the dynamic-coefficient
+ * projections) into `dst`, in the order in which forward_round streams them:
+ * per layer and projection, per workgroup of the round kernel, contiguous
+ * 8 KiB runs.  The values are copied unchanged (same dtype; fp8 row scales
+ * stay where dflash_load_weights found them).
+ *   dst  : device memory of >= dflash_packed_bytes(m) bytes, 256-byte
+ *          aligned, owned by the caller, kept alive and unchanged while the
+ *          model is used.  Borrowed like the weights themselves.
+ * forward_round and forward_full fail with DFLASH_E_INVAL until this has been
+ * called, or if the current device's CU count differs from the one packed
+ * for.  Asynchronous on `stream`; call again after changing the weights.
+ * Errors: DFLASH_E_INVAL (null/misaligned dst, too small), DFLASH_E_HIP (no
+ * usable device, launch error); nothing is enqueued on an argument error. */
+int dflash_pack_weights(dflash_model *m, void *dst, size_t bytes, void *stream);
+
 /* Bytes of device workspace (the per-step scratch of [atlas dflash_head]
  * "DflashScratch") needed by calls that process up to `max_rows` ctx rows at
  * once: ctx_features t, ingest_ctx t, or forward_full n.  The workspace must

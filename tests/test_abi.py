@@ -130,3 +130,25 @@ def test_fp8_needs_scales(D):
     with pytest.raises(D.DflashError) as ei:
         D.dflash_load_weights(D.make_cfg(cfg), fw.struct)
     assert ei.value.code == D.DFLASH_E_INVAL
+
+
+def test_round_needs_packed_weights(D):
+    """forward_round and pack_weights reject their arguments before any HIP call."""
+    cfg = synth.TINY_F32
+    fw = FakeWeights(D, cfg)
+    m = D.dflash_load_weights(D.make_cfg(cfg), fw.struct)
+    try:
+        with pytest.raises(D.DflashError) as ei:
+            D.dflash_pack_weights(m, None, 1 << 20, 0)
+        assert ei.value.code == D.DFLASH_E_INVAL
+        with pytest.raises(D.DflashError) as ei:
+            D.dflash_pack_weights(m, 0x10010, 1 << 20, 0)        # not 256-byte aligned
+        assert ei.value.code == D.DFLASH_E_INVAL
+        kv = D.dflash_kv(0x100000, 0x200000, 128, 0)
+        ws_bytes = D.dflash_workspace_bytes(m, 16)
+        rc = D.lib().dflash_forward_round(m, C.byref(kv), 0x300000, 0x400000, 16, 0x500000, 0x600000, ws_bytes, None)
+        assert rc == D.DFLASH_E_INVAL
+        assert "not packed" in D.dflash_last_error()
+        assert kv.len == 0
+    finally:
+        D.dflash_free(m)
