@@ -152,3 +152,20 @@ def test_round_needs_packed_weights(D):
         assert kv.len == 0
     finally:
         D.dflash_free(m)
+
+
+def test_packed_bytes_needs_a_device(D):
+    """The packed layout depends on the device's CU count: with no usable
+    device the size query reports an error instead of a size."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    cfg = synth.TINY_F32
+    fw = FakeWeights(D, cfg)
+    m = D.dflash_load_weights(D.make_cfg(cfg), fw.struct)
+    try:
+        with pytest.raises(D.DflashError) as ei:
+            D.dflash_packed_bytes(m)
+        assert ei.value.code == D.DFLASH_E_HIP
+    finally:
+        D.dflash_free(m)
