@@ -243,3 +243,33 @@ def test_errors_leave_state_unchanged():
     assert kv.len == 60
     out = dr.forward_round(kv, dev(synth.make_noise(cfg, rows=4)), dev(synth.positions(60, 4)))
     assert torch.isfinite(out).all()
+
+
+def test_round_reads_the_packed_copy():
+    """dflash_pack_weights copies the layer weights: a change to a layer
+    matrix reaches forward_round only after the weights are packed again.
+    Flipping the sign bits of layer 0's down projection is exact in bf16."""
+    import copy
+    cfg = SMALL_BF16
+    sw, m, dr, D = _setup(cfg, max_rows=cfg.ctx)
+    n, b = cfg.ctx, cfg.block
+    taps = synth.make_taps(cfg, n)
+    noise = synth.make_noise(cfg, rows=b)
+    pos = synth.positions(0, n + b)
+    run = lambda: host(dr.forward_full(dev(taps), dev(noise), dev(pos)))
+    out_a = run()
+    check("small_bf16 packed", out_a, O.forward_full(m, taps, noise, pos, n), tol_for(cfg))
+
+    ptr = dr.weights.layer_arr[0].wd.data
+    wd = next(t for t in dr.weights.tensors if t is not None and t.data_ptr() == ptr)
+    wd.bitwise_xor_(torch.tensor(-32768, dtype=torch.int16, device=wd.device))
+    out_b = run()
+    assert np.array_equal(out_a, out_b), "the round read the weights in place, not the packed copy"
+
+    D.dflash_pack_weights(dr.model, dr.packed, dr.packed_bytes)
+    out_c = run()
+    sw2 = copy.deepcopy(sw)
+    sw2.layers[0]["wd"].data = sw2.layers[0]["wd"].data ^ np.uint16(0x8000)
+    ref_c = O.forward_full(O.OracleModel(sw2), taps, noise, pos, n)
+    check("small_bf16 repacked, layer 0 wd negated", out_c, ref_c, tol_for(cfg))
+    assert not np.array_equal(out_a, out_c)
