@@ -42,13 +42,23 @@ int dflash_prof_start(int32_t kernel_class, int32_t max_launches);
 int dflash_prof_stop(double *total_ms, int32_t *launches);
 
 /* Phase trace of the persistent forward_round kernel.  While enabled, each
- * later launch makes workgroup 0 record the GPU wall clock (100 MHz
- * counter): once at kernel start, once after every grid barrier, once at the
- * end.  The stamps go to a region of the launch's workspace.  The trace
- * slots of one layer follow the phase order: qkv GEMM, qkv reduce,
- * attention, merge, o GEMM, o reduce, gate|up GEMM, SwiGLU, down GEMM,
- * down reduce.  dflash_prof_trace_read synchronises `stream` and copies the
- * first n stamps (n <= 1024) to host memory. */
+ * later launch records GPU wall-clock stamps (100 MHz counter) into a region
+ * of its workspace.  Phase p of a launch is 1 + layer * P + i, where i runs
+ * over the layer's phases (P = 6: q|k|v, attention, merge, o, gate|up,
+ * down; with the DFlash2 wrap P = 8, a coefficient phase before q|k|v and
+ * before gate|up).  Words 8p + k, workgroup 0:
+ *   k = 0  wave 0 sees the phase's inputs complete
+ *   k = 1  wave 0 done with its share
+ *   k = 2  the epilogue done and the phase signalled
+ *   k = 3  the loader issues the phase's first ring slot
+ *   k = 4  the loader has issued the phase's last ring slot
+ *   k = 5  the epilogue starts (GEMM phases)
+ * Words 512 + 8p + k hold wave 1's stamps in GEMM phases (k = 0 set up,
+ * 1 activations loaded, 4 first ring slot available, 2 k steps done,
+ * 3 partial sums stored),
+ * and word 1024 + 256 (p - 7) + w the time workgroup w signalled phase p,
+ * for p in [7, 19).  dflash_prof_trace_read synchronises `stream` and copies
+ * the first n stamps (n <= 4096) to host memory. */
 int dflash_prof_trace(int32_t enable);
 int dflash_prof_trace_read(const struct dflash_model *m, void *ws, size_t ws_bytes, uint64_t *out, int32_t n,
                            void *stream);
