@@ -28,8 +28,12 @@
  *    alive and unchanged until the stream has passed the call.
  *  - Return value: DFLASH_OK (0) or an error code.  dflash_last_error()
  *    returns a message for the calling thread's last error.  All argument
- *    checks run before any HIP call.  On an error nothing has been enqueued,
- *    and kv->len is unchanged.  A HIP launch failure is DFLASH_E_HIP.
+ *    checks run before anything is enqueued (device-attribute queries aside).
+ *    On an error nothing has been enqueued, and kv->len is unchanged.  A HIP
+ *    launch failure is DFLASH_E_HIP.
+ *  - Call order: dflash_load_weights, then dflash_pack_weights once per
+ *    model and device, then any number of ctx_features / ingest_ctx /
+ *    forward_round calls.
  *  - A model may serve several streams at once, each with its own workspace.
  *    One dflash_kv and one workspace must not be used by two calls in flight
  *    at the same time.
@@ -173,7 +177,8 @@ size_t dflash_packed_bytes(const dflash_model *m);
  *          model is used.  Borrowed like the weights themselves.
  * forward_round and forward_full fail with DFLASH_E_INVAL until this has been
  * called, or if the current device's CU count differs from the one packed
- * for.  Asynchronous on `stream`; call again after changing the weights.
+ * for.  Asynchronous on `stream`: calls on other streams must be ordered
+ * after it by the caller.  Call again after changing the weights.
  * Errors: DFLASH_E_INVAL (null/misaligned dst, too small), DFLASH_E_HIP (no
  * usable device, launch error); nothing is enqueued on an argument error. */
 int dflash_pack_weights(dflash_model *m, void *dst, size_t bytes, void *stream);
