@@ -493,6 +493,10 @@ __host__ __device__ inline long long pk_wg_slots(int wt, int K, int cols) {
     const int nkw = ((K / kw + SR_CW - 1) / SR_CW + nf - 1) / nf * nf;
     return (long long)(nkw / 4) * (cols / 4);
 }
+static_assert(TR<WT_BF16>::KW == 32 && TR<WT_FP8>::KW == 64 && TR<WT_F32>::KW == 16,
+              "pk_wg_slots repeats the k values per 16-byte weight load for host-side sizing");
+static_assert(PassCfg<WT_BF16>::NF == 8 && PassCfg<WT_FP8>::NF == 4 && PassCfg<WT_F32>::NF == 8,
+              "pk_wg_slots repeats the k steps per pass for host-side sizing");
 __host__ __device__ inline long long pk_wg_bytes(int wt, int kind, int H, int I, int qd, int cq, int ch, int ci) {
     const int K = kind == K_O ? qd : kind == K_D ? I : H;
     const int cols = kind == K_Q ? cq : (kind == K_O || kind == K_D) ? ch : kind == K_G ? 2 * ci : 16;
