@@ -273,3 +273,23 @@ def test_round_reads_the_packed_copy():
     ref_c = O.forward_full(O.OracleModel(sw2), taps, noise, pos, n)
     check("small_bf16 repacked, layer 0 wd negated", out_c, ref_c, tol_for(cfg))
     assert not np.array_equal(out_a, out_c)
+
+
+@pytest.mark.parametrize("cfg,b", [
+    (SMALL_BF16.replace(name="small_bf16_l10", n_layers=10, seed=50), 16),
+    (SMALL_BF16.replace(name="small_bf16_l10", n_layers=10, seed=50), 5),
+    (SMALL_FP8_D2.replace(name="small_fp8_d128_d2_l11", n_layers=11, seed=51), 7),
+    (synth.TINY_F32.replace(name="tiny_f32_l9", n_layers=9, seed=52), 16),
+], ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_forward_full_more_than_8_layers(cfg, b):
+    """A round over more than 8 layers runs as several launches, the residual
+    carried between them in the workspace and each launch reading its own
+    layers' part of the packed weight stream."""
+    sw, m, dr, D = _setup(cfg, max_rows=cfg.ctx)
+    n = cfg.ctx
+    taps = synth.make_taps(cfg, n)
+    noise = synth.make_noise(cfg, rows=b)
+    pos = synth.positions(0, n + b)
+    out = host(dr.forward_full(dev(taps), dev(noise), dev(pos)))
+    ref = O.forward_full(m, taps, noise, pos, n)
+    check(f"{cfg.name} forward_full n={n} b={b}", out, ref, tol_for(cfg))
