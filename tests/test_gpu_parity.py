@@ -293,3 +293,21 @@ def test_forward_full_more_than_8_layers(cfg, b):
     out = host(dr.forward_full(dev(taps), dev(noise), dev(pos)))
     ref = O.forward_full(m, taps, noise, pos, n)
     check(f"{cfg.name} forward_full n={n} b={b}", out, ref, tol_for(cfg))
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_FP8_D2], ids=lambda c: c.name)
+@pytest.mark.parametrize("b", [16, 3])
+def test_empty_context(cfg, b):
+    """No ctx rows: forward_round over an empty cache attends to the block's
+    own keys only, and forward_full with n = 0 gives the same rows."""
+    sw, m, dr, D = _setup(cfg, max_rows=16)
+    noise = synth.make_noise(cfg, rows=b)
+    pos = synth.positions(7, b)
+    kv = D.KVCache(cfg, 64)
+    out = host(dr.forward_round(kv, dev(noise), dev(pos)))
+    assert kv.len == 0
+    ref = O.forward_round(m, O.OracleKV(cfg), noise, pos)
+    check(f"{cfg.name} empty-cache round b={b}", out, ref, tol_for(cfg))
+    taps = synth.make_taps(cfg, 0)
+    full = host(dr.forward_full(dev(taps), dev(noise), dev(pos)))
+    assert np.array_equal(out, full), "forward_full(n = 0) != forward_round on an empty cache"
