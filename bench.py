@@ -108,6 +108,9 @@ def round_bytes(cfg, ctx: int, t: int = 16, b: int = 16) -> dict:
     scales = 0
     if cfg.weight_dtype == "fp8":
         scales = ((qd + 2 * kvd) + H + 3 * I + 2 * kvd) * 4 * L + H * 4
+    if cfg.d2_groups:      # DFlash2: dynamic-coefficient projections [4G][H] (+ fp8 scales) and static taps
+        G4 = 4 * cfg.d2_groups
+        scales += (2 * G4 * H * wb + (2 * G4 * 4 if cfg.weight_dtype == "fp8" else 0) + 2 * 2 * H * 2 * 4) * L
     tot = layer_w + fc_w + ingest_w + kv_read + kv_write + taps + scales
     return dict(layer_weights=layer_w, fc_weights=fc_w, ingest_weights=ingest_w, kv_read=kv_read,
                 kv_write=kv_write, taps=taps, scales=scales, total=tot)
@@ -174,6 +177,92 @@ def cpu_baseline(cfg, ctx: int, seconds: float) -> dict:
     return rec
 
 
+def full_bytes(cfg, n: int, b: int = 16) -> int:
+    """Algorithmic HBM bytes of one first-light forward over n ctx rows:
+    every weight once (W_k/W_v counted once though ingest and the round both
+    read them), the taps, and the n + b K/V rows written and read back."""
+    wb = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight_dtype]
+    kvb = 4 if cfg.kv_dtype == "f32" else 2
+    H, I, qd, kvd, L = cfg.hidden, cfg.intermediate, cfg.q_dim, cfg.kv_dim, cfg.n_layers
+    w = ((qd + 2 * kvd) * H + H * qd + 3 * I * H) * wb * L + H * cfg.n_taps * H * wb
+    return w + n * cfg.n_taps * H * 4 + 2 * (n + b) * kvd * 2 * kvb * L
+
+
+def other_config(name: str, args) -> int:
+    """Times one of the parity configurations with the same library calls
+    and prints one JSON line for it (these are not the headline metric).
+    c1 / c2: first-light forward_full latency.  c4 / c5: the cached round
+    (ctx_features 16 + ingest_ctx 16 + forward_round b = 16) over caches set
+    to their committed length directly (zero-filled rows move the same bytes
+    as a real prefill), c4 over 8 sequences back to back."""
+    import torch
+    import synth
+    from block_diffusion_drafter_round_amd import dflash as D
+    cfg = {"c1": synth.TINY_F32, "c2": synth.FULL5_BF16, "c4": synth.ROUND8_YARN, "c5": synth.ROUND8_FP8_D2}[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] loading {cfg.name}", file=sys.stderr, flush=True)
+    sw = synth.make_weights(cfg)
+    b = cfg.block
+    stream = torch.cuda.current_stream(dev)
+    if name in ("c1", "c2"):
+        n = cfg.ctx
+        dr = D.Drafter(sw, device=dev, max_rows=n)
+        scratch = D.KVCache(cfg, (n + b + 63) // 64 * 64, dev)
+        taps = torch.from_numpy(synth.make_taps(cfg, n)).to(dev)
+        noise = torch.from_numpy(synth.make_noise(cfg)).to(dev)
+        pos = torch.from_numpy(synth.positions(0, n + b)).to(dev)
+        step = lambda: dr.forward_full(taps, noise, pos, scratch)
+        units, unit, nbytes = 1, "forwards/s", full_bytes(cfg, n, b)
+        workload = f"{cfg.n_layers}-layer {cfg.weight_dtype} drafter first-light forward_full, n={n} ctx rows, block {b}"
+    else:
+        ctx, t = cfg.ctx, cfg.new_rows
+        base = ctx - t
+        dr = D.Drafter(sw, device=dev, max_rows=64)
+        nseq = cfg.n_seqs
+        kvs = [D.KVCache(cfg, (ctx + b + 63) // 64 * 64, dev) for _ in range(nseq)]
+        taps = torch.from_numpy(synth.make_taps(cfg, t, stream=1)).to(dev)
+        noise = torch.from_numpy(synth.make_noise(cfg)).to(dev)
+        pos_new = torch.from_numpy(synth.positions(base, t)).to(dev)
+        pos_blk = torch.from_numpy(synth.positions(ctx, b)).to(dev)
+        feats = torch.empty((t, cfg.hidden), dtype=torch.float32, device=dev)
+        out = torch.empty((b, cfg.hidden), dtype=torch.float32, device=dev)
+
+        def step():
+            for kv in kvs:
+                kv.c.len = base
+                D.dflash_ctx_features(dr.model, taps, t, feats, dr.ws, dr.ws_bytes, stream)
+                D.dflash_ingest_ctx(dr.model, kv.c, feats, pos_new, t, dr.ws, dr.ws_bytes, stream)
+                D.dflash_forward_round(dr.model, kv.c, noise, pos_blk, b, out, dr.ws, dr.ws_bytes, stream)
+        units, unit, nbytes = nseq, "sequence-rounds/s", round_bytes(cfg, ctx, t, b)["total"]
+        workload = (f"{cfg.n_layers}-layer {cfg.weight_dtype} drafter cached round at ctx {ctx}"
+                    f"{' (YaRN)' if cfg.rope_type == 'yarn' else ''}{' with the DFlash2 conv' if cfg.d2_groups else ''}"
+                    f", {nseq} sequence(s) back to back")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, z in evs:
+        a.record(stream)
+        step()
+        z.record(stream)
+    torch.cuda.synchronize()
+    dr.status()
+    per = np.sort(np.array([a.elapsed_time(z) for a, z in evs])) / 1e3      # s per step
+    med = float(np.median(per))
+    rec = {"metric": f"{cfg.name}: {unit}", "value": round(units / med, 2), "unit": unit, "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(med * 1e3, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.weight_dtype,
+           "data": "synthetic (seeded N(0,0.02) weights, N(0,1) taps/noise, random init)",
+           "config": {"workload": workload},
+           "step_ms_p10_p50_p90": [round(float(np.percentile(per, q)) * 1e3, 4) for q in (10, 50, 90)],
+           "algorithmic_bytes_per_unit": nbytes,
+           "hbm_gbs": round(nbytes * units / med / 1e9, 1),
+           "hbm_frac": round(nbytes * units / med / 1e9 / HBM_PEAK_GBS, 4)}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def copy_reference(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> dict:
     """Device-to-device copy of `nbytes`: the HBM rate a plain streaming
     kernel reaches on this GPU (it reads and writes nbytes per copy)."""
@@ -204,6 +293,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prof", action="store_true", help="skip the live per-kernel timing")
     ap.add_argument("--copy-calibration", action="store_true", help="only run the 256 MiB copy used to scale counters")
+    ap.add_argument("--config", choices=("c1", "c2", "c4", "c5"),
+                    help="time one of the other workloads instead (c1 tiny f32 forward_full, c2 5-layer forward_full "
+                         "n=1024, c4 YaRN ctx 32768 x 8 sequences, c5 fp8 + DFlash2 ctx 65536)")
     args = ap.parse_args(argv)
     if args.copy_calibration:
         return copy_calibration()
@@ -211,6 +303,8 @@ def main(argv=None) -> int:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the drafter path has no "
               f"cross-GPU work; sequences shard by data parallelism).", file=sys.stderr)
         return 2
+    if args.config:
+        return other_config(args.config, args)
 
     import torch
     from block_diffusion_drafter_round_amd import dflash as D
