@@ -359,6 +359,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} rounds", file=sys.stderr, flush=True)
     gpu_s, wall_s = timed(args.steps)
+    dr.status()     # raises if a round kernel's barrier wait expired (its output would be NaN)
     sec = max(gpu_s, wall_s)
     ms_per_step = sec * 1e3 / args.steps
     rounds_per_s = args.steps / sec

@@ -573,7 +573,9 @@ int dflash_workspace_status(const dflash_model *m, void *ws, size_t ws_bytes, vo
         e = hipMemset(ctr, 0, sizeof(unsigned) * dfl::SR_CTR_WORDS);
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) return hip_fail(e, "workspace_status");
-        return fail(DFLASH_E_HIP, "a bounded wait of the round kernel timed out (not all workgroups were resident)");
+        if (h == 2) return fail(DFLASH_E_HIP, "the round kernel found its arguments at an unexpected place; its output is NaN");
+        return fail(DFLASH_E_HIP, "a bounded wait of the round kernel timed out (not all workgroups were resident); "
+                                  "its output is NaN");
     }
     return DFLASH_OK;
 }

@@ -1723,9 +1723,35 @@ __device__ __forceinline__ void service_main(SrLds &S) {
     if (SS.last && wait_phase(S, p, 0u)) compute_rinv(S, (const float *)(layer_buf(nl) + SS.o_ssa), p, SS.H);
 }
 
+// A launch that could not finish (a bounded wait expired, so some workgroup
+// never arrived) leaves its result unmistakably invalid: every compute wave
+// that gives up writes NaN over all b output rows (last launch of a round)
+// or over the carried residual (earlier launches, whose successor then
+// produces NaN as well), and the error word is set.  Valid values that other
+// workgroups may still write cannot cover the columns of an aborted
+// workgroup, whose final phase never runs.
+__device__ __forceinline__ void poison_outputs() {
+    const int n = SS.b * SS.H;
+    float *dst = SS.last ? SS.out : SS.xsave;
+    for (int i = lane_id(); i < n; i += 64) st4(dst, (size_t)i * 4, 0x7FC00000u);
+    vm_wait();
+}
+
 template <int WT, int D, bool C>
-__global__ __launch_bounds__(SR_THREADS, 1) void sround_kernel(SrArgs) {
+__global__ __launch_bounds__(SR_THREADS, 1) void sround_kernel(SrArgs a) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // Every device function reads the arguments through ka(), which assumes
+    // the implicit arguments follow SrArgs directly in the kernel-argument
+    // segment.  Check that against the segment pointer this launch received;
+    // on a mismatch nothing below could be trusted, so the launch only marks
+    // its output invalid (through the by-value argument) and sets the error
+    // word.
+    if ((const void *)ka() != (const void *)__builtin_amdgcn_kernarg_segment_ptr()) {
+        if (threadIdx.x == 0) __hip_atomic_store(a.s.ctr + SR_CTR_ERR, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float *dst = a.s.last ? a.s.out : a.s.xsave;
+        for (int i = threadIdx.x; i < a.s.b * a.s.H; i += SR_THREADS) dst[i] = __uint_as_float(0x7FC00000u);
+        return;
+    }
     if (threadIdx.x < 64) {
         if (lane < SR_CW) S.cons[lane] = 0;
         if (lane == 0) { S.pub = 0; S.phase = 0; S.rphase = 0; S.done = 0; S.stg = 0; S.abort_ = 0; }
@@ -1741,7 +1767,10 @@ __global__ __launch_bounds__(SR_THREADS, 1) void sround_kernel(SrArgs) {
         return;
     }
     // compute waves
-    if (!compute_main<WT, D, C>(S)) stc_u(SS.ctr + SR_CTR_ERR, 1u);
+    if (!compute_main<WT, D, C>(S)) {
+        stc_u(SS.ctr + SR_CTR_ERR, 1u);
+        poison_outputs();
+    }
 }
 
 // one wave per workgroup writes that workgroup's slot runs of every layer

@@ -34,9 +34,22 @@
  *  - Call order: dflash_load_weights, then dflash_pack_weights once per
  *    model and device, then any number of ctx_features / ingest_ctx /
  *    forward_round calls.
- *  - A model may serve several streams at once, each with its own workspace.
- *    One dflash_kv and one workspace must not be used by two calls in flight
- *    at the same time.
+ *  - One round at a time per device.  forward_round and forward_full run a
+ *    persistent kernel that needs one resident workgroup on every compute
+ *    unit and spins at grid-wide barriers.  While it runs, no other kernel
+ *    may occupy the device's compute units: the caller keeps at most one
+ *    forward_round / forward_full in flight per device, and does not overlap
+ *    it with other work on other streams.  (ctx_features and ingest_ctx are
+ *    ordinary kernels; the same rule covers them only because they share
+ *    the device.)  One dflash_kv and one workspace must never be used by
+ *    two calls in flight at the same time.
+ *  - If that rule is broken and the round kernel cannot get every
+ *    workgroup resident, its bounded barrier waits expire after about a
+ *    second.  The call has already returned DFLASH_OK (the library never
+ *    synchronises), so the failure shows in the data instead: every output
+ *    row of that round is NaN, an error flag is set in the workspace, and
+ *    every later round on that workspace also yields NaN until
+ *    dflash_workspace_status reports the flag and clears it.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
@@ -66,7 +79,9 @@ extern "C" {
 /* Model dimensions and options ([DflashDraft] field "cfg"; [atlas
  * dflash_head] overview).  Supported: hidden, intermediate, n_q_heads*head_dim
  * and n_taps*hidden are multiples of 256.  head_dim is 64 or 128.  n_q_heads is
- * a multiple of n_kv_heads, with n_q_heads/n_kv_heads <= 16.  For DFLASH_F32
+ * a multiple of n_kv_heads, with n_q_heads/n_kv_heads <= 8 (the round
+ * kernel's attention item holds one q head per compute wave; a larger ratio
+ * is DFLASH_E_UNSUPPORTED).  For DFLASH_F32
  * weights the KV dtype must be DFLASH_F32; otherwise it must be DFLASH_BF16.
  * d2_groups divides hidden; 0 disables the DFlash2 conv wrap. */
 typedef struct dflash_cfg {
@@ -237,12 +252,15 @@ int dflash_forward_full(const dflash_model *m, const float *taps, const float *n
                         const int32_t *pos, int32_t n, int32_t b, float *out,
                         dflash_kv *scratch, void *ws, size_t ws_bytes, void *stream);
 
-/* Synchronise `stream`, then report whether a kernel that used `ws` hit its
- * bounded grid-barrier wait.  The persistent round kernel needs one resident
- * workgroup per CU; if some could not start, its barriers time out after
- * about a second.  The kernel then exits with an undefined output and sets a
- * flag in the workspace.  Returns DFLASH_E_HIP (and clears the flag) if the
- * flag was set, else DFLASH_OK.  A diagnostic call: it blocks the host. */
+/* Synchronise `stream`, then report whether a round kernel that used `ws`
+ * failed.  The persistent round kernel needs one resident workgroup per CU;
+ * if some could not start, its barriers time out after about a second, it
+ * writes NaN over its output rows and sets a flag in the workspace.  The
+ * kernel also sets the flag (and writes NaN) if it finds its arguments
+ * somewhere other than where its code expects them.  Returns DFLASH_E_HIP
+ * (and clears the flag and the barrier counters, so that later rounds work
+ * again) if the flag was set, else DFLASH_OK.  A diagnostic call: it blocks
+ * the host. */
 int dflash_workspace_status(const dflash_model *m, void *ws, size_t ws_bytes, void *stream);
 
 /* Message for the calling thread's last error ("" if none). */

@@ -3,8 +3,20 @@ cached round at ctx 4096 (ctx_features 16 + ingest 16 + forward_round b=16),
 in the same launch configuration bench.py times.
 
 The oracle computes every output element at this size in a few seconds, so
-the comparison is complete.  It also checks that the argmax over a seeded
-151,936-row stand-in lm_head agrees.
+the comparison is complete.  Each round is checked twice over:
+* every output element against the oracle (2e-2, per-row relative);
+* the argmax over a seeded 151,936-row stand-in lm_head, identical in every
+  row whose oracle top-2 gap is not a near-tie.
+
+With N(0, 0.02) weights and N(0, 1) block embeddings, attention contributes
+little to the output: dropping a whole 64-key split moves it by only
+~1.5e-2.  The second round therefore scales the block embeddings by 0.1, so
+that attention shapes the residual stream.  There the planted mistakes move
+the output by 0.08 to 0.27 while the kernel's bf16 rounding moves it by
+~1.1e-2 (a CPU emulation of its rounding points, and this test on the GPU);
+tests/test_parity_sensitivity.py pins the mistakes' effect on the CPU.  A
+smaller scale makes the layers amplify every rounding as much as the
+mistakes (x0.01: 1.8e-2 from rounding alone), so 0.1 is the balance.
 """
 import numpy as np
 import pytest
@@ -12,7 +24,7 @@ import torch
 
 import synth
 from oracle import dflash_oracle as O
-from tests.gpu_util import check, dev, host, tol_for
+from tests.gpu_util import argmax_check, check, dev, host, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -37,40 +49,36 @@ def c3():
         dr.ingest_ctx(kv, dr.ctx_features(dev(taps)), dev(pos))
         O.ingest_ctx(m, okv, O.ctx_features(m, taps), pos)
     print(f"[c3] prefilled {base} rows", flush=True)
-    return cfg, m, dr, kv, okv, D
+    lm = synth.make_lm_head(cfg).astype(np.float64)
+    return cfg, m, dr, kv, okv, D, lm
 
 
-def test_c3_round_matches_oracle(c3):
-    cfg, m, dr, kv, okv, D = c3
+@pytest.mark.parametrize("emb_scale", [1.0, 0.1])
+def test_c3_round_matches_oracle(c3, emb_scale):
+    cfg, m, dr, kv, okv, D, lm = c3
     ctx, t, b = cfg.ctx, cfg.new_rows, cfg.block
     base = ctx - t
+    kv.len = base
+    okv.truncate(base)
     taps = synth.make_taps(cfg, t, stream=1)
-    noise = synth.make_noise(cfg)
+    noise = synth.make_noise(cfg) * np.float32(emb_scale)
     pos_new, pos_blk = synth.positions(base, t), synth.positions(ctx, b)
+    tag = f"c3 emb x{emb_scale:g}"
 
     feats = dr.ctx_features(dev(taps))
-    check("c3 ctx_features(16)", host(feats), O.ctx_features(m, taps), 2e-3)
+    check(f"{tag} ctx_features(16)", host(feats), O.ctx_features(m, taps), 2e-3)
     dr.ingest_ctx(kv, feats, dev(pos_new))
     out = host(dr.forward_round(kv, dev(noise), dev(pos_blk)))
+    dr.status()
     assert kv.len == ctx
 
     O.ingest_ctx(m, okv, O.ctx_features(m, taps), pos_new)
     ref = O.forward_round(m, okv, noise, pos_blk)
-    check("c3 forward_round ctx 4096", out, ref, tol_for(cfg))
-
-    # identical argmax over a seeded lm_head, up to ties within the measured perturbation
-    lm = synth.make_lm_head(cfg).astype(np.float64)
-    am_o, lo_o = O.lm_argmax(ref, lm)
-    am_g, lo_g = O.lm_argmax(out, lm)
-    pert = np.abs(lo_g - lo_o).max(axis=1)
-    mism = [(r, am_g[r], am_o[r]) for r in range(b) if am_g[r] != am_o[r]]
-    real = [x for x in mism if lo_o[x[0], x[2]] - lo_o[x[0], x[1]] > pert[x[0]]]
-    print(f"[c3] argmax mismatches: {len(mism)} (beyond perturbation: {len(real)})", flush=True)
-    assert not real, real
+    check(f"{tag} forward_round ctx 4096", out, ref, tol_for(cfg))
+    argmax_check(f"{tag} forward_round ctx 4096", out, ref, lm)
 
     # rewind and repeat: deterministic, and len-only rewind is a valid state
     kv.len = base
-    okv.truncate(base)
     dr.ingest_ctx(kv, dr.ctx_features(dev(taps)), dev(pos_new))
     out2 = host(dr.forward_round(kv, dev(noise), dev(pos_blk)))
     assert np.array_equal(out, out2), "round is not bitwise deterministic"

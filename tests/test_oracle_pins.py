@@ -273,14 +273,30 @@ def test_p6_ctx_rows_are_keys_from_features():
 
 
 def test_p6_ctx_features_fc_then_norm():
-    """ctx features = hidden_norm(fc(concat taps)), taps in input order,
-    checked against torch's linear + rms_norm in float64."""
-    m = small_model()
-    taps = synth.make_taps(SMALL, 9)
-    ref = torch.nn.functional.rms_norm(
-        torch.from_numpy(taps.astype(np.float64)) @ torch.from_numpy(m.fc).T,
-        (SMALL.hidden,), torch.from_numpy(m.g_hidden_norm), SMALL.rms_eps)
-    assert rel(O.ctx_features(m, taps), ref.numpy()) <= 1e-13
+    """ctx features = hidden_norm(fc(concat taps)) against a closed form.
+
+    With fc = [0 | I | 0] (it selects tap 1 of the concatenation), fc(taps)
+    is tap 1 itself, so the features must be g_hn * tap1 / rms(tap1).  The
+    hidden_norm gain is 2 + N(0, 0.02) per channel and the final-norm gain
+    is set to 3, so using the wrong gain or the wrong tap changes every
+    value; the features' RMS must be ~2 (the gain), not ~3 or ~1."""
+    cfg = SMALL
+    m = small_model(cfg)
+    H, T = cfg.hidden, cfg.n_taps
+    m.fc = np.zeros((H, T * H))
+    m.fc[:, H:2 * H] = np.eye(H)
+    m.g_hidden_norm = 2.0 + 0.02 * np.random.default_rng(3).standard_normal(H)
+    m.g_norm = np.full(H, 3.0)
+    taps = synth.make_taps(cfg, 9).astype(np.float64)
+    tap1 = taps[:, H:2 * H]
+    expect = np.empty_like(tap1)
+    for r in range(tap1.shape[0]):                       # written out per row and channel
+        rms = math.sqrt(sum(v * v for v in tap1[r]) / H + cfg.rms_eps)
+        for c in range(H):
+            expect[r, c] = m.g_hidden_norm[c] * tap1[r, c] / rms
+    got = O.ctx_features(m, taps)
+    assert rel(got, expect) <= 1e-13
+    assert np.allclose(np.sqrt(np.mean(got ** 2, axis=1)), 2.0, atol=0.02)
 
 
 # ---------------------------------------------------------------- P7 -------
