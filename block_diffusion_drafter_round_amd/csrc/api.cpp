@@ -230,7 +230,8 @@ dfl::GemmSeg seg(const dflash_matrix &m, int n) { return dfl::GemmSeg{m.data, m.
 
 // ---- launch sequences (arguments already checked) ---------------------------
 
-hipError_t run_ctx_features(const dflash_model *m, const float *taps, int t, float *feats, void *ws, const WsLayout &L,
+// fc GEMM (split-K partials in `part`, counters in `cnt`) + hidden_norm
+hipError_t run_ctx_features(const dflash_model *m, const float *taps, int t, float *feats, float *part, unsigned *cnt,
                             hipStream_t s) {
     const dflash_cfg &c = m->cfg;
     dfl::GemmArgs g{};
@@ -240,7 +241,7 @@ hipError_t run_ctx_features(const dflash_model *m, const float *taps, int t, flo
     hipError_t e;
     {
         ProfScope p(DFLASH_K_GEMM_FC, s);
-        e = dfl::gemm(g, at<float>(ws, L.gpart), at<unsigned>(ws, L.gcnt), s);
+        e = dfl::gemm(g, part, cnt, s);
     }
     if (e != hipSuccess) return e;
     ProfScope p(DFLASH_K_NORM, s);
@@ -489,8 +490,27 @@ int dflash_ctx_features(const dflash_model *m, const float *taps, int32_t t, flo
     if (!aligned(taps, 16) || !aligned(feats, 16)) return fail(DFLASH_E_INVAL, "taps / feats null or not 16-byte aligned");
     int rc = check_ws(m, ws, ws_bytes, t);
     if (rc) return rc;
-    hipError_t e = run_ctx_features(m, taps, t, feats, ws, ws_layout(m->cfg, t), (hipStream_t)stream);
+    const WsLayout L = ws_layout(m->cfg, t);
+    hipError_t e = run_ctx_features(m, taps, t, feats, at<float>(ws, L.gpart), at<unsigned>(ws, L.gcnt), (hipStream_t)stream);
     return e == hipSuccess ? DFLASH_OK : hip_fail(e, "ctx_features");
+}
+
+int dflash_ctx_features_noalloc(const dflash_model *m, const float *taps, int32_t t, float *feats, void *stream) {
+    g_err.clear();
+    if (!m) return fail(DFLASH_E_INVAL, "model is null");
+    if (t < 0) return fail(DFLASH_E_INVAL, "t = %d is negative", t);
+    if (t > DFLASH_NOALLOC_MAX_ROWS)
+        return fail(DFLASH_E_INVAL, "t = %d exceeds the allocation-free entry point's maximum of %d rows", t,
+                    DFLASH_NOALLOC_MAX_ROWS);
+    if (t == 0) return DFLASH_OK;
+    if (!aligned(taps, 16) || !aligned(feats, 16)) return fail(DFLASH_E_INVAL, "taps / feats null or not 16-byte aligned");
+    void *sp = nullptr;
+    hipError_t e = dfl::noalloc_scratch(&sp, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ctx_features_noalloc scratch");
+    float *part = static_cast<float *>(sp);
+    unsigned *cnt = reinterpret_cast<unsigned *>(static_cast<char *>(sp) + dfl::NOALLOC_PART_BYTES);
+    e = run_ctx_features(m, taps, t, feats, part, cnt, (hipStream_t)stream);
+    return e == hipSuccess ? DFLASH_OK : hip_fail(e, "ctx_features_noalloc");
 }
 
 int dflash_ingest_ctx(const dflash_model *m, dflash_kv *kv, const float *feats, const int32_t *pos_new, int32_t t,
@@ -547,7 +567,7 @@ int dflash_forward_full(const dflash_model *m, const float *taps, const float *n
     dflash_kv kv = *scratch;
     kv.len = 0;
     if (n > 0) {
-        e = run_ctx_features(m, taps, n, feats, ws, L, s);
+        e = run_ctx_features(m, taps, n, feats, at<float>(ws, L.gpart), at<unsigned>(ws, L.gcnt), s);
         if (e == hipSuccess) e = run_ingest(m, &kv, feats, pos, n, ws, L, s);
         kv.len = n;
     }

@@ -35,7 +35,16 @@ constexpr int    GEMM_MAX_COUNTERS = 1 << 14;
 
 // Plans the split and launches.  part/cnt must point at workspace regions of
 // GEMM_PART_FLOATS floats / GEMM_MAX_COUNTERS counters (zero-filled counters).
+// The plan never needs more: it lowers the K split until the partials fit.
 hipError_t gemm(GemmArgs a, float *part, unsigned *cnt, hipStream_t s);
+
+// ---- allocation-free entry point: one static device scratch array ---------
+// The split-K partials, then the counters, of the ctx_features GEMM.
+constexpr size_t NOALLOC_PART_BYTES = 4 * GEMM_PART_FLOATS;
+constexpr size_t NOALLOC_SCRATCH_BYTES = NOALLOC_PART_BYTES + sizeof(unsigned) * GEMM_MAX_COUNTERS;
+// Device address of the current device's scratch array (looked up, and its
+// counters cleared by a kernel on `stream`, on the first call per device).
+hipError_t noalloc_scratch(void **out, hipStream_t stream);
 // number of workgroups a plan would use (for tests / diagnostics)
 int gemm_plan(GemmArgs &a);
 

@@ -61,7 +61,8 @@ _lib = None
 EXPORTS = ("dflash_load_weights", "dflash_free", "dflash_workspace_bytes", "dflash_ctx_features",
            "dflash_ingest_ctx", "dflash_forward_round", "dflash_forward_full", "dflash_last_error",
            "dflash_rope_table", "dflash_prof_start", "dflash_prof_stop", "dflash_workspace_status",
-           "dflash_prof_trace", "dflash_prof_trace_read", "dflash_packed_bytes", "dflash_pack_weights")
+           "dflash_prof_trace", "dflash_prof_trace_read", "dflash_packed_bytes", "dflash_pack_weights",
+           "dflash_ctx_features_noalloc")
 
 # kernel classes of the measurement hook (include/dflash_prof.h)
 K_GEMM_FC, K_GEMM_KV, K_GEMM_QKV, K_GEMM_O, K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN, K_ROPE, K_NORM, K_ROUND = range(1, 11)
@@ -85,6 +86,7 @@ def lib():
     L.dflash_packed_bytes.restype = sz
     L.dflash_pack_weights.argtypes = [vp, vp, sz, vp]
     L.dflash_ctx_features.argtypes = [vp, vp, i32, vp, vp, sz, vp]
+    L.dflash_ctx_features_noalloc.argtypes = [vp, vp, i32, vp, vp]
     L.dflash_ingest_ctx.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, i32, vp, sz, vp]
     L.dflash_forward_round.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, i32, vp, vp, sz, vp]
     L.dflash_forward_full.argtypes = [vp, vp, vp, vp, i32, i32, vp, C.POINTER(dflash_kv), vp, sz, vp]
@@ -154,6 +156,10 @@ def dflash_workspace_bytes(model: int, max_rows: int) -> int:
 
 def dflash_ctx_features(model, taps, t, feats, ws, ws_bytes, stream=None) -> None:
     _check(lib().dflash_ctx_features(model, _ptr(taps), t, _ptr(feats), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dflash_ctx_features_noalloc(model, taps, t, feats, stream=None) -> None:
+    _check(lib().dflash_ctx_features_noalloc(model, _ptr(taps), t, _ptr(feats), _stream(stream)))
 
 
 def dflash_ingest_ctx(model, kv: dflash_kv, feats, pos_new, t, ws, ws_bytes, stream=None) -> None:

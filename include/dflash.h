@@ -215,6 +215,21 @@ size_t dflash_workspace_bytes(const dflash_model *m, int32_t max_rows);
 int dflash_ctx_features(const dflash_model *m, const float *taps, int32_t t,
                         float *feats, void *ws, size_t ws_bytes, void *stream);
 
+/* Allocation-free variant of dflash_ctx_features, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): same arguments and result, but no
+ * workspace.  Its scratch (the fc GEMM's split-K partial sums and counters,
+ * 4 MiB + 64 KiB) is a static device array inside the library, one per
+ * device, held until the process ends; the first call on a device looks up
+ * that array's address and enqueues a kernel that zeroes its counters.  The
+ * call allocates nothing (no hipMalloc, no allocating library routine).
+ * t <= DFLASH_NOALLOC_MAX_ROWS, else DFLASH_E_INVAL.  Every call on one
+ * device shares that device's array: two such calls that overlap on one
+ * device (different streams, or different threads without ordering) race
+ * and give wrong results; calls ordered on one stream are fine. */
+#define DFLASH_NOALLOC_MAX_ROWS 65536
+int dflash_ctx_features_noalloc(const dflash_model *m, const float *taps, int32_t t, float *feats, void *stream);
+
 /* Append t committed ctx rows to the draft KV cache ([DflashDraft]
  * "ingest_ctx").  Per layer: k/v projections of the features, k head-norm,
  * rope (times the YaRN mscale), and the rows stored at kv->len.  Then
