@@ -53,6 +53,11 @@ class dflash_weights(C.Structure):
                 ("layers", C.POINTER(dflash_layer_weights))]
 
 
+class dflash2_selector(C.Structure):
+    _fields_ = [("vocab", C.c_int32), ("rank", C.c_int32), ("top_k", C.c_int32),
+                ("pred_codebook", C.c_void_p), ("succ_codebook", C.c_void_p), ("w_hidden_proj", C.c_void_p)]
+
+
 class dflash_kv(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("capacity", C.c_int32), ("len", C.c_int32)]
 
@@ -62,7 +67,8 @@ EXPORTS = ("dflash_load_weights", "dflash_free", "dflash_workspace_bytes", "dfla
            "dflash_ingest_ctx", "dflash_forward_round", "dflash_forward_full", "dflash_last_error",
            "dflash_rope_table", "dflash_prof_start", "dflash_prof_stop", "dflash_workspace_status",
            "dflash_prof_trace", "dflash_prof_trace_read", "dflash_packed_bytes", "dflash_pack_weights",
-           "dflash_ctx_features_noalloc")
+           "dflash_ctx_features_noalloc", "dflash_accept_prefix", "dflash_rejection_accept_len",
+           "dflash_confidence_vt", "dflash_slot_confidence_vt", "dflash2_walk_greedy", "dflash2_walk_sampled")
 
 # kernel classes of the measurement hook (include/dflash_prof.h)
 K_GEMM_FC, K_GEMM_KV, K_GEMM_QKV, K_GEMM_O, K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN, K_ROPE, K_NORM, K_ROUND = range(1, 11)
@@ -96,6 +102,14 @@ def lib():
     L.dflash_prof_stop.argtypes = [C.POINTER(C.c_double), C.POINTER(i32)]
     L.dflash_workspace_status.argtypes = [vp, vp, sz, vp]
     L.dflash_prof_trace.argtypes = [i32]
+    pi32, pf32, pf64 = C.POINTER(i32), C.POINTER(C.c_float), C.POINTER(C.c_double)
+    L.dflash_accept_prefix.argtypes = [pi32, i32, pi32, i32, pi32]
+    L.dflash_rejection_accept_len.argtypes = [pf64, pf64, pf64, i32, pi32]
+    L.dflash_confidence_vt.argtypes = [pf32, i32, C.c_double, i32, pi32]
+    L.dflash_slot_confidence_vt.argtypes = [pf32, i32, C.c_double, i32, pi32]
+    L.dflash2_walk_greedy.argtypes = [C.POINTER(dflash2_selector), pf32, pi32, pf32, i32, i32, pi32]
+    L.dflash2_walk_sampled.argtypes = [C.POINTER(dflash2_selector), pf32, pi32, pf32, i32, i32, C.c_double, pf64,
+                                       pi32, pf64, pf64]
     L.dflash_prof_trace_read.argtypes = [vp, vp, sz, C.POINTER(C.c_uint64), i32, vp]
     for name in EXPORTS:
         if name not in ("dflash_free", "dflash_workspace_bytes", "dflash_last_error", "dflash_packed_bytes"):
@@ -176,6 +190,96 @@ def dflash_forward_full(model, taps, noise_emb, pos, n, b, out, scratch: dflash_
                         stream=None) -> None:
     _check(lib().dflash_forward_full(model, _ptr(taps), _ptr(noise_emb), _ptr(pos), n, b, _ptr(out),
                                      C.byref(scratch), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+# ---- host policy functions (include/dflash_policy.h) ------------------------
+
+def _arr(ctype, values):
+    values = list(values)
+    return (ctype * max(len(values), 1))(*values), len(values)
+
+
+def _policy_check(rc: int, name: str):
+    if rc != DFLASH_OK:
+        raise DflashError(rc, f"{name}: invalid argument")
+
+
+def dflash_accept_prefix(cand, vam) -> int:
+    c, nc = _arr(C.c_int32, cand)
+    v, nv = _arr(C.c_int32, vam)
+    m = C.c_int32()
+    _policy_check(lib().dflash_accept_prefix(c, nc, v, nv, C.byref(m)), "accept_prefix")
+    return m.value
+
+
+def dflash_rejection_accept_len(p, q, u) -> int:
+    n = len(p)
+    pa, _ = _arr(C.c_double, p)
+    qa, _ = _arr(C.c_double, q)
+    ua, _ = _arr(C.c_double, u)
+    out = C.c_int32()
+    _policy_check(lib().dflash_rejection_accept_len(pa, qa, ua, n, C.byref(out)), "rejection_accept_len")
+    return out.value
+
+
+def dflash_confidence_vt(raws, tau: float, vt_cap: int) -> int:
+    r, n = _arr(C.c_float, raws)
+    out = C.c_int32()
+    _policy_check(lib().dflash_confidence_vt(r, n, tau, vt_cap, C.byref(out)), "confidence_vt")
+    return out.value
+
+
+def dflash_slot_confidence_vt(raws, tau: float, vt_cap: int) -> int:
+    r, n = _arr(C.c_float, raws)
+    out = C.c_int32()
+    _policy_check(lib().dflash_slot_confidence_vt(r, n, tau, vt_cap, C.byref(out)), "slot_confidence_vt")
+    return out.value
+
+
+def make_selector(pred_codebook, succ_codebook, top_k: int, w_hidden_proj=None):
+    """A dflash2_selector over host bf16 codebooks (uint16 numpy arrays
+    [vocab, rank], kept alive by the caller) and an optional device
+    projection matrix."""
+    import numpy as np
+    assert pred_codebook.dtype == np.uint16 and pred_codebook.flags.c_contiguous
+    assert succ_codebook.shape == pred_codebook.shape and succ_codebook.flags.c_contiguous
+    return dflash2_selector(vocab=pred_codebook.shape[0], rank=pred_codebook.shape[1], top_k=top_k,
+                            pred_codebook=pred_codebook.ctypes.data, succ_codebook=succ_codebook.ctypes.data,
+                            w_hidden_proj=_ptr(w_hidden_proj))
+
+
+def _np_ptr(a, ctype):
+    return a.ctypes.data_as(C.POINTER(ctype))
+
+
+def dflash2_walk_greedy(sel: dflash2_selector, unary, cand, hproj, anchor: int):
+    import numpy as np
+    unary = np.ascontiguousarray(unary, dtype=np.float32)
+    cand = np.ascontiguousarray(cand, dtype=np.int32)
+    hproj = np.ascontiguousarray(hproj, dtype=np.float32)
+    nd = unary.shape[0]
+    path = np.zeros(max(nd, 1), dtype=np.int32)
+    _policy_check(lib().dflash2_walk_greedy(C.byref(sel), _np_ptr(unary, C.c_float), _np_ptr(cand, C.c_int32),
+                                            _np_ptr(hproj, C.c_float), nd, anchor, _np_ptr(path, C.c_int32)),
+                  "walk_greedy")
+    return path[:nd].tolist()
+
+
+def dflash2_walk_sampled(sel: dflash2_selector, unary, cand, hproj, anchor: int, temperature: float, uniforms):
+    import numpy as np
+    unary = np.ascontiguousarray(unary, dtype=np.float32)
+    cand = np.ascontiguousarray(cand, dtype=np.int32)
+    hproj = np.ascontiguousarray(hproj, dtype=np.float32)
+    uni = np.ascontiguousarray(uniforms, dtype=np.float64)
+    nd, k = unary.shape
+    path = np.zeros(max(nd, 1), dtype=np.int32)
+    qc = np.zeros(max(nd, 1), dtype=np.float64)
+    qr = np.zeros(max(nd * k, 1), dtype=np.float64)
+    _policy_check(lib().dflash2_walk_sampled(C.byref(sel), _np_ptr(unary, C.c_float), _np_ptr(cand, C.c_int32),
+                                             _np_ptr(hproj, C.c_float), nd, anchor, temperature,
+                                             _np_ptr(uni, C.c_double), _np_ptr(path, C.c_int32),
+                                             _np_ptr(qc, C.c_double), _np_ptr(qr, C.c_double)), "walk_sampled")
+    return path[:nd].tolist(), qc[:nd].tolist(), qr[:nd * k].tolist()
 
 
 def dflash_last_error() -> str:

@@ -27,10 +27,10 @@ def D():
 
 def declared_functions():
     names = []
-    for h in ("dflash.h", "dflash_prof.h"):
+    for h in ("dflash.h", "dflash_prof.h", "dflash_policy.h"):
         src = open(os.path.join(ROOT, "include", h)).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(dflash_[a-z_0-9]+)\s*\(", src, flags=re.M)
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(dflash2?_[a-z_0-9]+)\s*\(", src, flags=re.M)
     return sorted(set(names))
 
 
