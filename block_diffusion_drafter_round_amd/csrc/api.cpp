@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "dflash.h"
+#include "dflash_policy.h"
 #include "dflash_prof.h"
 #include "kernels.h"
 #include "sround.h"
@@ -598,6 +599,86 @@ int dflash_workspace_status(const dflash_model *m, void *ws, size_t ws_bytes, vo
                                   "its output is NaN");
     }
     return DFLASH_OK;
+}
+
+// ---- DFlash2 proposal ([DflashDraft] "dflash2_propose_greedy") ----------------
+
+namespace {
+
+// device step into `packed`: [nd][k] values, [nd][k] indices, [nd][rank] projection
+int propose_prepare(const dflash_model *m, const dflash2_selector *sel, const float *logits, const float *hidden, int b,
+                    uint32_t *packed, void *ws, size_t ws_bytes, hipStream_t s) {
+    if (!m || !sel) return fail(DFLASH_E_INVAL, "model / selector is null");
+    if (sel->vocab <= 0 || sel->top_k < 1 || sel->top_k > DFLASH2_MAX_TOPK || sel->rank < 1 || sel->rank > DFLASH2_MAX_RANK)
+        return fail(DFLASH_E_INVAL, "selector: vocab %d, top_k %d (1..%d), rank %d (1..%d)", sel->vocab, sel->top_k,
+                    DFLASH2_MAX_TOPK, sel->rank, DFLASH2_MAX_RANK);
+    if (sel->top_k > sel->vocab) return fail(DFLASH_E_INVAL, "top_k %d exceeds the vocabulary %d", sel->top_k, sel->vocab);
+    if (!aligned(sel->w_hidden_proj, 16)) return fail(DFLASH_E_INVAL, "selector w_hidden_proj null or not 16-byte aligned");
+    if (b < 2 || b > MAX_BLOCK) return fail(DFLASH_E_INVAL, "block size b = %d outside [2, 16] (row 0 is the anchor)", b);
+    if (!aligned(logits, 4) || !aligned(hidden, 4) || !aligned(packed, 4))
+        return fail(DFLASH_E_INVAL, "draft logits / hidden / output null or misaligned");
+    const int nd = b - 1, k = sel->top_k, nc = dfl::topk_chunks(sel->vocab);
+    if ((size_t)nc * k > (size_t)dfl::TOPK_STAGE2)
+        return fail(DFLASH_E_UNSUPPORTED, "vocabulary %d with top_k %d needs %d stage-1 candidates per row (at most %d)",
+                    sel->vocab, k, nc * k, dfl::TOPK_STAGE2);
+    int rc = check_ws(m, ws, ws_bytes, 0);
+    if (rc) return rc;
+    const WsLayout L = ws_layout(m->cfg, 0);
+    const size_t part = (size_t)nd * nc * k;
+    if (2 * part * 4 > 4 * dfl::GEMM_PART_FLOATS)
+        return fail(DFLASH_E_UNSUPPORTED, "top-k partials of %zu bytes exceed the workspace's %zu", 2 * part * 4,
+                    4 * dfl::GEMM_PART_FLOATS);
+    float *pv = at<float>(ws, L.gpart);
+    int32_t *pi = reinterpret_cast<int32_t *>(pv + part);
+    float *vals = reinterpret_cast<float *>(packed);
+    int32_t *idx = reinterpret_cast<int32_t *>(packed + (size_t)nd * k);
+    float *hp = reinterpret_cast<float *>(packed + (size_t)2 * nd * k);
+    const long long V = sel->vocab;
+    hipError_t e = dfl::topk_rows(logits + V, V, nd, sel->vocab, k, pv, pi, vals, idx, s);
+    if (e == hipSuccess)
+        e = dfl::hidden_projection(hidden + m->cfg.hidden, m->cfg.hidden, sel->w_hidden_proj, sel->rank, nd, hp, s);
+    return e == hipSuccess ? DFLASH_OK : hip_fail(e, "dflash2_propose");
+}
+
+}  // namespace
+
+int dflash2_propose_prepare(const dflash_model *m, const dflash2_selector *sel, const float *draft_logits,
+                            const float *hidden, int32_t b, uint32_t *packed, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    return propose_prepare(m, sel, draft_logits, hidden, b, packed, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int dflash2_propose_greedy(const dflash_model *m, const dflash2_selector *sel, const float *draft_logits,
+                           const float *hidden, int32_t b, int32_t anchor, int32_t *drafts, void *ws, size_t ws_bytes,
+                           void *stream) {
+    g_err.clear();
+    if (!drafts) return fail(DFLASH_E_INVAL, "drafts is null");
+    if (!m || !sel) return fail(DFLASH_E_INVAL, "model / selector is null");
+    if (!sel->pred_codebook || !sel->succ_codebook) return fail(DFLASH_E_INVAL, "selector codebooks are null");
+    if (b < 2 || b > MAX_BLOCK) return fail(DFLASH_E_INVAL, "block size b = %d outside [2, 16] (row 0 is the anchor)", b);
+    if (anchor < 0 || anchor >= sel->vocab) return fail(DFLASH_E_INVAL, "anchor %d outside the vocabulary", anchor);
+    const int nd = b - 1, k = sel->top_k, rank = sel->rank;
+    // the packed block sits after the top-k partials in the GEMM scratch region
+    if (!aligned(ws, 256)) return fail(DFLASH_E_INVAL, "workspace null or not 256-byte aligned");
+    const WsLayout L = ws_layout(m->cfg, 0);
+    const size_t words = (size_t)nd * (2 * k + rank);
+    const size_t part_bytes = 2 * (size_t)nd * dfl::topk_chunks(std::max(sel->vocab, 1)) * k * 4;
+    if (part_bytes + 4 * words > 4 * dfl::GEMM_PART_FLOATS)
+        return fail(DFLASH_E_UNSUPPORTED, "top-k partials and packed block exceed the workspace's scratch region");
+    uint32_t *packed = at<uint32_t>(ws, L.gpart + (part_bytes + 255) / 256 * 256);
+    hipStream_t s = (hipStream_t)stream;
+    int rc = propose_prepare(m, sel, draft_logits, hidden, b, packed, ws, ws_bytes, s);
+    if (rc) return rc;
+    // the one small device-to-host copy of the round, then the host walk
+    std::vector<uint32_t> host(words);
+    hipError_t e = hipMemcpyAsync(host.data(), packed, 4 * words, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "dflash2_propose_greedy copy");
+    const float *vals = reinterpret_cast<const float *>(host.data());
+    const int32_t *idx = reinterpret_cast<const int32_t *>(host.data() + (size_t)nd * k);
+    const float *hp = reinterpret_cast<const float *>(host.data() + (size_t)2 * nd * k);
+    rc = dflash2_walk_greedy(sel, vals, idx, hp, nd, anchor, drafts);
+    return rc ? fail(rc, "dflash2_propose_greedy: walk rejected its inputs") : DFLASH_OK;
 }
 
 int dflash_prof_trace(int32_t enable) {

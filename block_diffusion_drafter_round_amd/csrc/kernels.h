@@ -38,6 +38,18 @@ constexpr int    GEMM_MAX_COUNTERS = 1 << 14;
 // The plan never needs more: it lowers the K split until the partials fit.
 hipError_t gemm(GemmArgs a, float *part, unsigned *cnt, hipStream_t s);
 
+// ---- DFlash2 proposal: top-k over draft logits, rank-r hidden projection ----
+constexpr int TOPK_CHUNK = 4096;     // values per stage-1 wave (64 per lane)
+constexpr int TOPK_STAGE2 = 4096;    // stage-1 candidates one stage-2 wave can hold
+int topk_chunks(int vocab);
+// Per row: the k largest logits (larger first, then lower index) and their
+// indices.  part_v / part_i hold rows * topk_chunks(vocab) * k entries, and
+// topk_chunks(vocab) * k <= TOPK_STAGE2.
+hipError_t topk_rows(const float *logits, long long ld, int rows, int vocab, int k, float *part_v, int32_t *part_i,
+                     float *vals, int32_t *idx, hipStream_t s);
+// out[r][j] = hidden[r] . w[j] for bf16 w [rank][H], f32 accumulation
+hipError_t hidden_projection(const float *hidden, int H, const void *w, int rank, int rows, float *out, hipStream_t s);
+
 // ---- allocation-free entry point: one static device scratch array ---------
 // The split-K partials, then the counters, of the ctx_features GEMM.
 constexpr size_t NOALLOC_PART_BYTES = 4 * GEMM_PART_FLOATS;

@@ -68,7 +68,8 @@ EXPORTS = ("dflash_load_weights", "dflash_free", "dflash_workspace_bytes", "dfla
            "dflash_rope_table", "dflash_prof_start", "dflash_prof_stop", "dflash_workspace_status",
            "dflash_prof_trace", "dflash_prof_trace_read", "dflash_packed_bytes", "dflash_pack_weights",
            "dflash_ctx_features_noalloc", "dflash_accept_prefix", "dflash_rejection_accept_len",
-           "dflash_confidence_vt", "dflash_slot_confidence_vt", "dflash2_walk_greedy", "dflash2_walk_sampled")
+           "dflash_confidence_vt", "dflash_slot_confidence_vt", "dflash2_walk_greedy", "dflash2_walk_sampled",
+           "dflash2_propose_prepare", "dflash2_propose_greedy")
 
 # kernel classes of the measurement hook (include/dflash_prof.h)
 K_GEMM_FC, K_GEMM_KV, K_GEMM_QKV, K_GEMM_O, K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN, K_ROPE, K_NORM, K_ROUND = range(1, 11)
@@ -110,6 +111,8 @@ def lib():
     L.dflash2_walk_greedy.argtypes = [C.POINTER(dflash2_selector), pf32, pi32, pf32, i32, i32, pi32]
     L.dflash2_walk_sampled.argtypes = [C.POINTER(dflash2_selector), pf32, pi32, pf32, i32, i32, C.c_double, pf64,
                                        pi32, pf64, pf64]
+    L.dflash2_propose_prepare.argtypes = [vp, C.POINTER(dflash2_selector), vp, vp, i32, vp, vp, sz, vp]
+    L.dflash2_propose_greedy.argtypes = [vp, C.POINTER(dflash2_selector), vp, vp, i32, i32, pi32, vp, sz, vp]
     L.dflash_prof_trace_read.argtypes = [vp, vp, sz, C.POINTER(C.c_uint64), i32, vp]
     for name in EXPORTS:
         if name not in ("dflash_free", "dflash_workspace_bytes", "dflash_last_error", "dflash_packed_bytes"):
@@ -280,6 +283,20 @@ def dflash2_walk_sampled(sel: dflash2_selector, unary, cand, hproj, anchor: int,
                                              _np_ptr(uni, C.c_double), _np_ptr(path, C.c_int32),
                                              _np_ptr(qc, C.c_double), _np_ptr(qr, C.c_double)), "walk_sampled")
     return path[:nd].tolist(), qc[:nd].tolist(), qr[:nd * k].tolist()
+
+
+def dflash2_propose_prepare(model, sel: dflash2_selector, draft_logits, hidden, b: int, packed, ws, ws_bytes,
+                            stream=None) -> None:
+    _check(lib().dflash2_propose_prepare(model, C.byref(sel), _ptr(draft_logits), _ptr(hidden), b, _ptr(packed),
+                                         _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dflash2_propose_greedy(model, sel: dflash2_selector, draft_logits, hidden, b: int, anchor: int, ws, ws_bytes,
+                           stream=None):
+    out = (C.c_int32 * max(b - 1, 1))()
+    _check(lib().dflash2_propose_greedy(model, C.byref(sel), _ptr(draft_logits), _ptr(hidden), b, anchor, out,
+                                        _ptr(ws), ws_bytes, _stream(stream)))
+    return list(out)[:b - 1]
 
 
 def dflash_last_error() -> str:

@@ -11,10 +11,12 @@
  *  [DflashDraft]          docs.rs memra_engine::dflash::DflashDraft, section
  *                         "dflash2_propose_greedy".
  *
- * Every function here is pure host code over caller-owned host arrays: no
- * HIP call, no allocation, no global state.  Each returns DFLASH_OK, or
- * DFLASH_E_INVAL for a null pointer, a negative count or a value outside
- * its stated range, in which case no output is written.
+ * The accept rules, windows and walks are pure host code over caller-owned
+ * host arrays: no HIP call, no allocation, no global state.  Each returns
+ * DFLASH_OK, or DFLASH_E_INVAL for a null pointer, a negative count or a
+ * value outside its stated range, in which case no output is written.  The
+ * two dflash2_propose_* calls at the end run device kernels and follow the
+ * conventions of dflash.h (dflash_last_error holds their messages).
  */
 #ifndef DFLASH_POLICY_H
 #define DFLASH_POLICY_H
@@ -97,6 +99,36 @@ int dflash2_walk_greedy(const dflash2_selector *s, const float *unary, const int
 int dflash2_walk_sampled(const dflash2_selector *s, const float *unary, const int32_t *cand, const float *hproj,
                          int32_t nd, int32_t anchor, double temperature, const double *uniforms, int32_t *path,
                          double *q_chosen, double *q_rows);
+
+/* Device step of the DFlash2 proposal ([DflashDraft] "dflash2_propose_greedy"):
+ * for the draft rows 1..b-1 (row 0 is the anchor row, not a draft), the
+ * top_k largest draft logits of each row (larger first, equal values in
+ * increasing index order) with their token ids, and the rank-r projection
+ * hproj = hidden . w_hidden_proj^T (f32 accumulation).  Asynchronous on
+ * `stream`; makes no host synchronisation.
+ *   m            : a loaded model (its hidden size and workspace layout).
+ *   sel          : vocab, rank, top_k and the device w_hidden_proj (bf16
+ *                  [rank][hidden]); the codebooks are not used here.
+ *   draft_logits : device f32 [b][vocab] (the target lm_head applied to the
+ *                  round's output; finite values).
+ *   hidden       : device f32 [b][hidden] (the round's output rows).
+ *   packed       : device, nd*(2*top_k + rank) 32-bit words, nd = b - 1:
+ *                  f32 values [nd][top_k], int32 ids [nd][top_k], f32
+ *                  hproj [nd][rank].
+ *   ws           : the model's workspace (dflash_workspace_bytes).
+ * 2 <= b <= 16.  DFLASH_E_UNSUPPORTED if vocab and top_k need more than
+ * 4096 first-stage candidates per row (ceil(vocab / 4096) * top_k). */
+int dflash2_propose_prepare(const struct dflash_model *m, const dflash2_selector *sel, const float *draft_logits,
+                            const float *hidden, int32_t b, uint32_t *packed, void *ws, size_t ws_bytes, void *stream);
+
+/* The whole greedy proposal ([DflashDraft] "dflash2_propose_greedy"): the
+ * device step into the workspace, ONE device-to-host copy of its
+ * nd*(2*top_k + rank) words, then dflash2_walk_greedy from `anchor` on the
+ * host codebooks.  Writes the nd = b - 1 drafted tokens to host `drafts`.
+ * Synchronises `stream` (the walk needs the copied values). */
+int dflash2_propose_greedy(const struct dflash_model *m, const dflash2_selector *sel, const float *draft_logits,
+                           const float *hidden, int32_t b, int32_t anchor, int32_t *drafts, void *ws, size_t ws_bytes,
+                           void *stream);
 
 #ifdef __cplusplus
 }
