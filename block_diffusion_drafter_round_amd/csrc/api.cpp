@@ -17,6 +17,7 @@
 #include "dflash.h"
 #include "dflash_policy.h"
 #include "dflash_prof.h"
+#include "batch.h"
 #include "kernels.h"
 #include "sround.h"
 
@@ -209,9 +210,45 @@ int check_kv(const dflash_model *m, const dflash_kv *kv) {
     if (!aligned(kv->k, 16) || !aligned(kv->v, 16)) return fail(DFLASH_E_INVAL, "kv->k / kv->v null or not 16-byte aligned");
     if (kv->capacity <= 0 || kv->capacity % 64) return fail(DFLASH_E_INVAL, "kv capacity %d must be a positive multiple of 64", kv->capacity);
     if (kv->len < 0 || kv->len > kv->capacity) return fail(DFLASH_E_INVAL, "kv len %d outside [0, capacity]", kv->len);
-    (void)m;
+    if (kv->ctx_cap < 0) return fail(DFLASH_E_INVAL, "kv ctx_cap %d is negative", kv->ctx_cap);
+    if (kv->page_rows < 0) return fail(DFLASH_E_INVAL, "kv page_rows %d is negative", kv->page_rows);
+    if (kv->page_rows > 0) {
+        if (kv->page_rows % 64 || kv->capacity % kv->page_rows)
+            return fail(DFLASH_E_INVAL, "kv page_rows %d must be a multiple of 64 that divides capacity %d", kv->page_rows,
+                        kv->capacity);
+        if (kv->pool_pages < 1) return fail(DFLASH_E_INVAL, "paged kv needs pool_pages >= 1");
+        if (!aligned(kv->block_table, 4)) return fail(DFLASH_E_INVAL, "paged kv needs a block table");
+        const size_t pool = (size_t)kv->pool_pages * m->cfg.n_kv_heads * kv->page_rows * m->cfg.head_dim;
+        if (pool * 4 > ((size_t)1 << 40)) return fail(DFLASH_E_INVAL, "paged kv pool of %d pages is too large", kv->pool_pages);
+    }
     return DFLASH_OK;
 }
+
+// the kernels' view of a cache (kvview.h): a contiguous cache is one page
+dfl::KvView kv_view(const dflash_model *m, const dflash_kv *kv) {
+    const dflash_cfg &c = m->cfg;
+    dfl::KvView v{};
+    v.k = static_cast<char *>(kv->k);
+    v.v = static_cast<char *>(kv->v);
+    v.esize = (int)kv_elem(c);
+    if (kv->page_rows > 0) {
+        v.page_rows = kv->page_rows;
+        v.pool_pages = kv->pool_pages;
+        v.table = kv->block_table;
+    } else {
+        v.page_rows = kv->capacity;
+        v.pool_pages = 1;
+        v.table = nullptr;
+    }
+    v.lstride = (long long)v.pool_pages * c.n_kv_heads * v.page_rows * c.head_dim * v.esize;
+    return v;
+}
+
+// first committed row a round attends ([atlas dflash_head] "dflash_ctx_cap")
+int window_lo(const dflash_kv *kv) { return kv->ctx_cap > 0 && kv->len > kv->ctx_cap ? kv->len - kv->ctx_cap : 0; }
+
+// a cache the persistent round kernel cannot serve: paged, or with a window
+bool needs_layered(const dflash_kv *kv) { return kv->page_rows > 0 || kv->ctx_cap > 0; }
 
 int check_ws(const dflash_model *m, void *ws, size_t ws_bytes, int rows) {
     if (!aligned(ws, 256)) return fail(DFLASH_E_INVAL, "workspace null or not 256-byte aligned");
@@ -274,14 +311,11 @@ hipError_t run_ingest(const dflash_model *m, dflash_kv *kv, const float *feats, 
         }
         if (e != hipSuccess) return e;
         dfl::RopeArgs r{};
-        r.src = kvbuf; r.ld = nl * 2 * kvd; r.lstride = 2 * kvd; r.nl = nl;
-        for (int i = 0; i < nl; ++i) {
-            r.g_k[i] = m->layers[l0 + i].g_k;
-            r.kc[i] = layer_ptr(kv->k, c, kv->capacity, l0 + i);
-            r.vc[i] = layer_ptr(kv->v, c, kv->capacity, l0 + i);
-        }
+        r.src = kvbuf; r.ld = nl * 2 * kvd; r.lstride = 2 * kvd; r.nl = nl; r.layer0 = l0;
+        for (int i = 0; i < nl; ++i) r.g_k[i] = m->layers[l0 + i].g_k;
+        r.kv = kv_view(m, kv);
         r.pos = pos; r.rows = t; r.nkv = c.n_kv_heads; r.d = c.head_dim; r.eps = c.rms_eps;
-        r.mscale = (float)m->mscale; r.cap = kv->capacity; r.row0 = kv->len; r.kv_f32 = c.kv_dtype == DFLASH_F32;
+        r.mscale = (float)m->mscale; r.row0 = kv->len; r.kv_f32 = c.kv_dtype == DFLASH_F32;
         memcpy(r.inv_freq, m->inv_freq, sizeof r.inv_freq);
         {
             ProfScope p(DFLASH_K_ROPE, s);
@@ -396,11 +430,166 @@ hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *no
     return hipSuccess;
 }
 
+// ---- the layered round path (batched sequences, paged or windowed caches) ----
+
+struct BatchLayout {
+    size_t x, xn, qkv, q, po, pml, attn, z, bytes;
+};
+
+// buffers of the layered path for up to S sequences of MAX_BLOCK rows,
+// relative to the start of its region
+BatchLayout batch_layout(const dflash_cfg &c, int S) {
+    const size_t rows = (size_t)S * MAX_BLOCK, H = c.hidden, qd = (size_t)c.n_q_heads * c.head_dim;
+    const size_t kvd = (size_t)c.n_kv_heads * c.head_dim, G = (size_t)(c.n_q_heads / c.n_kv_heads);
+    BatchLayout B{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    B.x = take(4 * rows * H);
+    B.xn = take(4 * rows * H);
+    B.qkv = take(4 * rows * (qd + 2 * kvd));
+    B.q = take(2 * (size_t)S * c.n_kv_heads * G * 16 * c.head_dim);
+    B.po = take(4 * (size_t)dfl::BATCH_MAX_ITEMS * G * 16 * c.head_dim);
+    B.pml = take(4 * (size_t)dfl::BATCH_MAX_ITEMS * G * 16 * 2);
+    B.attn = take(4 * rows * qd);
+    B.z = take(4 * rows * c.intermediate);
+    B.bytes = off;
+    return B;
+}
+
+int check_layered(const dflash_model *m, int S) {
+    const dflash_cfg &c = m->cfg;
+    if (c.kv_dtype != DFLASH_BF16)
+        return fail(DFLASH_E_UNSUPPORTED, "the layered round (batched, paged or windowed caches) needs a bf16 KV cache");
+    if (c.d2_groups > 0)
+        return fail(DFLASH_E_UNSUPPORTED, "the layered round (batched, paged or windowed caches) has no DFlash2 conv wrap");
+    if (S < 1 || S > dfl::BATCH_MAX_SEQ) return fail(DFLASH_E_INVAL, "n_seqs %d outside [1, %d]", S, dfl::BATCH_MAX_SEQ);
+    if (S * c.n_kv_heads > dfl::BATCH_MAX_ITEMS)
+        return fail(DFLASH_E_UNSUPPORTED, "%d sequences x %d kv heads exceed %d attention items", S, c.n_kv_heads,
+                    dfl::BATCH_MAX_ITEMS);
+    return DFLASH_OK;
+}
+
+// One round of S sequences through separate kernels; `base` is the offset of
+// the layered path's region in the workspace (after the standard layout).
+hipError_t run_round_layered(const dflash_model *m, const dflash_kv *kvs, int S, const float *noise, const int32_t *pos,
+                             int b, float *out, void *ws, const WsLayout &L, size_t base, hipStream_t s) {
+    const dflash_cfg &c = m->cfg;
+    const BatchLayout B = batch_layout(c, S);
+    const int H = c.hidden, I = c.intermediate, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+    const int M = S * b;
+    float *x = at<float>(ws, base + B.x), *xn = at<float>(ws, base + B.xn), *qkv = at<float>(ws, base + B.qkv);
+    float *attn = at<float>(ws, base + B.attn), *z = at<float>(ws, base + B.z);
+    float *part = at<float>(ws, L.gpart);
+    unsigned *cnt = at<unsigned>(ws, L.gcnt);
+
+    dfl::BatchArgs a{};
+    int nmax = 1;
+    for (int i = 0; i < S; ++i) {
+        a.seq[i].kv = kv_view(m, &kvs[i]);
+        a.seq[i].len = kvs[i].len;
+        a.seq[i].win_lo = window_lo(&kvs[i]);
+        nmax = std::max(nmax, kvs[i].len + b - (a.seq[i].win_lo & ~31));
+    }
+    a.S = S; a.b = b; a.nq = c.n_q_heads; a.nkv = c.n_kv_heads; a.G = c.n_q_heads / c.n_kv_heads; a.d = c.head_dim;
+    a.qd = qd; a.kvd = kvd;
+    a.qkv = qkv; a.qkv_ld = qd + 2 * kvd;
+    a.pos = pos; a.eps = c.rms_eps; a.mscale = (float)m->mscale;
+    a.qscale = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+    memcpy(a.inv_freq, m->inv_freq, sizeof a.inv_freq);
+    a.q = at<uint16_t>(ws, base + B.q);
+    a.po = at<float>(ws, base + B.po);
+    a.pml = at<float>(ws, base + B.pml);
+    a.attn = attn;
+    // key splits: about BATCH_MAX_ITEMS items in all, whole staged chunks per split
+    const int chunk = dfl::BATCH_CHUNK_KEYS;
+    int ns = std::max(1, dfl::BATCH_MAX_ITEMS / (S * c.n_kv_heads));
+    a.kps = std::max(chunk, ((nmax + ns - 1) / ns + chunk - 1) / chunk * chunk);
+    a.nsplit = (nmax + a.kps - 1) / a.kps;
+
+    auto gemm = [&](const float *A, int lda, int K, std::initializer_list<dfl::GemmSeg> segs, float *Y, int ldy, int epi,
+                    int cls) {
+        dfl::GemmArgs g{};
+        g.A = A; g.lda = lda; g.M = M; g.K = K;
+        for (const dfl::GemmSeg &sg : segs) g.seg[g.nseg++] = sg;
+        g.Y = Y; g.ldy = ldy; g.epi = epi; g.wtype = wtype(c);
+        ProfScope p(cls, s);
+        return dfl::gemm(g, part, cnt, s);
+    };
+    hipError_t e = hipMemcpyAsync(x, noise, sizeof(float) * (size_t)M * H, hipMemcpyDeviceToDevice, s);
+    for (int l = 0; l < c.n_layers && e == hipSuccess; ++l) {
+        const dflash_layer_weights &W = m->layers[l];
+        a.layer = l;
+        a.g_q = W.g_q;
+        a.g_k = W.g_k;
+        {
+            ProfScope p(DFLASH_K_NORM, s);
+            e = dfl::rmsnorm(x, H, W.g_in, xn, H, nullptr, M, H, c.rms_eps, s);
+        }
+        if (e == hipSuccess)
+            e = gemm(xn, H, H, {seg(W.wq, qd), seg(W.wk, kvd), seg(W.wv, kvd)}, qkv, qd + 2 * kvd, dfl::EPI_STORE,
+                     DFLASH_K_GEMM_QKV);
+        if (e == hipSuccess) {
+            ProfScope p(DFLASH_K_ROPE, s);
+            e = dfl::batch_qk_rope_launch(a, s);
+        }
+        if (e == hipSuccess) {
+            ProfScope p(DFLASH_K_ATTN, s);
+            e = dfl::batch_attn_launch(a, s);
+        }
+        if (e == hipSuccess) e = gemm(attn, qd, qd, {seg(W.wo, H)}, x, H, dfl::EPI_ADD, DFLASH_K_GEMM_O);
+        if (e == hipSuccess) {
+            ProfScope p(DFLASH_K_NORM, s);
+            e = dfl::rmsnorm(x, H, W.g_post, xn, H, nullptr, M, H, c.rms_eps, s);
+        }
+        if (e == hipSuccess) e = gemm(xn, H, H, {seg(W.wg, I), seg(W.wu, I)}, z, I, dfl::EPI_SWIGLU, DFLASH_K_GEMM_GATEUP);
+        if (e == hipSuccess) e = gemm(z, I, I, {seg(W.wd, H)}, x, H, dfl::EPI_ADD, DFLASH_K_GEMM_DOWN);
+    }
+    if (e == hipSuccess) {
+        ProfScope p(DFLASH_K_NORM, s);
+        e = dfl::rmsnorm(x, H, m->w.g_norm, out, H, nullptr, M, H, c.rms_eps, s);
+    }
+    return e;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char *dflash_last_error(void) { return g_err.c_str(); }
+
+size_t dflash_batch_workspace_bytes(const dflash_model *m, int32_t n_seqs, int32_t max_rows) {
+    if (!m || n_seqs < 1 || n_seqs > dfl::BATCH_MAX_SEQ || max_rows < 0) return 0;
+    return ws_layout(m->cfg, max_rows).total + batch_layout(m->cfg, n_seqs).bytes;
+}
+
+int dflash_forward_round_batch(const dflash_model *m, dflash_kv *kvs, int32_t n_seqs, const float *noise_emb,
+                               const int32_t *pos_block, int32_t b, float *out, void *ws, size_t ws_bytes,
+                               void *stream) {
+    g_err.clear();
+    if (!m) return fail(DFLASH_E_INVAL, "model is null");
+    if (!kvs) return fail(DFLASH_E_INVAL, "kvs is null");
+    int rc = check_layered(m, n_seqs);
+    if (rc) return rc;
+    if (b < 1 || b > MAX_BLOCK) return fail(DFLASH_E_INVAL, "block size b = %d outside [1, 16]", b);
+    for (int i = 0; i < n_seqs; ++i) {
+        if ((rc = check_kv(m, &kvs[i]))) return fail(rc, "sequence %d: %s", i, g_err.c_str());
+        if ((int64_t)kvs[i].len + b > kvs[i].capacity)
+            return fail(DFLASH_E_CAPACITY, "sequence %d: len %d + b %d exceeds capacity %d", i, kvs[i].len, b,
+                        kvs[i].capacity);
+        for (int j = 0; j < i; ++j)
+            if (kvs[j].k == kvs[i].k || kvs[j].v == kvs[i].v)
+                return fail(DFLASH_E_INVAL, "sequences %d and %d share KV storage", j, i);
+    }
+    if (!aligned(noise_emb, 16) || !aligned(out, 16) || !aligned(pos_block, 4))
+        return fail(DFLASH_E_INVAL, "noise_emb / out / pos_block null or misaligned");
+    if (!aligned(ws, 256)) return fail(DFLASH_E_INVAL, "workspace null or not 256-byte aligned");
+    const size_t need = dflash_batch_workspace_bytes(m, n_seqs, 0);
+    if (ws_bytes < need)
+        return fail(DFLASH_E_INVAL, "workspace of %zu bytes is smaller than the %zu the batched round needs", ws_bytes, need);
+    const WsLayout L = ws_layout(m->cfg, 0);
+    hipError_t e = run_round_layered(m, kvs, n_seqs, noise_emb, pos_block, b, out, ws, L, L.total, (hipStream_t)stream);
+    return e == hipSuccess ? DFLASH_OK : hip_fail(e, "forward_round_batch");
+}
 
 int dflash_load_weights(const dflash_cfg *cfg, const dflash_weights *w, dflash_model **out) {
     g_err.clear();
@@ -543,6 +732,17 @@ int dflash_forward_round(const dflash_model *m, dflash_kv *kv, const float *nois
         return fail(DFLASH_E_CAPACITY, "len %d + b %d exceeds capacity %d", kv->len, b, kv->capacity);
     if (!aligned(noise_emb, 16) || !aligned(out, 16) || !aligned(pos_block, 4))
         return fail(DFLASH_E_INVAL, "noise_emb / out / pos_block null or misaligned");
+    if (needs_layered(kv)) {
+        // paged or windowed cache: the layered path with one sequence
+        if ((rc = check_layered(m, 1))) return rc;
+        if (!aligned(ws, 256)) return fail(DFLASH_E_INVAL, "workspace null or not 256-byte aligned");
+        const size_t need = dflash_batch_workspace_bytes(m, 1, 0);
+        if (ws_bytes < need)
+            return fail(DFLASH_E_INVAL, "a paged or windowed cache needs a workspace of %zu bytes, got %zu", need, ws_bytes);
+        const WsLayout L = ws_layout(m->cfg, 0);
+        hipError_t e = run_round_layered(m, kv, 1, noise_emb, pos_block, b, out, ws, L, L.total, (hipStream_t)stream);
+        return e == hipSuccess ? DFLASH_OK : hip_fail(e, "forward_round");
+    }
     if ((rc = check_ws(m, ws, ws_bytes, 0)) || (rc = check_packed(m))) return rc;
     hipError_t e = run_round(m, kv, noise_emb, pos_block, b, out, ws, ws_layout(m->cfg, 0), (hipStream_t)stream);
     return e == hipSuccess ? DFLASH_OK : hip_fail(e, "forward_round");
@@ -560,7 +760,17 @@ int dflash_forward_full(const dflash_model *m, const float *taps, const float *n
         return fail(DFLASH_E_CAPACITY, "n %d + b %d exceeds scratch capacity %d", n, b, scratch->capacity);
     if ((n > 0 && !aligned(taps, 16)) || !aligned(noise_emb, 16) || !aligned(out, 16) || !aligned(pos, 4))
         return fail(DFLASH_E_INVAL, "taps / noise_emb / out / pos null or misaligned");
-    if ((rc = check_ws(m, ws, ws_bytes, n)) || (rc = check_packed(m))) return rc;
+    if (scratch->ctx_cap != 0) return fail(DFLASH_E_INVAL, "the first-light forward attends every row: scratch ctx_cap must be 0");
+    const bool layered = needs_layered(scratch);
+    if (layered) {
+        if ((rc = check_layered(m, 1))) return rc;
+        if (!aligned(ws, 256)) return fail(DFLASH_E_INVAL, "workspace null or not 256-byte aligned");
+        const size_t need = dflash_batch_workspace_bytes(m, 1, n);
+        if (ws_bytes < need)
+            return fail(DFLASH_E_INVAL, "a paged scratch cache needs a workspace of %zu bytes, got %zu", need, ws_bytes);
+    } else if ((rc = check_ws(m, ws, ws_bytes, n)) || (rc = check_packed(m))) {
+        return rc;
+    }
     const WsLayout L = ws_layout(m->cfg, n);
     hipStream_t s = (hipStream_t)stream;
     float *feats = at<float>(ws, L.feats);
@@ -572,7 +782,10 @@ int dflash_forward_full(const dflash_model *m, const float *taps, const float *n
         if (e == hipSuccess) e = run_ingest(m, &kv, feats, pos, n, ws, L, s);
         kv.len = n;
     }
-    if (e == hipSuccess) e = run_round(m, &kv, noise_emb, pos + n, b, out, ws, L, s);
+    if (e == hipSuccess) {
+        if (layered) e = run_round_layered(m, &kv, 1, noise_emb, pos + n, b, out, ws, L, L.total, s);
+        else e = run_round(m, &kv, noise_emb, pos + n, b, out, ws, L, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "forward_full");
     scratch->len = n;
     return DFLASH_OK;

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kvview.h"
+
 namespace dfl {
 
 // ---- skinny GEMM:  Y[M, N] (epi)= A[M, K] . W[N, K]^T  ---------------------
@@ -72,13 +74,13 @@ struct RopeArgs {
     const float *src; int ld;     // [rows, ld] projection output; layer i's k heads start at
     int lstride;                  // column i * lstride, its v heads kvd = nkv * d further on
     int nl;                       // layers in this launch (<= ROPE_MAX_LAYERS)
+    int layer0;                   // cache layer of launch layer 0
     const float *g_k[ROPE_MAX_LAYERS];
-    void *kc[ROPE_MAX_LAYERS];    // layer i's K [nkv][cap][d] and V [nkv][d][cap]
-    void *vc[ROPE_MAX_LAYERS];
+    KvView kv;                    // the cache (contiguous or paged)
     const int32_t *pos;
     int rows, nkv, d;
     float eps; float mscale;
-    int cap; int row0;            // cache rows row0 .. row0 + rows - 1
+    int row0;                     // cache rows row0 .. row0 + rows - 1
     int kv_f32;                   // 1: f32 cache, 0: bf16 cache
     double inv_freq[MAX_HALF_DIM];
 };

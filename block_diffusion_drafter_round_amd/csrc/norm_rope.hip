@@ -13,8 +13,9 @@
 // * Each wave then takes heads in turn.  Lane j < d/2 holds the rope pair
 //   (j, j + d/2) of one head: one wave-wide sum of squares gives the head's
 //   RMS, and the rotation is lane-local.
-// * k and v go to the layer's cache at rows row0 + r: K [nkv][cap][d],
-//   V transposed [nkv][d][cap].
+// * k and v go to the layer's cache at rows row0 + r (kvview.h: K
+//   [page][nkv][P][d], V transposed [page][nkv][d][P]; a contiguous cache
+//   is one page of P = capacity rows).
 #include "common.h"
 #include "kernels.h"
 
@@ -52,9 +53,9 @@ hipError_t rmsnorm(const float *x, int ldx, const float *g, float *y, int ldy, f
     return hipGetLastError();
 }
 
-__device__ __forceinline__ void store_kv(void *base, size_t idx, float v, int kv_f32) {
-    if (kv_f32) reinterpret_cast<float *>(base)[idx] = v;
-    else reinterpret_cast<uint16_t *>(base)[idx] = (uint16_t)f32_to_bf16_bits(v);
+__device__ __forceinline__ void store_kv(char *p, float v, int kv_f32) {
+    if (kv_f32) *reinterpret_cast<float *>(p) = v;
+    else *reinterpret_cast<uint16_t *>(p) = (uint16_t)f32_to_bf16_bits(v);
 }
 
 __global__ __launch_bounds__(256) void kv_norm_rope_kernel(RopeArgs a) {
@@ -72,11 +73,12 @@ __global__ __launch_bounds__(256) void kv_norm_rope_kernel(RopeArgs a) {
 
     const float *row = a.src + (size_t)r * a.ld + (size_t)l * a.lstride;
     const float *gain = a.g_k[l];
-    void *kc = a.kc[l], *vc = a.vc[l];
+    char *kc = a.kv.k + (size_t)(a.layer0 + l) * a.kv.lstride, *vc = a.kv.v + (size_t)(a.layer0 + l) * a.kv.lstride;
     const int kvd = a.nkv * a.d;
     const bool act = lane < half;
     const float c = act ? cs[lane] : 0.f, s = act ? sn[lane] : 0.f;
-    const size_t crow = (size_t)(a.row0 + r);
+    const int crow = a.row0 + r;
+    const int page = kv_page(a.kv, crow);
 
     for (int h = wave; h < 2 * a.nkv; h += 4) {
         if (h < a.nkv) {
@@ -88,15 +90,14 @@ __global__ __launch_bounds__(256) void kv_norm_rope_kernel(RopeArgs a) {
                 const float y0 = gain[lane] * (x0 * inv), y1 = gain[lane + half] * (x1 * inv);
                 const float o0 = (y0 * c - y1 * s) * a.mscale;
                 const float o1 = (y1 * c + y0 * s) * a.mscale;
-                const size_t base = ((size_t)h * a.cap + crow) * a.d;
-                store_kv(kc, base + lane, o0, a.kv_f32);
-                store_kv(kc, base + lane + half, o1, a.kv_f32);
+                store_kv(kc + kv_k_off(a.kv, page, a.nkv, h, crow, a.d, lane), o0, a.kv_f32);
+                store_kv(kc + kv_k_off(a.kv, page, a.nkv, h, crow, a.d, lane + half), o1, a.kv_f32);
             }
         } else if (act) {
             const int hh = h - a.nkv;
             const float *src = row + kvd + hh * a.d;
-            store_kv(vc, ((size_t)hh * a.d + lane) * a.cap + crow, src[lane], a.kv_f32);
-            store_kv(vc, ((size_t)hh * a.d + lane + half) * a.cap + crow, src[lane + half], a.kv_f32);
+            store_kv(vc + kv_v_off(a.kv, page, a.nkv, hh, crow, a.d, lane), src[lane], a.kv_f32);
+            store_kv(vc + kv_v_off(a.kv, page, a.nkv, hh, crow, a.d, lane + half), src[lane + half], a.kv_f32);
         }
     }
 }

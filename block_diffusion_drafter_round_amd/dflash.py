@@ -10,6 +10,7 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,7 +60,9 @@ class dflash2_selector(C.Structure):
 
 
 class dflash_kv(C.Structure):
-    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("capacity", C.c_int32), ("len", C.c_int32)]
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("capacity", C.c_int32), ("len", C.c_int32),
+                ("page_rows", C.c_int32), ("pool_pages", C.c_int32), ("block_table", C.c_void_p),
+                ("ctx_cap", C.c_int32)]
 
 
 _lib = None
@@ -69,7 +72,8 @@ EXPORTS = ("dflash_load_weights", "dflash_free", "dflash_workspace_bytes", "dfla
            "dflash_prof_trace", "dflash_prof_trace_read", "dflash_packed_bytes", "dflash_pack_weights",
            "dflash_ctx_features_noalloc", "dflash_accept_prefix", "dflash_rejection_accept_len",
            "dflash_confidence_vt", "dflash_slot_confidence_vt", "dflash2_walk_greedy", "dflash2_walk_sampled",
-           "dflash2_propose_prepare", "dflash2_propose_greedy")
+           "dflash2_propose_prepare", "dflash2_propose_greedy", "dflash_batch_workspace_bytes",
+           "dflash_forward_round_batch")
 
 # kernel classes of the measurement hook (include/dflash_prof.h)
 K_GEMM_FC, K_GEMM_KV, K_GEMM_QKV, K_GEMM_O, K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN, K_ROPE, K_NORM, K_ROUND = range(1, 11)
@@ -90,6 +94,9 @@ def lib():
     L.dflash_workspace_bytes.argtypes = [vp, i32]
     L.dflash_workspace_bytes.restype = sz
     L.dflash_packed_bytes.argtypes = [vp]
+    L.dflash_batch_workspace_bytes.argtypes = [vp, i32, i32]
+    L.dflash_batch_workspace_bytes.restype = sz
+    L.dflash_forward_round_batch.argtypes = [vp, C.POINTER(dflash_kv), i32, vp, vp, i32, vp, vp, sz, vp]
     L.dflash_packed_bytes.restype = sz
     L.dflash_pack_weights.argtypes = [vp, vp, sz, vp]
     L.dflash_ctx_features.argtypes = [vp, vp, i32, vp, vp, sz, vp]
@@ -115,7 +122,8 @@ def lib():
     L.dflash2_propose_greedy.argtypes = [vp, C.POINTER(dflash2_selector), vp, vp, i32, i32, pi32, vp, sz, vp]
     L.dflash_prof_trace_read.argtypes = [vp, vp, sz, C.POINTER(C.c_uint64), i32, vp]
     for name in EXPORTS:
-        if name not in ("dflash_free", "dflash_workspace_bytes", "dflash_last_error", "dflash_packed_bytes"):
+        if name not in ("dflash_free", "dflash_workspace_bytes", "dflash_last_error", "dflash_packed_bytes",
+                        "dflash_batch_workspace_bytes"):
             getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -187,6 +195,25 @@ def dflash_ingest_ctx(model, kv: dflash_kv, feats, pos_new, t, ws, ws_bytes, str
 def dflash_forward_round(model, kv: dflash_kv, noise_emb, pos_block, b, out, ws, ws_bytes, stream=None) -> None:
     _check(lib().dflash_forward_round(model, C.byref(kv), _ptr(noise_emb), _ptr(pos_block), b, _ptr(out),
                                       _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dflash_batch_workspace_bytes(model: int, n_seqs: int, max_rows: int = 0) -> int:
+    return int(lib().dflash_batch_workspace_bytes(model, n_seqs, max_rows))
+
+
+def dflash_forward_round_batch(model, kvs, noise_emb, pos_block, b, out, ws, ws_bytes, stream=None) -> None:
+    """kvs: a ctypes array of dflash_kv (see kv_array)."""
+    _check(lib().dflash_forward_round_batch(model, kvs, len(kvs), _ptr(noise_emb), _ptr(pos_block), b, _ptr(out),
+                                            _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def kv_array(caches):
+    """A ctypes array of the caches' dflash_kv structs (copies; write the
+    lens back with sync_lens if a call changes them)."""
+    arr = (dflash_kv * len(caches))()
+    for i, c in enumerate(caches):
+        arr[i] = c.c
+    return arr
 
 
 def dflash_forward_full(model, taps, noise_emb, pos, n, b, out, scratch: dflash_kv, ws, ws_bytes,
@@ -430,6 +457,51 @@ class KVCache:
                 self.v[layer, :, :, start:stop].permute(2, 0, 1))
 
 
+class PagedKVCache(KVCache):
+    """Paged storage for one dflash_kv: K [L][pages][nkv][P][d], V
+    [L][pages][nkv][d][P], a device block table mapping logical page i to
+    physical page table[i] (by default a fixed seeded permutation of the
+    pool, so logical order and storage order differ)."""
+
+    def __init__(self, cfg, capacity: int, page_rows: int = 64, pool_pages: int | None = None, device="cuda",
+                 table=None, seed: int = 0):
+        import numpy as np
+        dt = torch.float32 if cfg.kv_dtype == "f32" else torch.bfloat16
+        L, h, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+        npg = capacity // page_rows
+        pool = pool_pages if pool_pages is not None else npg
+        self.page_rows, self.pool_pages = page_rows, pool
+        self.k = torch.zeros((max(L, 1), pool, h, page_rows, d), dtype=dt, device=device)
+        self.v = torch.zeros((max(L, 1), pool, h, d, page_rows), dtype=dt, device=device)
+        if table is None:
+            table = np.random.default_rng(seed).permutation(pool)[:npg]
+        self.table_host = np.asarray(table, dtype=np.int32)
+        self.table = torch.from_numpy(self.table_host.copy()).to(device)
+        self.c = dflash_kv(self.k.data_ptr(), self.v.data_ptr(), capacity, 0, page_rows, pool, self.table.data_ptr(), 0)
+
+    def _locate(self, start: int, stop: int):
+        rows = np.arange(start, stop)
+        return self.table_host[rows // self.page_rows], rows % self.page_rows
+
+    def prefill(self, k_stored, v_stored) -> None:
+        rows = k_stored.shape[2]
+        k = _to_device(k_stored, self.k.device).view(self.k.dtype)
+        v = _to_device(v_stored, self.k.device).view(self.v.dtype)
+        pg, off = self._locate(0, rows)
+        pg_t = torch.from_numpy(pg).to(self.k.device)
+        off_t = torch.from_numpy(off).to(self.k.device)
+        # [L][h][rows][d] -> K[l][page][h][off][d], V[l][page][h][d][off]
+        self.k[:, pg_t, :, off_t, :] = k.permute(2, 0, 1, 3)
+        self.v[:, pg_t, :, :, off_t] = v.permute(2, 0, 1, 3)
+        self.c.len = rows
+
+    def rows(self, layer: int, start: int, stop: int):
+        pg, off = self._locate(start, stop)
+        pg_t = torch.from_numpy(pg).to(self.k.device)
+        off_t = torch.from_numpy(off).to(self.k.device)
+        return self.k[layer, pg_t, :, off_t, :], self.v[layer, pg_t, :, :, off_t]
+
+
 class Drafter:
     """A loaded model plus one workspace; wraps the five calls with torch
     tensors.  The caller supplies KV storage (:class:`KVCache`)."""
@@ -444,14 +516,21 @@ class Drafter:
         self.packed = torch.empty(max(self.packed_bytes, 256), dtype=torch.uint8, device=self.device)
         dflash_pack_weights(self.model, self.packed, self.packed_bytes)
         self.max_rows = 0
+        self.batch_seqs = 0
         self.ws = None
         self.ensure_rows(max_rows)
 
+    def _realloc(self, rows: int, seqs: int):
+        """A fresh zero-filled workspace for `rows` ctx rows and, with
+        seqs > 0, the layered path for `seqs` sequences."""
+        self.max_rows, self.batch_seqs = rows, seqs
+        self.ws_bytes = (dflash_batch_workspace_bytes(self.model, seqs, rows) if seqs
+                         else dflash_workspace_bytes(self.model, rows))
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=self.device)
+
     def ensure_rows(self, rows: int):
         if rows > self.max_rows or self.ws is None:
-            self.ws_bytes = dflash_workspace_bytes(self.model, rows)
-            self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=self.device)
-            self.max_rows = rows
+            self._realloc(rows, self.batch_seqs)
 
     def __del__(self):
         try:
@@ -480,15 +559,33 @@ class Drafter:
     def forward_round(self, kv: KVCache, noise_emb: torch.Tensor, pos_block: torch.Tensor,
                       out: torch.Tensor | None = None) -> torch.Tensor:
         b = noise_emb.shape[0]
+        if kv.c.page_rows or kv.c.ctx_cap:
+            self.ensure_batch(1)
         if out is None:
             out = torch.empty((b, self.cfg.hidden), dtype=torch.float32, device=self.device)
         dflash_forward_round(self.model, kv.c, noise_emb, pos_block, b, out, self.ws, self.ws_bytes)
+        return out
+
+    def ensure_batch(self, n_seqs: int):
+        """Grow the workspace to serve the layered path (batched rounds,
+        paged or windowed caches) for up to n_seqs sequences."""
+        if n_seqs > self.batch_seqs:
+            self._realloc(self.max_rows, n_seqs)
+
+    def forward_round_batch(self, caches, noise_emb: torch.Tensor, pos_block: torch.Tensor) -> torch.Tensor:
+        """noise_emb [S, b, H], pos_block [S, b] -> out [S, b, H]."""
+        S, b = noise_emb.shape[0], noise_emb.shape[1]
+        self.ensure_batch(S)
+        out = torch.empty((S, b, self.cfg.hidden), dtype=torch.float32, device=self.device)
+        dflash_forward_round_batch(self.model, kv_array(caches), noise_emb, pos_block, b, out, self.ws, self.ws_bytes)
         return out
 
     def forward_full(self, taps: torch.Tensor, noise_emb: torch.Tensor, pos: torch.Tensor,
                      scratch: KVCache | None = None) -> torch.Tensor:
         n, b = taps.shape[0], noise_emb.shape[0]
         self.ensure_rows(n)
+        if scratch is not None and scratch.c.page_rows:
+            self.ensure_batch(1)
         if scratch is None:
             scratch = KVCache(self.cfg, max(64, (n + b + 63) // 64 * 64), self.device)
         out = torch.empty((b, self.cfg.hidden), dtype=torch.float32, device=self.device)

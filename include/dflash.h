@@ -148,18 +148,44 @@ typedef struct dflash_weights {
 /* Draft KV cache ([memra dflash module] "DflashKv"; one per sequence, as
  * [atlas dflash_head] "DflashProposerState").  It holds, per layer, the
  * normed+roped ctx K and the raw ctx V, append-only in committed order.
+ *
+ * Contiguous storage (page_rows = 0):
  *   k: device, [n_layers][n_kv_heads][capacity][head_dim]   (row-major rows)
  *   v: device, [n_layers][n_kv_heads][head_dim][capacity]   (transposed: one
  *      row per head dimension, so that the attention's P.V product streams
  *      contiguous keys)
- * Both are in cfg.kv_dtype.  capacity is a positive multiple of 64.  Rows
- * [0, len) are committed.  forward_round overwrites rows [len, len+b) with
- * the block's K/V while it runs, and never commits them. */
+ *   capacity is a positive multiple of 64.
+ *
+ * Paged storage (page_rows > 0; [atlas dflash_head] "DflashProposerState":
+ * one paged cache per drafter layer, one block table shared by all layers):
+ *   k: device, [n_layers][pool_pages][n_kv_heads][page_rows][head_dim]
+ *   v: device, [n_layers][pool_pages][n_kv_heads][head_dim][page_rows]
+ *   block_table: device int32 [capacity / page_rows]; logical row r lives in
+ *      physical page block_table[r / page_rows], row r % page_rows, of every
+ *      layer.  page_rows is a positive multiple of 64 that divides capacity;
+ *      pool_pages >= 1.  Entries must lie in [0, pool_pages) for every page
+ *      the call touches (the kernels clamp other values into the pool, so a
+ *      bad table gives wrong results, never an access outside it).
+ *
+ * Context window ([atlas dflash_head] "dflash_ctx_cap": the drafter attends
+ * only the most recent target positions): ctx_cap = 0 attends every
+ * committed row; ctx_cap = N > 0 attends committed rows
+ * [max(0, len - N), len) plus the block.  Rows before the window are never
+ * read, so a paged caller may recycle pages that lie wholly before it.
+ *
+ * Both are in cfg.kv_dtype.  Rows [0, len) are committed.  forward_round
+ * overwrites rows [len, len+b) with the block's K/V while it runs, and never
+ * commits them.  A struct with page_rows = ctx_cap = 0 (the zero fill of the
+ * last four fields) is the plain contiguous cache. */
 typedef struct dflash_kv {
     void   *k;
     void   *v;
     int32_t capacity;
     int32_t len;
+    int32_t page_rows;
+    int32_t pool_pages;
+    const int32_t *block_table;
+    int32_t ctx_cap;
 } dflash_kv;
 
 typedef struct dflash_model dflash_model;   /* opaque host handle */
@@ -249,10 +275,44 @@ int dflash_ingest_ctx(const dflash_model *m, dflash_kv *kv, const float *feats,
  *   pos_block: device int32 [b], the block rows' absolute positions.
  *   out      : device f32 [b, hidden], the final normed hidden states (fed to
  *              the target's lm_head by the caller).
- * 1 <= b <= 16.  DFLASH_E_CAPACITY if kv->len + b > kv->capacity. */
+ * 1 <= b <= 16.  DFLASH_E_CAPACITY if kv->len + b > kv->capacity.
+ * A paged or windowed cache (page_rows or ctx_cap set) runs the layered
+ * path of dflash_forward_round_batch with one sequence, so `ws` must then
+ * hold dflash_batch_workspace_bytes(m, 1, 0) bytes; a plain contiguous
+ * cache runs the persistent round kernel. */
 int dflash_forward_round(const dflash_model *m, dflash_kv *kv, const float *noise_emb,
                          const int32_t *pos_block, int32_t b, float *out,
                          void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of device workspace for the layered round path: calls of
+ * dflash_forward_round_batch over up to n_seqs sequences, and calls on a
+ * paged or windowed cache (n_seqs = 1), that also process up to max_rows
+ * ctx rows at once (as dflash_workspace_bytes).  It is
+ * dflash_workspace_bytes(m, max_rows) plus the stacked block rows' buffers
+ * and the attention partials.  Such a workspace serves every other call
+ * too.  Returns 0 for n_seqs outside [1, 8] or max_rows < 0. */
+size_t dflash_batch_workspace_bytes(const dflash_model *m, int32_t n_seqs, int32_t max_rows);
+
+/* Batched round: one drafting round of n_seqs independent sequences, each
+ * over its own draft KV cache ([atlas dflash_head] "DflashProposerState"),
+ * with the same result per sequence as n_seqs forward_round calls.  The
+ * sequences' n_seqs * b block rows go through every projection together,
+ * so each layer's weights are read once per call instead of once per
+ * sequence.  The steps are separate kernels (RMSNorm, the projections,
+ * q/k head-norm + rope + block K/V stores, split-K attention, split merge).
+ *   kvs       : host array of n_seqs caches (distinct storage; contiguous or
+ *               paged, with or without a window); lens unchanged.
+ *   noise_emb : device f32 [n_seqs][b][hidden].
+ *   pos_block : device int32 [n_seqs][b].
+ *   out       : device f32 [n_seqs][b][hidden].
+ *   ws        : >= dflash_batch_workspace_bytes(m, n_seqs, 0) bytes, 256-byte
+ *               aligned (zero-filled once, like every workspace).
+ * 1 <= n_seqs <= 8, 1 <= b <= 16.  DFLASH_E_UNSUPPORTED for an f32 KV cache
+ * or a model with the DFlash2 conv wrap.  No grid-wide barriers: unlike
+ * forward_round, it may share the device with other work. */
+int dflash_forward_round_batch(const dflash_model *m, dflash_kv *kvs, int32_t n_seqs, const float *noise_emb,
+                               const int32_t *pos_block, int32_t b, float *out, void *ws, size_t ws_bytes,
+                               void *stream);
 
 /* First-light forward ([DflashDraft] "forward"): full non-causal attention
  * over [ctx features ; block], with no persistent cache.  It runs
@@ -262,7 +322,10 @@ int dflash_forward_round(const dflash_model *m, dflash_kv *kv, const float *nois
  *   taps: device f32 [n, n_taps*hidden]; noise_emb: device f32 [b, hidden]
  *   pos : device int32 [n + b], the ctx positions, then the block positions.
  *   out : device f32 [b, hidden].
- * n >= 0, 1 <= b <= 16, and n <= the workspace's max_rows. */
+ * n >= 0, 1 <= b <= 16, and n <= the workspace's max_rows.  scratch may be
+ * paged (then ws must hold dflash_batch_workspace_bytes(m, 1, n) bytes); it
+ * must have no window (ctx_cap = 0): the first-light forward attends
+ * everything. */
 int dflash_forward_full(const dflash_model *m, const float *taps, const float *noise_emb,
                         const int32_t *pos, int32_t n, int32_t b, float *out,
                         dflash_kv *scratch, void *ws, size_t ws_bytes, void *stream);

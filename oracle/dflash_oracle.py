@@ -24,10 +24,12 @@ Readings of the pages that the oracle fixes, where the pages leave a step open:
   "k/v projections + k head-norm + rope" and nothing else.
 * R-2: a block row's q, k and v all come from the same normed block row
   (Qwen3 decoder layer).
-* R-3: no mask and no window: every block query attends every ctx key and
-  every block key.  [DflashDraft, ``ctx_features``/``forward``] says "full
+* R-3: no mask: every block query attends every attended ctx key and every
+  block key.  [DflashDraft, ``ctx_features``/``forward``] says "full
   non-causal attention"; [atlas dflash_head, overview] says "bidirectional
-  in-block attention".
+  in-block attention".  No window unless a round is given one
+  ([atlas dflash_head, ``dflash_ctx_cap``]): then only the most recent
+  ctx_cap committed rows are attended; first light has none.
 * R-4: the softmax scale is 1/sqrt(head_dim).  The YaRN mscale multiplies q
   and k after rope ([DflashDraft, ``rope_yarn``]).
 * R-5: q/k head RMSNorm (gain [head_dim], same eps) comes before rope
@@ -52,7 +54,7 @@ import numpy as np
 __all__ = [
     "decode_bf16", "decode_e4m3fn", "decode_matrix", "rope_tables", "rms_norm",
     "apply_rope", "OracleModel", "OracleKV", "ctx_features", "ctx_kv",
-    "ingest_ctx", "attention", "block_layer", "forward_round", "forward_full",
+    "ingest_ctx", "attention", "block_layer", "forward_round", "forward_round_batch", "forward_full",
     "d2_prepare", "d2_finish", "lm_argmax",
 ]
 
@@ -385,17 +387,31 @@ def block_layer(m: OracleModel, layer: int, X: np.ndarray, pos_block: np.ndarray
     return X + y
 
 
-def forward_round(m: OracleModel, kv: OracleKV, noise_emb: np.ndarray, pos_block: np.ndarray) -> np.ndarray:
+def forward_round(m: OracleModel, kv: OracleKV, noise_emb: np.ndarray, pos_block: np.ndarray,
+                  ctx_cap: int = 0) -> np.ndarray:
     """Block forward over the cached ctx K/V (O8, O7).
 
     [DflashDraft, ``forward_round``]: only the block rows are projected per
     layer.  The block K/V land transiently after the cache's ``len`` rows and
     are never committed, so ``kv`` is left unchanged.  Returns the final
-    normed hidden states [b, hidden] for all b rows."""
+    normed hidden states [b, hidden] for all b rows.
+
+    ctx_cap > 0 is the context window of [atlas dflash_head,
+    ``dflash_ctx_cap``]: the block attends only the most recent ctx_cap
+    committed rows, [max(0, len - ctx_cap), len), plus its own rows."""
+    lo = max(0, kv.len - ctx_cap) if ctx_cap > 0 else 0
     X = np.asarray(noise_emb, dtype=np.float64)
     for l in range(m.cfg.n_layers):
-        X = block_layer(m, l, X, pos_block, kv.k[l], kv.v[l])
+        X = block_layer(m, l, X, pos_block, kv.k[l][lo:], kv.v[l][lo:])
     return rms_norm(X, m.g_norm, m.eps)
+
+
+def forward_round_batch(m: OracleModel, kvs, noise_emb, pos_block) -> np.ndarray:
+    """Several sequences' rounds ([atlas dflash_head, ``DflashProposerState``]:
+    per-sequence drafter state): each sequence's round on its own cache, one
+    after another.  noise_emb [S, b, hidden], pos_block [S, b]; returns
+    [S, b, hidden]."""
+    return np.stack([forward_round(m, kv, noise_emb[s], pos_block[s]) for s, kv in enumerate(kvs)])
 
 
 def forward_full(m: OracleModel, taps: np.ndarray, noise_emb: np.ndarray,

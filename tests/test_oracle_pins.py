@@ -413,3 +413,63 @@ def test_p11_argmax_ties_lowest_index():
     am, logits = O.lm_argmax(h, lm)
     assert list(am) == [1, 3]
     assert logits.shape == (2, 4)
+
+
+# ---------------------------------------------------------- context window --
+@pytest.mark.parametrize("cap", [1, 5, 7])
+def test_window_equals_round_over_the_last_rows(cap):
+    """[atlas dflash_head, dflash_ctx_cap]: a window of N rows gives the same
+    result as a plain round over a cache that holds only the last N
+    committed rows (built separately, at their own positions)."""
+    cfg = SMALL
+    m = small_model(cfg)
+    n, b = cfg.ctx, cfg.block
+    taps, noise, pos = synth.make_taps(cfg, n), synth.make_noise(cfg), synth.positions(0, n + b)
+    feats = O.ctx_features(m, taps)
+    full = O.OracleKV(cfg)
+    O.ingest_ctx(m, full, feats, pos[:n])
+    last = O.OracleKV(cfg)
+    O.ingest_ctx(m, last, feats[n - cap:], pos[n - cap:n])
+    win = O.forward_round(m, full, noise, pos[n:], ctx_cap=cap)
+    assert rel(win, O.forward_round(m, last, noise, pos[n:])) <= 1e-13
+    # a window that covers everything changes nothing; a smaller one does
+    assert rel(O.forward_round(m, full, noise, pos[n:], ctx_cap=n), O.forward_round(m, full, noise, pos[n:])) == 0
+    assert rel(win, O.forward_round(m, full, noise, pos[n:])) > 1e-6
+
+
+def test_window_attention_brute_force():
+    """Windowed attention of one query over explicit loops (tiny shapes)."""
+    rng = np.random.default_rng(4)
+    d, nq, nkv, n, b, cap = 4, 2, 1, 6, 2, 3
+    q = rng.standard_normal((b, nq, d))
+    K = rng.standard_normal((n + b, nkv, d))
+    V = rng.standard_normal((n + b, nkv, d))
+    keys = list(range(n - cap, n + b))               # the last cap ctx rows, then the block
+    got = O.attention(q, K[keys], V[keys])
+    for r in range(b):
+        for hq in range(nq):
+            s = [sum(q[r, hq, i] * K[j, 0, i] for i in range(d)) / math.sqrt(d) for j in keys]
+            w = [math.exp(x - max(s)) for x in s]
+            ref = [sum(w[t] * V[j, 0, i] for t, j in enumerate(keys)) / sum(w) for i in range(d)]
+            assert np.allclose(got[r, hq], ref, atol=1e-13)
+
+
+def test_batch_is_independent_rounds():
+    """The batched round is each sequence's own round: permuting the
+    sequences permutes the outputs, and sequence 0 does not depend on the
+    others' caches."""
+    cfg = SMALL
+    m = small_model(cfg)
+    b = cfg.block
+    kvs = []
+    for sidx, n in enumerate((3, 12, 7)):
+        kv = O.OracleKV(cfg)
+        O.ingest_ctx(m, kv, O.ctx_features(m, synth.make_taps(cfg, n, stream=sidx)), synth.positions(0, n))
+        kvs.append(kv)
+    noise = np.stack([synth.make_noise(cfg, stream=s) for s in range(3)])
+    pos = np.stack([synth.positions(n, b) for n in (3, 12, 7)])
+    out = O.forward_round_batch(m, kvs, noise, pos)
+    perm = [2, 0, 1]
+    out_p = O.forward_round_batch(m, [kvs[i] for i in perm], noise[perm], pos[perm])
+    assert np.array_equal(out_p, out[perm])
+    assert np.array_equal(O.forward_round_batch(m, kvs[:1], noise[:1], pos[:1])[0], out[0])
