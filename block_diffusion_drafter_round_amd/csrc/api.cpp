@@ -502,7 +502,7 @@ hipError_t run_round_layered(const dflash_model *m, const dflash_kv *kvs, int S,
     a.attn = attn;
     // key splits: about BATCH_MAX_ITEMS items in all, whole staged chunks per split
     const int chunk = dfl::BATCH_CHUNK_KEYS;
-    int ns = std::max(1, dfl::BATCH_MAX_ITEMS / (S * c.n_kv_heads));
+    int ns = std::max(1, std::min(dfl::BATCH_MAX_SPLITS, dfl::BATCH_MAX_ITEMS / (S * c.n_kv_heads)));
     a.kps = std::max(chunk, ((nmax + ns - 1) / ns + chunk - 1) / chunk * chunk);
     a.nsplit = (nmax + a.kps - 1) / a.kps;
 

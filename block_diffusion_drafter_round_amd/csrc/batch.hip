@@ -222,31 +222,49 @@ __global__ __launch_bounds__(BATCH_ATTN_THREADS) void batch_attn(BatchArgs a) {
     if (g == 0) *reinterpret_cast<float2 *>(a.pml + (item * 16 + n16) * 2) = make_float2(m, l);
 }
 
-// one wave per (stacked row, q head): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// one wave per (stacked row, q head): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Lane i reads split i's (m, l) (nsplit <= 64), so M and L take one load
+// round trip and two wave reductions; the partial O rows are then read 8
+// splits at a time, all loads of a group issued before the first use.
 __global__ __launch_bounds__(256) void batch_merge(BatchArgs a) {
     const int unit = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int rows = a.S * a.b;
     if (unit >= rows * a.nq) return;
     const int row = unit / a.nq, hq = unit - row * a.nq;
     const int s = row / a.b, r = row - s * a.b;
-    const int h = hq / a.G, j = hq - h * a.G, d = a.d;
-    const size_t item0 = (((size_t)s * a.nkv + h) * a.nsplit) * a.G + j;
-    float M = -1e30f;
-    for (int sp = 0; sp < a.nsplit; ++sp) M = fmaxf(M, a.pml[((item0 + (size_t)sp * a.G) * 16 + r) * 2]);
-    float L = 0.f, acc0 = 0.f, acc1 = 0.f;
-    for (int sp = 0; sp < a.nsplit; ++sp) {
-        const size_t it = (item0 + (size_t)sp * a.G) * 16 + r;
-        const float2 ml = *reinterpret_cast<const float2 *>(a.pml + it * 2);
-        const float w = __builtin_amdgcn_exp2f(ml.x - M);
-        L += w * ml.y;
-        const float *po = a.po + it * d;
-        acc0 += w * po[lane];
-        if (d > 64) acc1 += w * po[lane + 64];
+    const int h = hq / a.G, j = hq - h * a.G, d = a.d, ns = a.nsplit;
+    const size_t item0 = (((size_t)s * a.nkv + h) * ns) * a.G + j;     // split sp: item0 + sp * G
+    float2 ml = make_float2(-1e30f, 0.f);
+    if (lane < ns) ml = *reinterpret_cast<const float2 *>(a.pml + ((item0 + (size_t)lane * a.G) * 16 + r) * 2);
+    float M = ml.x;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float w = lane < ns ? __builtin_amdgcn_exp2f(ml.x - M) : 0.f;
+    const float L = wave_sum(w * ml.y);
+    const float *po = a.po + (item0 * 16 + r) * d + lane;
+    const size_t sstride = (size_t)a.G * 16 * d;                       // floats between consecutive splits
+    const bool two = d > 64;
+    float acc0 = 0.f, acc1 = 0.f;
+    constexpr int U = 8;
+    for (int sp0 = 0; sp0 < ns; sp0 += U) {
+        float v0[U], v1[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int sp = min(sp0 + u, ns - 1);
+            v0[u] = po[(size_t)sp * sstride];
+            v1[u] = two ? po[(size_t)sp * sstride + 64] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float ws = sp0 + u < ns ? __shfl(w, sp0 + u, 64) : 0.f;
+            acc0 += ws * v0[u];
+            acc1 += ws * v1[u];
+        }
     }
     float *dst = a.attn + (size_t)row * a.qd + (size_t)hq * d;
     const float il = 1.f / L;
     dst[lane] = acc0 * il;
-    if (d > 64) dst[lane + 64] = acc1 * il;
+    if (two) dst[lane + 64] = acc1 * il;
 }
 
 }  // namespace
