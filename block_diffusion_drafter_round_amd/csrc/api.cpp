@@ -433,7 +433,7 @@ hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *no
 // ---- the layered round path (batched sequences, paged or windowed caches) ----
 
 struct BatchLayout {
-    size_t x, xn, qkv, q, po, pml, attn, z, bytes;
+    size_t x, xn, qkv, q, po, pml, attn, z, xc, y, dc, bytes;
 };
 
 // buffers of the layered path for up to S sequences of MAX_BLOCK rows,
@@ -452,6 +452,11 @@ BatchLayout batch_layout(const dflash_cfg &c, int S) {
     B.pml = take(4 * (size_t)dfl::BATCH_MAX_ITEMS * G * 16 * 2);
     B.attn = take(4 * rows * qd);
     B.z = take(4 * rows * c.intermediate);
+    // DFlash2 conv wrap: the convolved input, the sublayer output, the coefficients
+    const bool d2 = c.d2_groups > 0;
+    B.xc = take(d2 ? 4 * rows * H : 0);
+    B.y = take(d2 ? 4 * rows * H : 0);
+    B.dc = take(d2 ? 4 * rows * 4 * (size_t)c.d2_groups : 0);
     B.bytes = off;
     return B;
 }
@@ -460,8 +465,6 @@ int check_layered(const dflash_model *m, int S) {
     const dflash_cfg &c = m->cfg;
     if (c.kv_dtype != DFLASH_BF16)
         return fail(DFLASH_E_UNSUPPORTED, "the layered round (batched, paged or windowed caches) needs a bf16 KV cache");
-    if (c.d2_groups > 0)
-        return fail(DFLASH_E_UNSUPPORTED, "the layered round (batched, paged or windowed caches) has no DFlash2 conv wrap");
     if (S < 1 || S > dfl::BATCH_MAX_SEQ) return fail(DFLASH_E_INVAL, "n_seqs %d outside [1, %d]", S, dfl::BATCH_MAX_SEQ);
     if (S * c.n_kv_heads > dfl::BATCH_MAX_ITEMS)
         return fail(DFLASH_E_UNSUPPORTED, "%d sequences x %d kv heads exceed %d attention items", S, c.n_kv_heads,
@@ -515,6 +518,15 @@ hipError_t run_round_layered(const dflash_model *m, const dflash_kv *kvs, int S,
         ProfScope p(cls, s);
         return dfl::gemm(g, part, cnt, s);
     };
+    // DFlash2 conv wrap: coefficients of the sublayer's normed input (kept
+    // for its finish conv), and the prepare conv of that input into xc
+    const bool d2 = c.d2_groups > 0;
+    float *xc = at<float>(ws, base + B.xc), *y = at<float>(ws, base + B.y), *dc = at<float>(ws, base + B.dc);
+    auto d2_in = [&](const float *src, const dflash_matrix &w_dyn, const float *wbase) {
+        hipError_t r = dfl::d2_dyn_launch(src, H, w_dyn.data, w_dyn.scale, c.weight_dtype, 4 * c.d2_groups, M, dc, s);
+        if (r == hipSuccess) r = dfl::d2_conv_launch(src, dc, 0, wbase, H, c.d2_groups, b, M, xc, false, s);
+        return r;
+    };
     hipError_t e = hipMemcpyAsync(x, noise, sizeof(float) * (size_t)M * H, hipMemcpyDeviceToDevice, s);
     for (int l = 0; l < c.n_layers && e == hipSuccess; ++l) {
         const dflash_layer_weights &W = m->layers[l];
@@ -525,9 +537,11 @@ hipError_t run_round_layered(const dflash_model *m, const dflash_kv *kvs, int S,
             ProfScope p(DFLASH_K_NORM, s);
             e = dfl::rmsnorm(x, H, W.g_in, xn, H, nullptr, M, H, c.rms_eps, s);
         }
+        // DFlash2: the attention sublayer sees the prepare conv of its normed input
+        if (e == hipSuccess && d2) e = d2_in(xn, W.attn_w_dyn, W.attn_base);
         if (e == hipSuccess)
-            e = gemm(xn, H, H, {seg(W.wq, qd), seg(W.wk, kvd), seg(W.wv, kvd)}, qkv, qd + 2 * kvd, dfl::EPI_STORE,
-                     DFLASH_K_GEMM_QKV);
+            e = gemm(d2 ? xc : xn, H, H, {seg(W.wq, qd), seg(W.wk, kvd), seg(W.wv, kvd)}, qkv, qd + 2 * kvd,
+                     dfl::EPI_STORE, DFLASH_K_GEMM_QKV);
         if (e == hipSuccess) {
             ProfScope p(DFLASH_K_ROPE, s);
             e = dfl::batch_qk_rope_launch(a, s);
@@ -536,13 +550,29 @@ hipError_t run_round_layered(const dflash_model *m, const dflash_kv *kvs, int S,
             ProfScope p(DFLASH_K_ATTN, s);
             e = dfl::batch_attn_launch(a, s);
         }
-        if (e == hipSuccess) e = gemm(attn, qd, qd, {seg(W.wo, H)}, x, H, dfl::EPI_ADD, DFLASH_K_GEMM_O);
+        if (e == hipSuccess) {
+            if (d2) {   // o_proj, then its finish conv into the residual
+                e = gemm(attn, qd, qd, {seg(W.wo, H)}, y, H, dfl::EPI_STORE, DFLASH_K_GEMM_O);
+                if (e == hipSuccess) e = dfl::d2_conv_launch(y, dc, 1, W.attn_base, H, c.d2_groups, b, M, x, true, s);
+            } else {
+                e = gemm(attn, qd, qd, {seg(W.wo, H)}, x, H, dfl::EPI_ADD, DFLASH_K_GEMM_O);
+            }
+        }
         if (e == hipSuccess) {
             ProfScope p(DFLASH_K_NORM, s);
             e = dfl::rmsnorm(x, H, W.g_post, xn, H, nullptr, M, H, c.rms_eps, s);
         }
-        if (e == hipSuccess) e = gemm(xn, H, H, {seg(W.wg, I), seg(W.wu, I)}, z, I, dfl::EPI_SWIGLU, DFLASH_K_GEMM_GATEUP);
-        if (e == hipSuccess) e = gemm(z, I, I, {seg(W.wd, H)}, x, H, dfl::EPI_ADD, DFLASH_K_GEMM_DOWN);
+        if (e == hipSuccess && d2) e = d2_in(xn, W.mlp_w_dyn, W.mlp_base);
+        if (e == hipSuccess)
+            e = gemm(d2 ? xc : xn, H, H, {seg(W.wg, I), seg(W.wu, I)}, z, I, dfl::EPI_SWIGLU, DFLASH_K_GEMM_GATEUP);
+        if (e == hipSuccess) {
+            if (d2) {
+                e = gemm(z, I, I, {seg(W.wd, H)}, y, H, dfl::EPI_STORE, DFLASH_K_GEMM_DOWN);
+                if (e == hipSuccess) e = dfl::d2_conv_launch(y, dc, 1, W.mlp_base, H, c.d2_groups, b, M, x, true, s);
+            } else {
+                e = gemm(z, I, I, {seg(W.wd, H)}, x, H, dfl::EPI_ADD, DFLASH_K_GEMM_DOWN);
+            }
+        }
     }
     if (e == hipSuccess) {
         ProfScope p(DFLASH_K_NORM, s);

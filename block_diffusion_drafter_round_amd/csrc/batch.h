@@ -34,6 +34,12 @@ struct BatchArgs {
 };
 
 hipError_t batch_qk_rope_launch(const BatchArgs &a, hipStream_t s);
+// DFlash2 conv wrap: D[rows][nj] = xn . W_dyn^T (weight type wt), and the
+// two-tap causal conv over each sequence's b rows (dst = or += result)
+hipError_t d2_dyn_launch(const float *xn, int H, const void *w, const float *scale, int wt, int nj, int rows, float *D,
+                         hipStream_t s);
+hipError_t d2_conv_launch(const float *src, const float *D, int half, const float *base, int H, int G, int b, int rows,
+                          float *dst, bool accumulate, hipStream_t s);
 // attention splits, then their merge into a.attn
 hipError_t batch_attn_launch(const BatchArgs &a, hipStream_t s);
 

@@ -17,7 +17,10 @@
 //                  eight waves; wave v computes q head v with MFMA 16x16x32
 //                  bf16 (S^T = K Q^T, online softmax, O^T += V^T P^T) and
 //                  writes the split's partial (m, l, O);
-//   batch_merge    the splits' log-sum-exp merge into the attention output.
+//   batch_merge    the splits' log-sum-exp merge into the attention output;
+//   d2_dyn/d2_conv the DFlash2 conv wrap: the dynamic coefficients of a
+//                  sublayer's normed input, its prepare conv, and its finish
+//                  conv added into the residual stream.
 #include "batch.h"
 #include "common.h"
 
@@ -267,7 +270,65 @@ __global__ __launch_bounds__(256) void batch_merge(BatchArgs a) {
     if (two) dst[lane + 64] = acc1 * il;
 }
 
+// ---- DFlash2 grouped dynamic causal conv ([memra dflash module] "Dflash2Conv";
+// [DflashDraft] "d2_conv_prepare", "d2_conv_finish") --------------------------
+
+// D[row][j] = (xn[row] . W_dyn[j]) * scale[j]: one wave per (row, j); the
+// 4G coefficients of a row are laid out [half][group][tap]
+template <int WT>
+__global__ __launch_bounds__(256) void d2_dyn(const float *xn, int H, const void *w, const float *scale, int nj, int rows,
+                                              float *D) {
+    const int unit = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (unit >= rows * nj) return;
+    const int row = unit / nj, j = unit - row * nj;
+    const float *x = xn + (size_t)row * H;
+    float acc = 0.f;
+    for (int c = lane; c < H; c += 64) {
+        float wv;
+        if constexpr (WT == WT_BF16) wv = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(w)[(size_t)j * H + c]);
+        else if constexpr (WT == WT_FP8) wv = __builtin_amdgcn_cvt_f32_fp8((uint32_t)reinterpret_cast<const uint8_t *>(w)[(size_t)j * H + c], 0);
+        else wv = reinterpret_cast<const float *>(w)[(size_t)j * H + c];
+        acc += x[c] * wv;
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) D[(size_t)row * nj + j] = acc * (WT == WT_FP8 ? scale[j] : 1.f);
+}
+
+// Two-tap causal conv over each sequence's block rows (row 0's predecessor
+// is zero), coefficients base[c][tap] + D[row][half][g(c)][tap] with
+// g(c) = floor(c G / H); tap 0 multiplies row r - 1, tap 1 row r.  Writes
+// the result, or adds it to dst (the finish conv into the residual).
+__global__ __launch_bounds__(256) void d2_conv(const float *src, const float *D, int half, const float *base, int H, int G,
+                                               int b, int rows, float *dst, int accumulate) {
+    const int row = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+    if (row >= rows || c >= H) return;
+    const int r = row % b, g = (int)(((long long)c * G) / H);
+    const float *Dr = D + (size_t)row * 4 * G + (size_t)(half * G + g) * 2;
+    const float *bh = base + (size_t)half * H * 2 + (size_t)c * 2;
+    const float cur = src[(size_t)row * H + c];
+    const float prev = r > 0 ? src[(size_t)(row - 1) * H + c] : 0.f;
+    const float y = (bh[0] + Dr[0]) * prev + (bh[1] + Dr[1]) * cur;
+    float *o = dst + (size_t)row * H + c;
+    *o = accumulate ? *o + y : y;
+}
+
 }  // namespace
+
+hipError_t d2_dyn_launch(const float *xn, int H, const void *w, const float *scale, int wt, int nj, int rows, float *D,
+                         hipStream_t s) {
+    const dim3 grid((rows * nj + 3) / 4), block(256);
+    if (wt == WT_BF16) hipLaunchKernelGGL(d2_dyn<WT_BF16>, grid, block, 0, s, xn, H, w, scale, nj, rows, D);
+    else if (wt == WT_FP8) hipLaunchKernelGGL(d2_dyn<WT_FP8>, grid, block, 0, s, xn, H, w, scale, nj, rows, D);
+    else hipLaunchKernelGGL(d2_dyn<WT_F32>, grid, block, 0, s, xn, H, w, scale, nj, rows, D);
+    return hipGetLastError();
+}
+
+hipError_t d2_conv_launch(const float *src, const float *D, int half, const float *base, int H, int G, int b, int rows,
+                          float *dst, bool accumulate, hipStream_t s) {
+    hipLaunchKernelGGL(d2_conv, dim3((H + 255) / 256, rows), dim3(256), 0, s, src, D, half, base, H, G, b, rows, dst,
+                       accumulate ? 1 : 0);
+    return hipGetLastError();
+}
 
 hipError_t batch_qk_rope_launch(const BatchArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(batch_qk_rope, dim3(a.S * 16, (a.nq + 2 * a.nkv + 3) / 4), dim3(256), 0, s, a);

@@ -307,9 +307,9 @@ size_t dflash_batch_workspace_bytes(const dflash_model *m, int32_t n_seqs, int32
  *   out       : device f32 [n_seqs][b][hidden].
  *   ws        : >= dflash_batch_workspace_bytes(m, n_seqs, 0) bytes, 256-byte
  *               aligned (zero-filled once, like every workspace).
- * 1 <= n_seqs <= 8, 1 <= b <= 16.  DFLASH_E_UNSUPPORTED for an f32 KV cache
- * or a model with the DFlash2 conv wrap.  No grid-wide barriers: unlike
- * forward_round, it may share the device with other work. */
+ * 1 <= n_seqs <= 8, 1 <= b <= 16.  DFLASH_E_UNSUPPORTED for an f32 KV
+ * cache.  No grid-wide barriers: unlike the persistent round kernel, it may
+ * share the device with other work. */
 int dflash_forward_round_batch(const dflash_model *m, dflash_kv *kvs, int32_t n_seqs, const float *noise_emb,
                                const int32_t *pos_block, int32_t b, float *out, void *ws, size_t ws_bytes,
                                void *stream);

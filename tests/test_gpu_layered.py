@@ -32,6 +32,9 @@ SMALL_D128_FP8 = SMALL_BF16.replace(name="small_fp8_d128", hidden=1024, n_q_head
                                     head_dim=128, weight_dtype="fp8", seed=24)
 SMALL_YARN = SMALL_BF16.replace(name="small_yarn_d128", hidden=1024, n_q_heads=8, n_kv_heads=1,
                                 head_dim=128, rope_type="yarn", seed=25)
+# DFlash2 conv wrap around every sublayer: bf16 with G = 4, fp8 head_dim 128 with G = 16
+SMALL_D2 = SMALL_BF16.replace(name="small_bf16_d2", d2_groups=4, seed=27)
+SMALL_FP8_D2 = SMALL_D128_FP8.replace(name="small_fp8_d128_d2", d2_groups=16, seed=28)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -54,7 +57,7 @@ def _ingest_both(cfg, m, dr, kv, okv, n, stream, pos0=0):
     O.ingest_ctx(m, okv, O.ctx_features(m, taps), pos)
 
 
-@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_D128_FP8, SMALL_YARN], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_D128_FP8, SMALL_YARN, SMALL_D2, SMALL_FP8_D2], ids=lambda c: c.name)
 @pytest.mark.parametrize("b", [16, 5])
 def test_batched_round_matches_oracle(cfg, b):
     m, dr, D = _setup(cfg)
@@ -214,3 +217,27 @@ def test_c4_sweep_batched():
             tag = f"c4 batched seq {s} emb x{scale:g} ctx {ctx}"
             check(tag, out[s], ref, tol_for(cfg))
             argmax_check(tag, out[s], ref, lm)
+
+
+def test_c5_fp8_d2conv_layered():
+    """The c5 drafter (fp8 weights, DFlash2 conv, ctx 65536) on the layered
+    path (one sequence through the batched call), N(0,1) and x0.1 block
+    embeddings, against the oracle on the same directly prefilled cache."""
+    cfg = synth.ROUND8_FP8_D2
+    m, dr, D = _setup(cfg, max_rows=16)
+    ctx, b = cfg.ctx, cfg.block
+    kv = D.KVCache(cfg, (ctx + b + 63) // 64 * 64)
+    ks, vs = synth.make_prefill_kv(cfg, ctx)
+    kv.prefill(ks, vs)
+    okv = O.OracleKV(cfg)
+    okv.prefill(ks, vs)
+    del ks, vs
+    lm = synth.make_lm_head(cfg).astype(np.float64)
+    pos = synth.positions(ctx, b)
+    for scale in (1.0, 0.1):
+        noise = synth.make_noise(cfg) * np.float32(scale)
+        out = host(dr.forward_round_batch([kv], dev(noise[None]), dev(pos[None])))[0]
+        ref = O.forward_round(m, okv, noise, pos)
+        tag = f"c5 layered emb x{scale:g} ctx {ctx}"
+        check(tag, out, ref, tol_for(cfg))
+        argmax_check(tag, out, ref, lm)
