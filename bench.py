@@ -188,6 +188,29 @@ def full_bytes(cfg, n: int, b: int = 16) -> int:
     return w + n * cfg.n_taps * H * 4 + 2 * (n + b) * kvd * 2 * kvb * L
 
 
+def batched_sweep_bytes(cfg, ctx: int, S: int, t: int = 16, b: int = 16) -> int:
+    """Algorithmic HBM bytes of one batched sweep over S sequences: every
+    weight read once for all S (layer weights, fc, ingest W_k/W_v), and per
+    sequence its K/V read over ctx + b keys per layer, its new K/V rows
+    written and its taps read."""
+    r = round_bytes(cfg, ctx, t, b)
+    return (r["layer_weights"] + r["fc_weights"] + r["ingest_weights"] + r["scales"]
+            + S * (r["kv_read"] + r["kv_write"] + r["taps"]))
+
+
+def window_round_bytes(cfg, window: int, t: int = 16, b: int = 16) -> int:
+    """One round with a context window: as round_bytes, with the K/V read
+    over the window's rows plus the block."""
+    return round_bytes(cfg, window, t, b)["total"]
+
+
+def propose_bytes(vocab: int, hidden: int, rank: int, b: int) -> int:
+    """The proposal's device step: the draft rows' logits and hidden rows
+    read once, the bf16 projection matrix, the packed result written."""
+    nd = b - 1
+    return nd * vocab * 4 + nd * hidden * 4 + rank * hidden * 2
+
+
 def other_config(name: str, args) -> int:
     """Times one of the parity configurations with the same library calls
     and prints one JSON line for it (these are not the headline metric).
@@ -198,14 +221,99 @@ def other_config(name: str, args) -> int:
     import torch
     import synth
     from block_diffusion_drafter_round_amd import dflash as D
-    cfg = {"c1": synth.TINY_F32, "c2": synth.FULL5_BF16, "c4": synth.ROUND8_YARN, "c5": synth.ROUND8_FP8_D2}[name]
+    cfg = {"c1": synth.TINY_F32, "c2": synth.FULL5_BF16, "c4": synth.ROUND8_YARN, "c5": synth.ROUND8_FP8_D2,
+           "c4b": synth.ROUND8_YARN, "c3w": synth.ROUND8_BF16, "propose": synth.ROUND8_BF16}[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] loading {cfg.name}", file=sys.stderr, flush=True)
     sw = synth.make_weights(cfg)
     b = cfg.block
     stream = torch.cuda.current_stream(dev)
-    if name in ("c1", "c2"):
+    if name == "propose":
+        # DFlash2 proposal over a 151,936-token vocabulary: top-32 of 15 draft
+        # rows, rank-64 projection, one small copy, host greedy walk
+        V, k, rank = 151936, 32, 64
+        dr = D.Drafter(synth.make_weights(cfg.replace(n_layers=1)), device=dev, max_rows=16)
+        rng = np.random.default_rng(7)
+        logits = torch.from_numpy(rng.standard_normal((b, V)).astype(np.float32)).to(dev)
+        hidden = torch.from_numpy(rng.standard_normal((b, cfg.hidden)).astype(np.float32)).to(dev)
+        w_hp = torch.from_numpy(synth.encode_bf16((rng.standard_normal((rank, cfg.hidden)) * 0.02)
+                                                  .astype(np.float32)).view(np.int16)).to(dev)
+        pred = synth.encode_bf16(rng.standard_normal((V, rank)).astype(np.float32))
+        succ = synth.encode_bf16(rng.standard_normal((V, rank)).astype(np.float32))
+        sel = D.make_selector(pred, succ, k, w_hp)
+        packed = torch.empty((b - 1) * (2 * k + rank), dtype=torch.int32, device=dev)
+        step = lambda: D.dflash2_propose_greedy(dr.model, sel, logits, hidden, b, 1, dr.ws, dr.ws_bytes, stream)
+        units, unit, nbytes = 1, "proposals/s", propose_bytes(V, cfg.hidden, rank, b)
+        workload = (f"DFlash2 greedy proposal: top-{k} of {b - 1} draft rows over a {V}-token vocabulary, rank-{rank} "
+                    f"projection, one device-to-host copy, host walk (synchronous)")
+        prof_cls = None
+        # the device step alone, timed with events on its stream
+        for _ in range(10):
+            D.dflash2_propose_prepare(dr.model, sel, logits, hidden, b, packed, dr.ws, dr.ws_bytes, stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(100):
+            D.dflash2_propose_prepare(dr.model, sel, logits, hidden, b, packed, dr.ws, dr.ws_bytes, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        prep_us = e0.elapsed_time(e1) / 100 * 1e3
+        extra = {"device_step_us": round(prep_us, 2),
+                 "device_step_gbs": round(nbytes / (prep_us * 1e-6) / 1e9, 1),
+                 "device_step_hbm_frac": round(nbytes / (prep_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    elif name == "c4b":
+        # the c4 sweep as one batched step: ctx_features of the 8 sequences' 16
+        # new rows in one call, one batched ingest, one batched round
+        ctx, t, S = cfg.ctx, cfg.new_rows, cfg.n_seqs
+        base = ctx - t
+        dr = D.Drafter(sw, device=dev, max_rows=S * t)
+        dr.ensure_batch(S)
+        kvs = [D.KVCache(cfg, (ctx + b + 63) // 64 * 64, dev) for _ in range(S)]
+        taps = torch.from_numpy(synth.make_taps(cfg, S * t, stream=1)).to(dev)
+        noise = torch.from_numpy(np.stack([synth.make_noise(cfg, stream=q) for q in range(S)])).to(dev)
+        pos_new = torch.from_numpy(np.stack([synth.positions(base, t)] * S)).to(dev)
+        pos_blk = torch.from_numpy(np.stack([synth.positions(ctx, b)] * S)).to(dev)
+        feats = torch.empty((S * t, cfg.hidden), dtype=torch.float32, device=dev)
+        out = torch.empty((S, b, cfg.hidden), dtype=torch.float32, device=dev)
+        arr = D.kv_array(kvs)
+
+        def step():
+            for q in range(S):
+                arr[q].len = base
+            D.dflash_ctx_features(dr.model, taps, S * t, feats, dr.ws, dr.ws_bytes, stream)
+            D.dflash_ingest_ctx_batch(dr.model, arr, feats, pos_new, t, dr.ws, dr.ws_bytes, stream)
+            D.dflash_forward_round_batch(dr.model, arr, noise, pos_blk, b, out, dr.ws, dr.ws_bytes, stream)
+        units, unit, nbytes = S, "sequence-rounds/s", batched_sweep_bytes(cfg, ctx, S, t, b) / S
+        workload = (f"{cfg.n_layers}-layer bf16 drafter (YaRN), {S} sequences at ctx {ctx} in one batched step: "
+                    f"ctx_features of {S}x{t} rows, batched ingest, batched round (weights read once per step)")
+        prof_cls, extra = D.K_ATTN, {"bytes_per_step": batched_sweep_bytes(cfg, ctx, S, t, b)}
+    elif name == "c3w":
+        # c3 on a paged cache (256-row pages, permuted block table) with a
+        # 1024-row context window: ctx_features 16 + ingest 16 + round
+        ctx, t, W = cfg.ctx, cfg.new_rows, 1024
+        base = ctx - t
+        dr = D.Drafter(sw, device=dev, max_rows=16)
+        dr.ensure_batch(1)
+        kv = D.PagedKVCache(cfg, (ctx + b + 255) // 256 * 256, page_rows=256, device=dev, seed=5)
+        kv.c.ctx_cap = W
+        taps = torch.from_numpy(synth.make_taps(cfg, t, stream=1)).to(dev)
+        noise = torch.from_numpy(synth.make_noise(cfg)).to(dev)
+        pos_new = torch.from_numpy(synth.positions(base, t)).to(dev)
+        pos_blk = torch.from_numpy(synth.positions(ctx, b)).to(dev)
+        feats = torch.empty((t, cfg.hidden), dtype=torch.float32, device=dev)
+        out = torch.empty((b, cfg.hidden), dtype=torch.float32, device=dev)
+
+        def step():
+            kv.c.len = base
+            D.dflash_ctx_features(dr.model, taps, t, feats, dr.ws, dr.ws_bytes, stream)
+            D.dflash_ingest_ctx(dr.model, kv.c, feats, pos_new, t, dr.ws, dr.ws_bytes, stream)
+            D.dflash_forward_round(dr.model, kv.c, noise, pos_blk, b, out, dr.ws, dr.ws_bytes, stream)
+        units, unit, nbytes = 1, "rounds/s", window_round_bytes(cfg, W, t, b)
+        workload = (f"{cfg.n_layers}-layer bf16 drafter cached round at ctx {ctx} on a paged cache (256-row pages) "
+                    f"with a {W}-row context window (layered path)")
+        prof_cls, extra = D.K_ATTN, {}
+    elif name in ("c1", "c2"):
         n = cfg.ctx
         dr = D.Drafter(sw, device=dev, max_rows=n)
         scratch = D.KVCache(cfg, (n + b + 63) // 64 * 64, dev)
@@ -215,6 +323,7 @@ def other_config(name: str, args) -> int:
         step = lambda: dr.forward_full(taps, noise, pos, scratch)
         units, unit, nbytes = 1, "forwards/s", full_bytes(cfg, n, b)
         workload = f"{cfg.n_layers}-layer {cfg.weight_dtype} drafter first-light forward_full, n={n} ctx rows, block {b}"
+        prof_cls, extra = D.K_GEMM_FC, {}
     else:
         ctx, t = cfg.ctx, cfg.new_rows
         base = ctx - t
@@ -238,6 +347,7 @@ def other_config(name: str, args) -> int:
         workload = (f"{cfg.n_layers}-layer {cfg.weight_dtype} drafter cached round at ctx {ctx}"
                     f"{' (YaRN)' if cfg.rope_type == 'yarn' else ''}{' with the DFlash2 conv' if cfg.d2_groups else ''}"
                     f", {nseq} sequence(s) back to back")
+        prof_cls, extra = D.K_ROUND, {}
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -250,6 +360,16 @@ def other_config(name: str, args) -> int:
     dr.status()
     per = np.sort(np.array([a.elapsed_time(z) for a, z in evs])) / 1e3      # s per step
     med = float(np.median(per))
+    if prof_cls is not None:
+        # the dominant kernel class's average launch time, events on its stream
+        D.dflash_prof_start(prof_cls, 4096)
+        for _ in range(min(args.steps, 20)):
+            step()
+        tot_ms, nl = D.dflash_prof_stop()
+        extra["dominant_kernel_class"] = {D.K_ATTN: "attention (splits + merge)", D.K_ROUND: "persistent round kernel",
+                                          D.K_GEMM_FC: "fc GEMM"}[prof_cls]
+        extra["dominant_kernel_avg_us"] = round(tot_ms * 1e3 / max(nl, 1), 2)
+        extra["dominant_kernel_launches_per_step"] = round(nl / min(args.steps, 20), 2)
     rec = {"metric": f"{cfg.name}: {unit}", "value": round(units / med, 2), "unit": unit, "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(med * 1e3, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.weight_dtype,
@@ -258,7 +378,7 @@ def other_config(name: str, args) -> int:
            "step_ms_p10_p50_p90": [round(float(np.percentile(per, q)) * 1e3, 4) for q in (10, 50, 90)],
            "algorithmic_bytes_per_unit": nbytes,
            "hbm_gbs": round(nbytes * units / med / 1e9, 1),
-           "hbm_frac": round(nbytes * units / med / 1e9 / HBM_PEAK_GBS, 4)}
+           "hbm_frac": round(nbytes * units / med / 1e9 / HBM_PEAK_GBS, 4), **extra}
     print(json.dumps(rec), flush=True)
     return 0
 
@@ -293,9 +413,11 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prof", action="store_true", help="skip the live per-kernel timing")
     ap.add_argument("--copy-calibration", action="store_true", help="only run the 256 MiB copy used to scale counters")
-    ap.add_argument("--config", choices=("c1", "c2", "c4", "c5"),
+    ap.add_argument("--config", choices=("c1", "c2", "c4", "c5", "c4b", "c3w", "propose"),
                     help="time one of the other workloads instead (c1 tiny f32 forward_full, c2 5-layer forward_full "
-                         "n=1024, c4 YaRN ctx 32768 x 8 sequences, c5 fp8 + DFlash2 ctx 65536)")
+                         "n=1024, c4 YaRN ctx 32768 x 8 sequences back to back, c5 fp8 + DFlash2 ctx 65536, "
+                         "c4b the c4 sweep as one batched step, c3w c3 on a paged cache with a 1024-row window, "
+                         "propose the DFlash2 greedy proposal)")
     args = ap.parse_args(argv)
     if args.copy_calibration:
         return copy_calibration()

@@ -286,17 +286,19 @@ hipError_t run_ctx_features(const dflash_model *m, const float *taps, int t, flo
     return dfl::rmsnorm(feats, c.hidden, m->w.g_hidden_norm, feats, c.hidden, nullptr, t, c.hidden, c.rms_eps, s);
 }
 
-hipError_t run_ingest(const dflash_model *m, dflash_kv *kv, const float *feats, const int32_t *pos, int t, void *ws,
-                      const WsLayout &L, hipStream_t s) {
+// ingest of t rows into each of S caches (feats / pos: S blocks of t rows)
+hipError_t run_ingest(const dflash_model *m, const dflash_kv *kvs, int S, const float *feats, const int32_t *pos, int t,
+                      void *ws, const WsLayout &L, hipStream_t s) {
     const dflash_cfg &c = m->cfg;
     const int kvd = c.n_kv_heads * c.head_dim;
-    const int per = ingest_layers_per_launch(t);
+    const int rows = S * t;
+    const int per = ingest_layers_per_launch(rows);
     float *kvbuf = at<float>(ws, L.qkv);
     for (int l0 = 0; l0 < c.n_layers; l0 += per) {
         const int nl = std::min(per, c.n_layers - l0);
         // k|v of layers l0 .. l0 + nl - 1 side by side: [t][nl * 2 * kvd]
         dfl::GemmArgs g{};
-        g.A = feats; g.lda = c.hidden; g.M = t; g.K = c.hidden;
+        g.A = feats; g.lda = c.hidden; g.M = rows; g.K = c.hidden;
         for (int i = 0; i < nl; ++i) {
             const dflash_layer_weights &W = m->layers[l0 + i];
             g.seg[2 * i] = seg(W.wk, kvd);
@@ -313,9 +315,13 @@ hipError_t run_ingest(const dflash_model *m, dflash_kv *kv, const float *feats, 
         dfl::RopeArgs r{};
         r.src = kvbuf; r.ld = nl * 2 * kvd; r.lstride = 2 * kvd; r.nl = nl; r.layer0 = l0;
         for (int i = 0; i < nl; ++i) r.g_k[i] = m->layers[l0 + i].g_k;
-        r.kv = kv_view(m, kv);
-        r.pos = pos; r.rows = t; r.nkv = c.n_kv_heads; r.d = c.head_dim; r.eps = c.rms_eps;
-        r.mscale = (float)m->mscale; r.row0 = kv->len; r.kv_f32 = c.kv_dtype == DFLASH_F32;
+        for (int q = 0; q < S; ++q) {
+            r.kv[q] = kv_view(m, &kvs[q]);
+            r.row0[q] = kvs[q].len;
+        }
+        r.seq_rows = t;
+        r.pos = pos; r.rows = rows; r.nkv = c.n_kv_heads; r.d = c.head_dim; r.eps = c.rms_eps;
+        r.mscale = (float)m->mscale; r.kv_f32 = c.kv_dtype == DFLASH_F32;
         memcpy(r.inv_freq, m->inv_freq, sizeof r.inv_freq);
         {
             ProfScope p(DFLASH_K_ROPE, s);
@@ -745,9 +751,35 @@ int dflash_ingest_ctx(const dflash_model *m, dflash_kv *kv, const float *feats, 
     if (t == 0) return DFLASH_OK;
     if (!aligned(feats, 16) || !aligned(pos_new, 4)) return fail(DFLASH_E_INVAL, "feats / pos_new null or misaligned");
     if ((rc = check_ws(m, ws, ws_bytes, t))) return rc;
-    hipError_t e = run_ingest(m, kv, feats, pos_new, t, ws, ws_layout(m->cfg, t), (hipStream_t)stream);
+    hipError_t e = run_ingest(m, kv, 1, feats, pos_new, t, ws, ws_layout(m->cfg, t), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "ingest_ctx");
     kv->len += t;
+    return DFLASH_OK;
+}
+
+int dflash_ingest_ctx_batch(const dflash_model *m, dflash_kv *kvs, int32_t n_seqs, const float *feats,
+                            const int32_t *pos_new, int32_t t, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    if (!m) return fail(DFLASH_E_INVAL, "model is null");
+    if (!kvs) return fail(DFLASH_E_INVAL, "kvs is null");
+    if (n_seqs < 1 || n_seqs > dfl::ROPE_MAX_SEQ) return fail(DFLASH_E_INVAL, "n_seqs %d outside [1, %d]", n_seqs, dfl::ROPE_MAX_SEQ);
+    if (t < 0) return fail(DFLASH_E_INVAL, "t = %d is negative", t);
+    int rc;
+    for (int i = 0; i < n_seqs; ++i) {
+        if ((rc = check_kv(m, &kvs[i]))) return fail(rc, "sequence %d: %s", i, g_err.c_str());
+        if ((int64_t)kvs[i].len + t > kvs[i].capacity)
+            return fail(DFLASH_E_CAPACITY, "sequence %d: len %d + t %d exceeds capacity %d", i, kvs[i].len, t, kvs[i].capacity);
+        for (int j = 0; j < i; ++j)
+            if (kvs[j].k == kvs[i].k || kvs[j].v == kvs[i].v)
+                return fail(DFLASH_E_INVAL, "sequences %d and %d share KV storage", j, i);
+    }
+    if (t == 0) return DFLASH_OK;
+    if (!aligned(feats, 16) || !aligned(pos_new, 4)) return fail(DFLASH_E_INVAL, "feats / pos_new null or misaligned");
+    const int rows = n_seqs * t;
+    if ((rc = check_ws(m, ws, ws_bytes, rows))) return rc;
+    hipError_t e = run_ingest(m, kvs, n_seqs, feats, pos_new, t, ws, ws_layout(m->cfg, rows), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ingest_ctx_batch");
+    for (int i = 0; i < n_seqs; ++i) kvs[i].len += t;
     return DFLASH_OK;
 }
 
@@ -809,7 +841,7 @@ int dflash_forward_full(const dflash_model *m, const float *taps, const float *n
     kv.len = 0;
     if (n > 0) {
         e = run_ctx_features(m, taps, n, feats, at<float>(ws, L.gpart), at<unsigned>(ws, L.gcnt), s);
-        if (e == hipSuccess) e = run_ingest(m, &kv, feats, pos, n, ws, L, s);
+        if (e == hipSuccess) e = run_ingest(m, &kv, 1, feats, pos, n, ws, L, s);
         kv.len = n;
     }
     if (e == hipSuccess) {
@@ -860,16 +892,13 @@ int propose_prepare(const dflash_model *m, const dflash2_selector *sel, const fl
     if (b < 2 || b > MAX_BLOCK) return fail(DFLASH_E_INVAL, "block size b = %d outside [2, 16] (row 0 is the anchor)", b);
     if (!aligned(logits, 4) || !aligned(hidden, 4) || !aligned(packed, 4))
         return fail(DFLASH_E_INVAL, "draft logits / hidden / output null or misaligned");
-    const int nd = b - 1, k = sel->top_k, nc = dfl::topk_chunks(sel->vocab);
-    if ((size_t)nc * k > (size_t)dfl::TOPK_STAGE2)
-        return fail(DFLASH_E_UNSUPPORTED, "vocabulary %d with top_k %d needs %d stage-1 candidates per row (at most %d)",
-                    sel->vocab, k, nc * k, dfl::TOPK_STAGE2);
+    const int nd = b - 1, k = sel->top_k;
     int rc = check_ws(m, ws, ws_bytes, 0);
     if (rc) return rc;
     const WsLayout L = ws_layout(m->cfg, 0);
-    const size_t part = (size_t)nd * nc * k;
+    const size_t part = dfl::topk_scratch_entries(nd, sel->vocab, k);
     if (2 * part * 4 > 4 * dfl::GEMM_PART_FLOATS)
-        return fail(DFLASH_E_UNSUPPORTED, "top-k partials of %zu bytes exceed the workspace's %zu", 2 * part * 4,
+        return fail(DFLASH_E_UNSUPPORTED, "top-k candidates of %zu bytes exceed the workspace's %zu", 2 * part * 4,
                     4 * dfl::GEMM_PART_FLOATS);
     float *pv = at<float>(ws, L.gpart);
     int32_t *pi = reinterpret_cast<int32_t *>(pv + part);
@@ -905,7 +934,7 @@ int dflash2_propose_greedy(const dflash_model *m, const dflash2_selector *sel, c
     if (!aligned(ws, 256)) return fail(DFLASH_E_INVAL, "workspace null or not 256-byte aligned");
     const WsLayout L = ws_layout(m->cfg, 0);
     const size_t words = (size_t)nd * (2 * k + rank);
-    const size_t part_bytes = 2 * (size_t)nd * dfl::topk_chunks(std::max(sel->vocab, 1)) * k * 4;
+    const size_t part_bytes = 2 * dfl::topk_scratch_entries(nd, std::max(sel->vocab, 1), std::max(k, 1)) * 4;
     if (part_bytes + 4 * words > 4 * dfl::GEMM_PART_FLOATS)
         return fail(DFLASH_E_UNSUPPORTED, "top-k partials and packed block exceed the workspace's scratch region");
     uint32_t *packed = at<uint32_t>(ws, L.gpart + (part_bytes + 255) / 256 * 256);

@@ -41,12 +41,13 @@ constexpr int    GEMM_MAX_COUNTERS = 1 << 14;
 hipError_t gemm(GemmArgs a, float *part, unsigned *cnt, hipStream_t s);
 
 // ---- DFlash2 proposal: top-k over draft logits, rank-r hidden projection ----
-constexpr int TOPK_CHUNK = 4096;     // values per stage-1 wave (64 per lane)
-constexpr int TOPK_STAGE2 = 4096;    // stage-1 candidates one stage-2 wave can hold
-int topk_chunks(int vocab);
+constexpr int TOPK_CHUNK = 1024;     // candidates per wave and stage (16 per lane)
+int topk_chunks(int n);
+// entries part_v / part_i must hold for rows of a vocabulary (k <= 64, so
+// each stage shrinks the candidates at least 16-fold)
+size_t topk_scratch_entries(int rows, int vocab, int k);
 // Per row: the k largest logits (larger first, then lower index) and their
-// indices.  part_v / part_i hold rows * topk_chunks(vocab) * k entries, and
-// topk_chunks(vocab) * k <= TOPK_STAGE2.
+// indices.
 hipError_t topk_rows(const float *logits, long long ld, int rows, int vocab, int k, float *part_v, int32_t *part_i,
                      float *vals, int32_t *idx, hipStream_t s);
 // out[r][j] = hidden[r] . w[j] for bf16 w [rank][H], f32 accumulation
@@ -70,17 +71,19 @@ hipError_t rmsnorm(const float *x, int ldx, const float *g, float *y, int ldy,
 // ---- k head norm + rope (+ mscale) and KV stores, several layers at once ----
 constexpr int MAX_HALF_DIM = 64;
 constexpr int ROPE_MAX_LAYERS = 8;
+constexpr int ROPE_MAX_SEQ = 8;
 struct RopeArgs {
     const float *src; int ld;     // [rows, ld] projection output; layer i's k heads start at
     int lstride;                  // column i * lstride, its v heads kvd = nkv * d further on
     int nl;                       // layers in this launch (<= ROPE_MAX_LAYERS)
     int layer0;                   // cache layer of launch layer 0
     const float *g_k[ROPE_MAX_LAYERS];
-    KvView kv;                    // the cache (contiguous or paged)
+    KvView kv[ROPE_MAX_SEQ];      // the caches (contiguous or paged) of the sequences
+    int row0[ROPE_MAX_SEQ];       // sequence s's rows go to its cache rows row0[s] ..
+    int seq_rows;                 // rows per sequence: row r belongs to sequence r / seq_rows
     const int32_t *pos;
     int rows, nkv, d;
     float eps; float mscale;
-    int row0;                     // cache rows row0 .. row0 + rows - 1
     int kv_f32;                   // 1: f32 cache, 0: bf16 cache
     double inv_freq[MAX_HALF_DIM];
 };

@@ -7,7 +7,9 @@
 // normed+roped, V raw; [DflashDraft] "rope_yarn": rope_neox_ff with
 // per-dimension inverse frequencies, then the q/k scale mscale).
 // * One workgroup per (row, layer), so one launch covers every layer whose
-//   k|v projections one GEMM produced side by side.  It first builds the
+//   k|v projections one GEMM produced side by side, and the rows of up to
+//   ROPE_MAX_SEQ sequences (consecutive blocks of seq_rows rows), each into
+//   its own cache.  It first builds the
 //   row's cos/sin table.  The angle pos * inv_freq[j] and its sin/cos are
 //   evaluated in f64, so long positions keep full accuracy.
 // * Each wave then takes heads in turn.  Lane j < d/2 holds the rope pair
@@ -73,12 +75,14 @@ __global__ __launch_bounds__(256) void kv_norm_rope_kernel(RopeArgs a) {
 
     const float *row = a.src + (size_t)r * a.ld + (size_t)l * a.lstride;
     const float *gain = a.g_k[l];
-    char *kc = a.kv.k + (size_t)(a.layer0 + l) * a.kv.lstride, *vc = a.kv.v + (size_t)(a.layer0 + l) * a.kv.lstride;
+    const int seq = r / a.seq_rows;
+    const KvView &kv = a.kv[seq];
+    char *kc = kv.k + (size_t)(a.layer0 + l) * kv.lstride, *vc = kv.v + (size_t)(a.layer0 + l) * kv.lstride;
     const int kvd = a.nkv * a.d;
     const bool act = lane < half;
     const float c = act ? cs[lane] : 0.f, s = act ? sn[lane] : 0.f;
-    const int crow = a.row0 + r;
-    const int page = kv_page(a.kv, crow);
+    const int crow = a.row0[seq] + r - seq * a.seq_rows;
+    const int page = kv_page(kv, crow);
 
     for (int h = wave; h < 2 * a.nkv; h += 4) {
         if (h < a.nkv) {
@@ -90,14 +94,14 @@ __global__ __launch_bounds__(256) void kv_norm_rope_kernel(RopeArgs a) {
                 const float y0 = gain[lane] * (x0 * inv), y1 = gain[lane + half] * (x1 * inv);
                 const float o0 = (y0 * c - y1 * s) * a.mscale;
                 const float o1 = (y1 * c + y0 * s) * a.mscale;
-                store_kv(kc + kv_k_off(a.kv, page, a.nkv, h, crow, a.d, lane), o0, a.kv_f32);
-                store_kv(kc + kv_k_off(a.kv, page, a.nkv, h, crow, a.d, lane + half), o1, a.kv_f32);
+                store_kv(kc + kv_k_off(kv, page, a.nkv, h, crow, a.d, lane), o0, a.kv_f32);
+                store_kv(kc + kv_k_off(kv, page, a.nkv, h, crow, a.d, lane + half), o1, a.kv_f32);
             }
         } else if (act) {
             const int hh = h - a.nkv;
             const float *src = row + kvd + hh * a.d;
-            store_kv(vc + kv_v_off(a.kv, page, a.nkv, hh, crow, a.d, lane), src[lane], a.kv_f32);
-            store_kv(vc + kv_v_off(a.kv, page, a.nkv, hh, crow, a.d, lane + half), src[lane + half], a.kv_f32);
+            store_kv(vc + kv_v_off(kv, page, a.nkv, hh, crow, a.d, lane), src[lane], a.kv_f32);
+            store_kv(vc + kv_v_off(kv, page, a.nkv, hh, crow, a.d, lane + half), src[lane + half], a.kv_f32);
         }
     }
 }

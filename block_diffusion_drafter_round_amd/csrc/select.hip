@@ -2,13 +2,13 @@
 // top-k over each draft row's logits and the rank-r projection of the draft
 // rows' hidden states, packed for one small device-to-host copy.
 //
-// Top-k runs in two stages of the same kernel.  One wave takes a chunk of
-// one row, keeps up to VPL values per lane in registers and extracts the
-// chunk's k best by k rounds of a wave-wide argmax (order: larger value
-// first, then lower index), marking each winner as taken.  Stage 1 runs one
-// wave per (row, 2048-value chunk); stage 2 one wave per row over the
-// stage-1 candidates.  Every load is in bounds (lanes past the chunk hold
-// "taken" entries), and every wave runs exactly k rounds.
+// Top-k runs in stages of one kernel.  One wave takes a chunk of 1024
+// candidates of one row, 16 per lane in registers, and extracts the chunk's
+// k best by k rounds of a wave-wide argmax (order: larger value first, then
+// lower index), marking each winner as taken.  Each stage keeps k of every
+// 1024 candidates, until a single chunk holds them all (three stages for a
+// 151,936-token vocabulary).  Every load is in bounds (lanes past the chunk
+// hold "taken" entries), and every wave runs exactly k rounds.
 #include <climits>
 
 #include "common.h"
@@ -69,7 +69,9 @@ __global__ __launch_bounds__(64) void topk_wave(const float *in, const int32_t *
     }
 }
 
-// hproj[r][j] = sum_c hidden[r][c] * W[j][c]: one wave per output, f32 accumulation
+// hproj[r][j] = sum_c hidden[r][c] * W[j][c]: one wave per output, f32
+// accumulation; lane l takes 8 consecutive columns per 512, with the loads
+// of up to four such groups in flight at once (H is a multiple of 256)
 __global__ __launch_bounds__(256) void hidden_proj(const float *hidden, int H, const uint16_t *w, int rank, int rows,
                                                    float *out) {
     const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -78,7 +80,27 @@ __global__ __launch_bounds__(256) void hidden_proj(const float *hidden, int H, c
     const float *x = hidden + (size_t)r * H;
     const uint16_t *wr = w + (size_t)j * H;
     float s = 0.f;
-    for (int c = lane; c < H; c += 64) s += x[c] * bf16_bits_to_f32(wr[c]);
+    for (int c0 = 0; c0 < H; c0 += 4 * 512) {
+        u32x4 wv[4];
+        float4 xa[4], xb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = min(c0 + u * 512 + 8 * lane, H - 8);
+            wv[u] = *reinterpret_cast<const u32x4 *>(wr + c);
+            xa[u] = *reinterpret_cast<const float4 *>(x + c);
+            xb[u] = *reinterpret_cast<const float4 *>(x + c + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (c0 + u * 512 + 8 * lane >= H) continue;
+            const float xs[8] = {xa[u].x, xa[u].y, xa[u].z, xa[u].w, xb[u].x, xb[u].y, xb[u].z, xb[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s += xs[2 * i] * bf16_bits_to_f32(wv[u][i] & 0xFFFFu);
+                s += xs[2 * i + 1] * __uint_as_float(wv[u][i] & 0xFFFF0000u);
+            }
+        }
+    }
     s = wave_sum(s);
     if (lane == 0) out[(size_t)r * rank + j] = s;
 }
@@ -87,17 +109,40 @@ __global__ __launch_bounds__(256) void hidden_proj(const float *hidden, int H, c
 
 int topk_chunks(int vocab) { return (vocab + TOPK_CHUNK - 1) / TOPK_CHUNK; }
 
+size_t topk_scratch_entries(int rows, int vocab, int k) {
+    // the first stage's candidates, then the second stage's, side by side
+    const size_t n1 = (size_t)topk_chunks(vocab) * k;
+    return (size_t)rows * (n1 + (size_t)topk_chunks((int)n1) * k);
+}
+
 hipError_t topk_rows(const float *logits, long long ld, int rows, int vocab, int k, float *part_v, int32_t *part_i,
                      float *vals, int32_t *idx, hipStream_t s) {
-    const int nc = topk_chunks(vocab);
-    hipLaunchKernelGGL(topk_wave<TOPK_CHUNK / 64>, dim3(nc, rows), dim3(64), 0, s, logits, (const int32_t *)nullptr,
-                       vocab, ld, TOPK_CHUNK, k, part_v, part_i, nc * k);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int n2 = nc * k;                               // <= TOPK_STAGE2 (checked by the caller)
-    hipLaunchKernelGGL(topk_wave<TOPK_STAGE2 / 64>, dim3(1, rows), dim3(64), 0, s, (const float *)part_v,
-                       (const int32_t *)part_i, n2, (long long)n2, TOPK_STAGE2, k, vals, idx, k);
-    return hipGetLastError();
+    // each stage keeps the k best of every TOPK_CHUNK candidates, until one
+    // chunk holds them all; stages alternate between two candidate regions
+    const float *in = logits;
+    const int32_t *in_i = nullptr;
+    long long in_ld = ld;
+    int n = vocab;
+    // region A holds the first stage's output, region B (right after it) the
+    // second's; every later stage is smaller than both
+    const size_t region_b = (size_t)rows * topk_chunks(vocab) * k;
+    size_t off = 0;
+    while (true) {
+        const int nc = topk_chunks(n);
+        const bool last = nc == 1;
+        float *ov = last ? vals : part_v + off;
+        int32_t *oi = last ? idx : part_i + off;
+        const int out_ld = nc * k;
+        hipLaunchKernelGGL(topk_wave<TOPK_CHUNK / 64>, dim3(nc, rows), dim3(64), 0, s, in, in_i, n, in_ld, TOPK_CHUNK,
+                           k, ov, oi, out_ld);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || last) return e;
+        in = ov;
+        in_i = oi;
+        in_ld = out_ld;
+        n = out_ld;
+        off = off == 0 ? region_b : 0;                  // the next stage writes the other region
+    }
 }
 
 hipError_t hidden_projection(const float *hidden, int H, const void *w, int rank, int rows, float *out, hipStream_t s) {

@@ -73,7 +73,7 @@ EXPORTS = ("dflash_load_weights", "dflash_free", "dflash_workspace_bytes", "dfla
            "dflash_ctx_features_noalloc", "dflash_accept_prefix", "dflash_rejection_accept_len",
            "dflash_confidence_vt", "dflash_slot_confidence_vt", "dflash2_walk_greedy", "dflash2_walk_sampled",
            "dflash2_propose_prepare", "dflash2_propose_greedy", "dflash_batch_workspace_bytes",
-           "dflash_forward_round_batch")
+           "dflash_forward_round_batch", "dflash_ingest_ctx_batch")
 
 # kernel classes of the measurement hook (include/dflash_prof.h)
 K_GEMM_FC, K_GEMM_KV, K_GEMM_QKV, K_GEMM_O, K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN, K_ROPE, K_NORM, K_ROUND = range(1, 11)
@@ -97,6 +97,7 @@ def lib():
     L.dflash_batch_workspace_bytes.argtypes = [vp, i32, i32]
     L.dflash_batch_workspace_bytes.restype = sz
     L.dflash_forward_round_batch.argtypes = [vp, C.POINTER(dflash_kv), i32, vp, vp, i32, vp, vp, sz, vp]
+    L.dflash_ingest_ctx_batch.argtypes = [vp, C.POINTER(dflash_kv), i32, vp, vp, i32, vp, sz, vp]
     L.dflash_packed_bytes.restype = sz
     L.dflash_pack_weights.argtypes = [vp, vp, sz, vp]
     L.dflash_ctx_features.argtypes = [vp, vp, i32, vp, vp, sz, vp]
@@ -205,6 +206,12 @@ def dflash_forward_round_batch(model, kvs, noise_emb, pos_block, b, out, ws, ws_
     """kvs: a ctypes array of dflash_kv (see kv_array)."""
     _check(lib().dflash_forward_round_batch(model, kvs, len(kvs), _ptr(noise_emb), _ptr(pos_block), b, _ptr(out),
                                             _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dflash_ingest_ctx_batch(model, kvs, feats, pos_new, t, ws, ws_bytes, stream=None) -> None:
+    """kvs: a ctypes array of dflash_kv (see kv_array); their lens advance by t."""
+    _check(lib().dflash_ingest_ctx_batch(model, kvs, len(kvs), _ptr(feats), _ptr(pos_new), t, _ptr(ws), ws_bytes,
+                                         _stream(stream)))
 
 
 def kv_array(caches):
@@ -571,6 +578,15 @@ class Drafter:
         paged or windowed caches) for up to n_seqs sequences."""
         if n_seqs > self.batch_seqs:
             self._realloc(self.max_rows, n_seqs)
+
+    def ingest_ctx_batch(self, caches, feats: torch.Tensor, pos_new: torch.Tensor) -> None:
+        """feats [S, t, H], pos_new [S, t]: t new rows into each cache."""
+        S, t = feats.shape[0], feats.shape[1]
+        self.ensure_rows(S * t)
+        arr = kv_array(caches)
+        dflash_ingest_ctx_batch(self.model, arr, feats, pos_new, t, self.ws, self.ws_bytes)
+        for c, k in zip(caches, arr):
+            c.c.len = k.len
 
     def forward_round_batch(self, caches, noise_emb: torch.Tensor, pos_block: torch.Tensor) -> torch.Tensor:
         """noise_emb [S, b, H], pos_block [S, b] -> out [S, b, H]."""

@@ -267,6 +267,17 @@ int dflash_ingest_ctx(const dflash_model *m, dflash_kv *kv, const float *feats,
                       const int32_t *pos_new, int32_t t, void *ws, size_t ws_bytes,
                       void *stream);
 
+/* ingest_ctx for n_seqs sequences at once ([atlas dflash_head]
+ * "DflashProposerState": one cache per sequence): t new rows per sequence,
+ * whose k|v projections share one pass over each layer's W_k / W_v.
+ *   feats  : device f32 [n_seqs][t][hidden]; pos_new: device int32 [n_seqs][t].
+ *   kvs    : host array of n_seqs caches with distinct storage; each
+ *            kvs[i].len += t on the host, at enqueue time.
+ * 1 <= n_seqs <= 8; n_seqs * t <= the workspace's max_rows.  Any cache's
+ * capacity error rejects the whole call (no len changes). */
+int dflash_ingest_ctx_batch(const dflash_model *m, dflash_kv *kvs, int32_t n_seqs, const float *feats,
+                            const int32_t *pos_new, int32_t t, void *ws, size_t ws_bytes, void *stream);
+
 /* One drafting round over the cached ctx K/V ([DflashDraft] "forward_round").
  * Only the b block rows are projected per layer.  Their K/V land transiently
  * at rows [kv->len, kv->len + b), and attention over all kv->len + b keys is

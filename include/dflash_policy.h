@@ -116,8 +116,10 @@ int dflash2_walk_sampled(const dflash2_selector *s, const float *unary, const in
  *                  f32 values [nd][top_k], int32 ids [nd][top_k], f32
  *                  hproj [nd][rank].
  *   ws           : the model's workspace (dflash_workspace_bytes).
- * 2 <= b <= 16.  DFLASH_E_UNSUPPORTED if vocab and top_k need more than
- * 4096 first-stage candidates per row (ceil(vocab / 4096) * top_k). */
+ * 2 <= b <= 16.  DFLASH_E_UNSUPPORTED if the top-k candidates of the draft
+ * rows do not fit the workspace's 4 MiB scratch region (about
+ * (b-1) * vocab * top_k / 128 bytes: vocabularies of up to ~1.5M tokens at
+ * top_k 64). */
 int dflash2_propose_prepare(const struct dflash_model *m, const dflash2_selector *sel, const float *draft_logits,
                             const float *hidden, int32_t b, uint32_t *packed, void *ws, size_t ws_bytes, void *stream);
 

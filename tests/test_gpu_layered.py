@@ -241,3 +241,38 @@ def test_c5_fp8_d2conv_layered():
         tag = f"c5 layered emb x{scale:g} ctx {ctx}"
         check(tag, out, ref, tol_for(cfg))
         argmax_check(tag, out, ref, lm)
+
+
+def test_batched_ingest_matches_oracle():
+    """dflash_ingest_ctx_batch: t rows into each of three caches (two
+    contiguous, one paged) in one k|v pass; every cache row against the
+    oracle's per-sequence ingest, and bitwise equal to one ingest per cache."""
+    cfg = SMALL_BF16
+    m, dr, D = _setup(cfg, max_rows=128)
+    S, t, lens = 3, 21, (0, 40, 77)
+    caches = [D.KVCache(cfg, 256), D.PagedKVCache(cfg, 256, page_rows=64, seed=4), D.KVCache(cfg, 256)]
+    singles = [D.KVCache(cfg, 256), D.PagedKVCache(cfg, 256, page_rows=64, seed=4), D.KVCache(cfg, 256)]
+    okvs = []
+    for q, n in enumerate(lens):
+        okv = O.OracleKV(cfg)
+        if n:
+            taps = synth.make_taps(cfg, n, stream=50 + q)
+            pos = synth.positions(0, n)
+            for c in (caches[q], singles[q]):
+                dr.ingest_ctx(c, dr.ctx_features(dev(taps)), dev(pos))
+            O.ingest_ctx(m, okv, O.ctx_features(m, taps), pos)
+        okvs.append(okv)
+    taps = np.stack([synth.make_taps(cfg, t, stream=60 + q) for q in range(S)])
+    pos = np.stack([synth.positions(n, t) for n in lens])
+    feats = dr.ctx_features(dev(taps.reshape(S * t, -1))).reshape(S, t, cfg.hidden)
+    dr.ingest_ctx_batch(caches, feats, dev(pos))
+    assert [c.len for c in caches] == [n + t for n in lens]
+    for q in range(S):
+        dr.ingest_ctx(singles[q], feats[q].contiguous(), dev(pos[q]))
+        O.ingest_ctx(m, okvs[q], O.ctx_features(m, taps[q]), pos[q])
+        for l in range(cfg.n_layers):
+            k, v = kv_rows_f64(caches[q], l, 0, lens[q] + t)
+            check(f"batched ingest seq {q} layer {l} K", k, okvs[q].k[l], 1e-2)
+            check(f"batched ingest seq {q} layer {l} V", v, okvs[q].v[l], 1e-2)
+            k1, v1 = kv_rows_f64(singles[q], l, 0, lens[q] + t)
+            assert np.array_equal(k, k1) and np.array_equal(v, v1), "batched and single ingest differ"
