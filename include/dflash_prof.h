@@ -20,7 +20,9 @@
 extern "C" {
 #endif
 
-/* kernel classes */
+/* kernel classes (3-7 are launches of the layered round path: batched,
+ * paged or windowed rounds; the persistent kernel runs those steps inside
+ * its one launch, class 10) */
 #define DFLASH_K_GEMM_FC      1   /* fc projection of the taps */
 #define DFLASH_K_GEMM_KV      2   /* ingest k|v projection */
 #define DFLASH_K_GEMM_QKV     3   /* block q|k|v projection */
