@@ -1024,39 +1024,81 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
     }
 }
 
-// One pass of NF k steps (groups of 4) with the pass's activations in registers.
-template <int WT, bool C>
+// One pass of NF k steps (groups of 4) with the pass's activations in
+// registers.  The ring parts of a step are read together before its MFMAs,
+// so the LDS latency is paid about once per step rather than once per part:
+// every tile's part of a step (tiles past nt read a valid part that is not
+// used).  ONE (a workgroup with exactly one tile, built as its own function
+// so that it holds a single accumulator) reads the parts of all four steps of
+// a group at once.
+template <int WT, bool C, bool ONE>
 __device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, const Grp &G, u32x4 *a, u32x4 *alo, int ks, int nst, int nt,
                                           bool conv, const float *cbase, const float *cD, f32x4 (&acc)[SR_MAXT]) {
     constexpr int AFR = TR<WT>::AFR, NF = PassCfg<WT>::NF;
     constexpr bool HL = C && TR<WT>::AB == 2;       // alo != a: the activations' low plane
     const int v = wave_id();
     const u32x4 *ringv = &S.ring[0][v][0];
+    // ring part of tile t at step j4 of the group whose first slot is s0 in the
+    // ring.  Lane L of a part of an n-wide tile holds row L % n of lane group
+    // L / n (n is 16, 8 or 4, so shifts and masks instead of products).
+    auto part = [&](unsigned s0, int j4, int t) -> u32x4 {
+        const int n = G.n[t];
+        const int lg = n == 16 ? 4 : n == 8 ? 3 : 2;
+        // off < the group's slots <= SR_NSLOT - SR_DEPTH (sround_nwg), so one
+        // subtraction wraps s0 + off into the ring
+        unsigned slot = s0 + (unsigned)G.off[t][j4];
+        slot = __builtin_amdgcn_readfirstlane(slot >= SR_NSLOT ? slot - SR_NSLOT : slot);
+        const int ln = lane_id();
+        const int m = (16 >> lg) - 1;                            // 16 / n - 1
+        const int L = (((j4 & m) << 2) << lg) + (((ln >> 4) << lg) | (ln & (n - 1)));
+        return ringv[(size_t)slot * (SR_SLOT / 16) + L];
+    };
 #pragma unroll
     for (int q = 0; q < NF / 4; ++q) {
         const unsigned g0 = cs.seq;
-#pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-            const int j = 4 * q + j4;
-            u32x4 *aj = &a[j * AFR], *alj = &alo[j * AFR];
-            const bool live = ks + j < nst;
+        const unsigned s0 = __builtin_amdgcn_readfirstlane(g0 % SR_NSLOT);
+        if constexpr (ONE) {
             if constexpr (C) {
-                if (conv && live) d2_prepare<WT, HL>(S, aj, alj, ks + j, cbase, cD);
-            }
-            if (!ring_wait(S, cs, g0 + G.cnt[j4])) return false;
+                if (conv) {
 #pragma unroll
-            for (int t = 0; t < SR_MAXT; ++t) {
-                if (t < nt) {
-                    const int n = G.n[t];
-                    const unsigned slot = __builtin_amdgcn_readfirstlane((g0 + G.off[t][j4]) % SR_NSLOT);
-                    // lane index taken afresh so the 16 (tile, step) offsets are not all held live
-                    const int ln = lane_id();
-                    const int m = n == 16 ? 0 : n == 8 ? 1 : 3;          // 16 / n - 1
-                    const int L = (j4 & m) * 4 * n + (ln >> 4) * n + (ln & (n - 1));
-                    const u32x4 wv = ringv[(size_t)slot * (SR_SLOT / 16) + L];
-                    if (live) {
-                        mac<WT>(acc[t], wv, aj);
-                        if constexpr (HL) { if (alo != a) mac<WT>(acc[t], wv, alj); }
+                    for (int j4 = 0; j4 < 4; ++j4) {
+                        const int j = 4 * q + j4;
+                        if (ks + j < nst) d2_prepare<WT, HL>(S, &a[j * AFR], &alo[j * AFR], ks + j, cbase, cD);
+                    }
+                }
+            }
+            if (!ring_wait(S, cs, g0 + G.slots)) return false;
+            u32x4 wv[4];
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) wv[j4] = part(s0, j4, 0);
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const int j = 4 * q + j4;
+                if (ks + j < nst) {
+                    mac<WT>(acc[0], wv[j4], &a[j * AFR]);
+                    if constexpr (HL) { if (alo != a) mac<WT>(acc[0], wv[j4], &alo[j * AFR]); }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const int j = 4 * q + j4;
+                u32x4 *aj = &a[j * AFR], *alj = &alo[j * AFR];
+                const bool live = ks + j < nst;
+                if constexpr (C) {
+                    if (conv && live) d2_prepare<WT, HL>(S, aj, alj, ks + j, cbase, cD);
+                }
+                if (!ring_wait(S, cs, g0 + G.cnt[j4])) return false;
+                u32x4 wv[SR_MAXT];
+#pragma unroll
+                for (int t = 0; t < SR_MAXT; ++t) wv[t] = part(s0, j4, t);
+                if (live) {
+#pragma unroll
+                    for (int t = 0; t < SR_MAXT; ++t) {
+                        if (t < nt) {
+                            mac<WT>(acc[t], wv[t], aj);
+                            if constexpr (HL) { if (alo != a) mac<WT>(acc[t], wv[t], alj); }
+                        }
                     }
                 }
             }
@@ -1068,7 +1110,7 @@ __device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, const Grp &G, u32x
 }
 
 // all k steps of one wave: up to SR_MAXPASS passes, activations double-buffered
-template <int WT, bool C>
+template <int WT, bool C, bool ONE>
 __device__ __forceinline__ bool gemm_steps(SrLds &S, Cons &cs, const Grp &G, const char *act, int ks0, int nst, int nt, int npass,
                                            bool conv, bool hl, const float *cbase, const float *cD, f32x4 (&acc)[SR_MAXT],
                                            unsigned p) {
@@ -1094,7 +1136,7 @@ __device__ __forceinline__ bool gemm_steps(SrLds &S, Cons &cs, const Grp &G, con
                 if (ps < npass) {
                     load_pass(ps, a0, 0);
                     load_pass(ps, a1, lo_off);
-                    if (!gemm_pass<WT, C>(S, cs, G, a0, a1, ks0 + ps * NF, nst, nt, conv, cbase, cD, acc)) return false;
+                    if (!gemm_pass<WT, C, ONE>(S, cs, G, a0, a1, ks0 + ps * NF, nst, nt, conv, cbase, cD, acc)) return false;
                 }
             }
             return true;
@@ -1108,12 +1150,12 @@ __device__ __forceinline__ bool gemm_steps(SrLds &S, Cons &cs, const Grp &G, con
         if (!ring_wait(S, cs, cs.seq + G.cnt[0])) return false;
         dbg_at(p, 4);
     }
-    if (!gemm_pass<WT, C>(S, cs, G, a0, a0, ks0, nst, nt, conv, cbase, cD, acc)) return false;
+    if (!gemm_pass<WT, C, ONE>(S, cs, G, a0, a0, ks0, nst, nt, conv, cbase, cD, acc)) return false;
     if (npass > 1) {
         if (npass > 2) load_pass(2, a0, 0);
-        if (!gemm_pass<WT, C>(S, cs, G, a1, a1, ks0 + NF, nst, nt, conv, cbase, cD, acc)) return false;
+        if (!gemm_pass<WT, C, ONE>(S, cs, G, a1, a1, ks0 + NF, nst, nt, conv, cbase, cD, acc)) return false;
         if (npass > 2) {
-            if (!gemm_pass<WT, C>(S, cs, G, a0, a0, ks0 + 2 * NF, nst, nt, conv, cbase, cD, acc)) return false;
+            if (!gemm_pass<WT, C, ONE>(S, cs, G, a0, a0, ks0 + 2 * NF, nst, nt, conv, cbase, cD, acc)) return false;
         }
     }
     return true;
@@ -1123,7 +1165,7 @@ __device__ __forceinline__ bool gemm_steps(SrLds &S, Cons &cs, const Grp &G, con
 // register allocator spill heavily.  Arguments arrive in VGPRs and are made
 // scalar again.
 // Returns the consumer's next ring slot, or ~0u if the kernel is aborting.
-template <int WT, int D, bool C>
+template <int WT, int D, bool C, bool ONE>
 __device__ __attribute__((noinline)) unsigned gemm_phase(int kind, int l, unsigned p, unsigned seq) {
     constexpr int KW = TR<WT>::KW, AFR = TR<WT>::AFR;
     kind = __builtin_amdgcn_readfirstlane(kind);
@@ -1131,7 +1173,7 @@ __device__ __attribute__((noinline)) unsigned gemm_phase(int kind, int l, unsign
     p = __builtin_amdgcn_readfirstlane(p);
     Cons cs{(unsigned)__builtin_amdgcn_readfirstlane(seq), 0u};
     const int lane = lane_id(), v = wave_id();
-    const int nt = gemm_nt(kind);
+    const int nt = ONE ? 1 : gemm_nt(kind);
     char *lb = layer_buf(l);
     if (nt > 0) {
         const int K = gemm_K(kind), nst = K / KW, npass = gemm_npass<WT>(nst);
@@ -1167,7 +1209,7 @@ __device__ __attribute__((noinline)) unsigned gemm_phase(int kind, int l, unsign
         const Grp G = grp_layout<WT>(kind, l, nt);
         // with the DFlash2 wrap every GEMM input but o_proj's has two planes
         const bool hl = C && TR<WT>::AB == 2 && kind != K_O;
-        const bool ok = gemm_steps<WT, C>(S, cs, G, act, ks0, nst, nt, npass, conv, hl, cbase, cD, acc, p);
+        const bool ok = gemm_steps<WT, C, ONE>(S, cs, G, act, ks0, nst, nt, npass, conv, hl, cbase, cD, acc, p);
         dbg_at(p, 2);
         if (!ok) return ~0u;
 #pragma unroll
@@ -1526,11 +1568,32 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
             const size_t row = (size_t)item * GQ + qi;
             char *po = lb + SS.o_po;
             float *pml = (float *)(lb + SS.o_pml);
+            // The wave's 16 rows of partial O are one contiguous block of
+            // 16 D AB bytes.  Lane (r16, g) holds dims 16 t + 4 g .. + 3 of row
+            // r16; stored as they are, an instruction writes 16 pieces of
+            // 4 AB bytes, and such partial-line write-through stores cost
+            // several microseconds per wave.  So the rows go through a 1 KB
+            // LDS buffer of the wave, RPR rows at a time, and every store
+            // instruction writes RPR whole rows.
+            constexpr int RB2 = D * AB, RPR = 1024 / RB2, LPR = RB2 / 16;
+            static_assert(1024 % RB2 == 0 && 16 % RPR == 0, "whole rows per 1 KB round");
+            static_assert(sizeof(S.red) >= 4 * STG + 16 * KRS + KRB + SR_CW * 1024, "transpose buffers fit the reduction area");
+            char *tb = bv + KRB + 1024 * v;
+            char *wblk = po + ((size_t)item * GQ + v * 16) * RB2;
 #pragma unroll
-            for (int t = 0; t < NDT; ++t) {
-                const size_t e = row * D + 16 * t + 4 * g;
-                if constexpr (AB == 4) st16(po, e * 4, __builtin_bit_cast(u32x4, st.o[t]));
-                else st8(po, e * 2, u32x2{bf2(st.o[t][0], st.o[t][1]), bf2(st.o[t][2], st.o[t][3])});
+            for (int j = 0; j < 16 / RPR; ++j) {
+                if (r16 / RPR == j) {
+                    char *dst = tb + (r16 % RPR) * RB2 + 4 * g * AB;
+#pragma unroll
+                    for (int t = 0; t < NDT; ++t) {
+                        if constexpr (AB == 4) *reinterpret_cast<f32x4 *>(dst + 16 * t * AB) = st.o[t];
+                        else *reinterpret_cast<u32x2 *>(dst + 16 * t * AB) = u32x2{bf2(st.o[t][0], st.o[t][1]), bf2(st.o[t][2], st.o[t][3])};
+                    }
+                }
+                cbar();
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(tb + 16 * lane);
+                cbar();
+                st16(wblk, (size_t)j * 1024 + 16 * lane, x);
             }
             if (g == 0) st8(pml, row * 8, u32x2{__float_as_uint(st.m), __float_as_uint(st.l)});
         }
@@ -1692,7 +1755,8 @@ __device__ __forceinline__ bool compute_main(SrLds &S) {
             if (k == K_A) ok = attn_phase<WT, D>(S, cs, l, p);
             else if (k == K_M) ok = merge_phase<WT, D>(S, l, p);
             else {
-                cs.seq = gemm_phase<WT, D, C>(k, l, p, cs.seq);
+                // a workgroup with a single tile runs the one-tile build
+                cs.seq = gemm_nt(k) == 1 ? gemm_phase<WT, D, C, true>(k, l, p, cs.seq) : gemm_phase<WT, D, C, false>(k, l, p, cs.seq);
                 ok = cs.seq != ~0u;
             }
             if (!ok) return false;
