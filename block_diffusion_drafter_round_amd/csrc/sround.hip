@@ -719,19 +719,18 @@ __device__ __forceinline__ bool wait_phase(SrLds &S, unsigned p, unsigned E) {
     return true;
 }
 
-// 1/rms of the 16 rows from partial sums of squares [16][nwg] (wave 0).
+// 1/rms of the 16 rows from partial sums of squares [nwg][16] (wave 0).
 // Lane (r, q) sums workgroups q, q + 4, ...; every load is issued before the
-// first add.
+// first add, and each load instruction reads 4 workgroups' 64 bytes at once.
 __device__ __forceinline__ void compute_rinv(SrLds &S, const float *ssq, unsigned p, int width) {
     const int lane = lane_id(), r = lane & 15, q = lane >> 4;
     const int nwg = gridDim.x;
-    const float *src = ssq + (size_t)r * nwg;
     constexpr int NPL = 256 / 4;                       // workgroups per lane at most
     float v[NPL];
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int w = q + 4 * i;
-        v[i] = src[w < nwg ? w : 0];
+        v[i] = ssq[(size_t)(w < nwg ? w : 0) * 16 + r];
     }
     float s = 0.f;
 #pragma unroll
@@ -802,7 +801,8 @@ __device__ __forceinline__ void emit_input(SrLds &S, const float *gain, char *fr
             const float4 x = *reinterpret_cast<const float4 *>(&S.xown[lane][c]);
             s += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
         }
-        st4(ssq, ((size_t)lane * gridDim.x + blockIdx.x) * 4, __float_as_uint(s));
+        // [workgroup][row]: the 16 sums of one workgroup are one 64-byte store
+        st4(ssq, ((size_t)blockIdx.x * 16 + lane) * 4, __float_as_uint(s));
     }
 }
 
@@ -1486,34 +1486,37 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
         for (int t = 0; t < NDT; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (it.last && actw) {
             // the block's own keys: normed + roped k and raw v of the b block
-            // rows, read from the LDS copy.  Lanes of tile keys 16..31 (no
-            // such rows) take zeros; their scores are masked anyway.
-            u32x4 kraw[2][HW], vraw[NDT][A::VH];
+            // rows, read from the LDS copy.  Block key k takes position
+            // 8 (k / 4) + k % 4 of a 32-key block, so every block key is a row
+            // of key tile 0 (lane r16 holds key r16) and tile 1 is empty: one
+            // head norm + rope per lane, and lane group g's positions
+            // 8 g .. 8 g + 3 hold keys 4 g .. 4 g + 3 (the others are masked).
+            u32x4 kraw[HW], vraw[NDT][A::VH];
+            {
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(bk + r16 * KRS + g * (D / 4) * AB);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const int key = 8 * (r16 >> 2) + 4 * kt + (r16 & 3);
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(bk + key * KRS + g * (D / 4) * AB);
-#pragma unroll
-                for (int i = 0; i < HW; ++i) kraw[kt][i] = key < 16 ? src[i] : u32x4{0, 0, 0, 0};
+                for (int i = 0; i < HW; ++i) kraw[i] = src[i];
             }
 #pragma unroll
-            for (int t = 0; t < NDT; ++t)
-#pragma unroll
-                for (int hv = 0; hv < A::VH; ++hv) {
-                    const int e = (16 * t + r16) * 16 + 8 * (g & 1) + 4 * hv;
-                    vraw[t][hv] = *reinterpret_cast<const u32x4 *>(bv + (size_t)e * AB);
+            for (int t = 0; t < NDT; ++t) {
+                const char *vsrc = bv + ((size_t)(16 * t + r16) * 16 + 4 * g) * AB;   // v^T row 16 t + r16, keys 4 g ..
+                if constexpr (A::VH == 2) {
+                    vraw[t][0] = *reinterpret_cast<const u32x4 *>(vsrc);
+                    vraw[t][A::VH - 1] = u32x4{0, 0, 0, 0};
+                } else {
+                    const u32x2 x2 = *reinterpret_cast<const u32x2 *>(vsrc);
+                    vraw[t][0] = u32x4{x2.x, x2.y, 0, 0};
                 }
-            u32x4 kb[2][NC];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const int key = 8 * (r16 >> 2) + 4 * kt + (r16 & 3);
+            }
+            u32x4 kb[NC];
+            {
                 float x[NQV];
-                decode_head<WT, D>(x, kraw[kt]);
-                norm_rope<WT, D>(x, stg + D, stg + CS0 + key * CSR, SS.mscale);
-                if (v == 0 && key < SS.b) {   // block K row to the cache (rows len + key)
+                decode_head<WT, D>(x, kraw);
+                norm_rope<WT, D>(x, stg + D, stg + CS0 + r16 * CSR, SS.mscale);
+                if (v == 0 && r16 < SS.b) {   // block K row to the cache (row len + r16)
                     constexpr int PQ = A::PQ;
                     char *kcache = SS.kc + (size_t)l * SS.kv_lstride;
-                    const size_t rowb = (((size_t)it.h * SS.cap + SS.len + key) * D) * A::KVB;
+                    const size_t rowb = (((size_t)it.h * SS.cap + SS.len + r16) * D) * A::KVB;
 #pragma unroll
                     for (int c = 0; c < NC; ++c) {
                         const size_t off = rowb + (size_t)(4 * PQ * c + PQ * g) * A::KVB;
@@ -1528,18 +1531,18 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     if constexpr (WT == WT_F32) {
-                        kb[kt][c] = u32x4{__float_as_uint(x[4 * c]), __float_as_uint(x[4 * c + 1]), __float_as_uint(x[4 * c + 2]),
-                                          __float_as_uint(x[4 * c + 3])};
+                        kb[c] = u32x4{__float_as_uint(x[4 * c]), __float_as_uint(x[4 * c + 1]), __float_as_uint(x[4 * c + 2]),
+                                      __float_as_uint(x[4 * c + 3])};
                     } else {
-                        kb[kt][c] = u32x4{bf2(x[8 * c], x[8 * c + 1]), bf2(x[8 * c + 2], x[8 * c + 3]),
-                                          bf2(x[8 * c + 4], x[8 * c + 5]), bf2(x[8 * c + 6], x[8 * c + 7])};
+                        kb[c] = u32x4{bf2(x[8 * c], x[8 * c + 1]), bf2(x[8 * c + 2], x[8 * c + 3]),
+                                      bf2(x[8 * c + 4], x[8 * c + 5]), bf2(x[8 * c + 6], x[8 * c + 7])};
                     }
                 }
             }
-            auto kf = [&](int kt, int c) -> u32x4 { return kb[kt][c]; };
-            auto vf = [&](int t, int hv) -> u32x4 { return g >= 2 ? u32x4{0, 0, 0, 0} : vraw[t][hv]; };
-            const int kend = SS.b - 8 * g;
-            auto valid = [&](int i) { return i < kend; };
+            auto kf = [&](int kt, int c) -> u32x4 { return kt == 0 ? kb[c] : u32x4{0, 0, 0, 0}; };
+            auto vf = [&](int t, int hv) -> u32x4 { return vraw[t][hv]; };
+            const int b4 = SS.b - 4 * g;
+            auto valid = [&](int i) { return i < 4 && i < b4; };
             attn_block<WT, D>(st, qf, kf, vf, valid);
         }
         for (int blk = 0; blk < it.nblk; ++blk) {
