@@ -209,6 +209,7 @@ struct SrLds {
     unsigned done;             // compute-wave arrivals (8 per phase)
     unsigned stg;              // compute-wave arrivals at the attention staging (8 per layer)
     unsigned abort_;
+    unsigned sink_;            // never read: keeps the service wave's L2 prefetch loads alive
 };
 
 // the workgroup's LDS (each kernel instance allocates its own copy)
@@ -697,11 +698,11 @@ __device__ __forceinline__ bool wait_phase(SrLds &S, unsigned p, unsigned E) {
             if (__all(seen)) break;
             if (lds_ld(&S.abort_)) return false;
             if (++spins > SPIN_LIMIT / 8) { set_error(S); return false; }
-            // about 1.7 us between polls: each poll reads 64 lines device-wide
+            // about 0.85 us between polls: each poll reads 64 lines device-wide
             // from every workgroup, and tighter polling slows the whole grid
-            // (measured: polling without a pause costs about 2% of a round;
-            // pauses much longer than this delay the phase starts instead)
-            __builtin_amdgcn_s_sleep(64);
+            // (measured: polling without a pause costs about 2% of a round,
+            // and pauses of 0.4 or 1.7 us were slower than this one)
+            __builtin_amdgcn_s_sleep(32);
         }
         if (blockIdx.x == 0 && lane == 0) {
             if (SS.trace && 8 * p < SR_TRACE) SS.trace[8 * p] = wall_clock64();
@@ -1028,10 +1029,9 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
 // registers.  The ring parts of a step are read together before its MFMAs,
 // so the LDS latency is paid about once per step rather than once per part:
 // every tile's part of a step (tiles past nt read a valid part that is not
-// used).  ONE (a workgroup with exactly one tile, built as its own function
-// so that it holds a single accumulator) reads the parts of all four steps of
-// a group at once.
-template <int WT, bool C, bool ONE>
+// used).  The build for exactly NTF = 1 tile (its own function, so it holds
+// a single accumulator) reads the parts of all four steps of a group at once.
+template <int WT, bool C, int NTF>
 __device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, const Grp &G, u32x4 *a, u32x4 *alo, int ks, int nst, int nt,
                                           bool conv, const float *cbase, const float *cD, f32x4 (&acc)[SR_MAXT]) {
     constexpr int AFR = TR<WT>::AFR, NF = PassCfg<WT>::NF;
@@ -1057,7 +1057,7 @@ __device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, const Grp &G, u32x
     for (int q = 0; q < NF / 4; ++q) {
         const unsigned g0 = cs.seq;
         const unsigned s0 = __builtin_amdgcn_readfirstlane(g0 % SR_NSLOT);
-        if constexpr (ONE) {
+        if constexpr (NTF > 0) {
             if constexpr (C) {
                 if (conv) {
 #pragma unroll
@@ -1068,15 +1068,24 @@ __device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, const Grp &G, u32x
                 }
             }
             if (!ring_wait(S, cs, g0 + G.slots)) return false;
-            u32x4 wv[4];
+            constexpr int B = 4 / NTF;                   // steps per batch of 4 parts
 #pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) wv[j4] = part(s0, j4, 0);
+            for (int j0 = 0; j0 < 4; j0 += B) {
+                u32x4 wv[B][NTF];
 #pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
-                const int j = 4 * q + j4;
-                if (ks + j < nst) {
-                    mac<WT>(acc[0], wv[j4], &a[j * AFR]);
-                    if constexpr (HL) { if (alo != a) mac<WT>(acc[0], wv[j4], &alo[j * AFR]); }
+                for (int jb = 0; jb < B; ++jb)
+#pragma unroll
+                    for (int t = 0; t < NTF; ++t) wv[jb][t] = part(s0, j0 + jb, t);
+#pragma unroll
+                for (int jb = 0; jb < B; ++jb) {
+                    const int j = 4 * q + j0 + jb;
+                    if (ks + j < nst) {
+#pragma unroll
+                        for (int t = 0; t < NTF; ++t) {
+                            mac<WT>(acc[t], wv[jb][t], &a[j * AFR]);
+                            if constexpr (HL) { if (alo != a) mac<WT>(acc[t], wv[jb][t], &alo[j * AFR]); }
+                        }
+                    }
                 }
             }
         } else {
@@ -1110,7 +1119,7 @@ __device__ __forceinline__ bool gemm_pass(SrLds &S, Cons &cs, const Grp &G, u32x
 }
 
 // all k steps of one wave: up to SR_MAXPASS passes, activations double-buffered
-template <int WT, bool C, bool ONE>
+template <int WT, bool C, int NTF>
 __device__ __forceinline__ bool gemm_steps(SrLds &S, Cons &cs, const Grp &G, const char *act, int ks0, int nst, int nt, int npass,
                                            bool conv, bool hl, const float *cbase, const float *cD, f32x4 (&acc)[SR_MAXT],
                                            unsigned p) {
@@ -1136,7 +1145,7 @@ __device__ __forceinline__ bool gemm_steps(SrLds &S, Cons &cs, const Grp &G, con
                 if (ps < npass) {
                     load_pass(ps, a0, 0);
                     load_pass(ps, a1, lo_off);
-                    if (!gemm_pass<WT, C, ONE>(S, cs, G, a0, a1, ks0 + ps * NF, nst, nt, conv, cbase, cD, acc)) return false;
+                    if (!gemm_pass<WT, C, NTF>(S, cs, G, a0, a1, ks0 + ps * NF, nst, nt, conv, cbase, cD, acc)) return false;
                 }
             }
             return true;
@@ -1150,12 +1159,12 @@ __device__ __forceinline__ bool gemm_steps(SrLds &S, Cons &cs, const Grp &G, con
         if (!ring_wait(S, cs, cs.seq + G.cnt[0])) return false;
         dbg_at(p, 4);
     }
-    if (!gemm_pass<WT, C, ONE>(S, cs, G, a0, a0, ks0, nst, nt, conv, cbase, cD, acc)) return false;
+    if (!gemm_pass<WT, C, NTF>(S, cs, G, a0, a0, ks0, nst, nt, conv, cbase, cD, acc)) return false;
     if (npass > 1) {
         if (npass > 2) load_pass(2, a0, 0);
-        if (!gemm_pass<WT, C, ONE>(S, cs, G, a1, a1, ks0 + NF, nst, nt, conv, cbase, cD, acc)) return false;
+        if (!gemm_pass<WT, C, NTF>(S, cs, G, a1, a1, ks0 + NF, nst, nt, conv, cbase, cD, acc)) return false;
         if (npass > 2) {
-            if (!gemm_pass<WT, C, ONE>(S, cs, G, a0, a0, ks0 + 2 * NF, nst, nt, conv, cbase, cD, acc)) return false;
+            if (!gemm_pass<WT, C, NTF>(S, cs, G, a0, a0, ks0 + 2 * NF, nst, nt, conv, cbase, cD, acc)) return false;
         }
     }
     return true;
@@ -1165,7 +1174,7 @@ __device__ __forceinline__ bool gemm_steps(SrLds &S, Cons &cs, const Grp &G, con
 // register allocator spill heavily.  Arguments arrive in VGPRs and are made
 // scalar again.
 // Returns the consumer's next ring slot, or ~0u if the kernel is aborting.
-template <int WT, int D, bool C, bool ONE>
+template <int WT, int D, bool C, int NTF>
 __device__ __attribute__((noinline)) unsigned gemm_phase(int kind, int l, unsigned p, unsigned seq) {
     constexpr int KW = TR<WT>::KW, AFR = TR<WT>::AFR;
     kind = __builtin_amdgcn_readfirstlane(kind);
@@ -1173,7 +1182,7 @@ __device__ __attribute__((noinline)) unsigned gemm_phase(int kind, int l, unsign
     p = __builtin_amdgcn_readfirstlane(p);
     Cons cs{(unsigned)__builtin_amdgcn_readfirstlane(seq), 0u};
     const int lane = lane_id(), v = wave_id();
-    const int nt = ONE ? 1 : gemm_nt(kind);
+    const int nt = NTF > 0 ? NTF : gemm_nt(kind);
     char *lb = layer_buf(l);
     if (nt > 0) {
         const int K = gemm_K(kind), nst = K / KW, npass = gemm_npass<WT>(nst);
@@ -1209,7 +1218,7 @@ __device__ __attribute__((noinline)) unsigned gemm_phase(int kind, int l, unsign
         const Grp G = grp_layout<WT>(kind, l, nt);
         // with the DFlash2 wrap every GEMM input but o_proj's has two planes
         const bool hl = C && TR<WT>::AB == 2 && kind != K_O;
-        const bool ok = gemm_steps<WT, C, ONE>(S, cs, G, act, ks0, nst, nt, npass, conv, hl, cbase, cD, acc, p);
+        const bool ok = gemm_steps<WT, C, NTF>(S, cs, G, act, ks0, nst, nt, npass, conv, hl, cbase, cD, acc, p);
         dbg_at(p, 2);
         if (!ok) return ~0u;
 #pragma unroll
@@ -1758,8 +1767,10 @@ __device__ __forceinline__ bool compute_main(SrLds &S) {
             if (k == K_A) ok = attn_phase<WT, D>(S, cs, l, p);
             else if (k == K_M) ok = merge_phase<WT, D>(S, l, p);
             else {
-                // a workgroup with a single tile runs the one-tile build
-                cs.seq = gemm_nt(k) == 1 ? gemm_phase<WT, D, C, true>(k, l, p, cs.seq) : gemm_phase<WT, D, C, false>(k, l, p, cs.seq);
+                // a workgroup with a single tile runs the one-tile build (a
+                // two-tile build measured slower: more code for the
+                // instruction cache than it saves in the step loop)
+                cs.seq = gemm_nt(k) == 1 ? gemm_phase<WT, D, C, 1>(k, l, p, cs.seq) : gemm_phase<WT, D, C, 0>(k, l, p, cs.seq);
                 ok = cs.seq != ~0u;
             }
             if (!ok) return false;
@@ -1772,9 +1783,38 @@ __device__ __forceinline__ bool compute_main(SrLds &S) {
     return lds_ld(&S.abort_) == 0;
 }
 
+// The tail of this workgroup's gate|up weight run (the slots past what the
+// ring can hold when the phase opens) into L2, so the loader's reads of those
+// slots hit there: one 4-byte load per 128-byte line, all issued before the
+// first wait.  The loaded values are folded into a word that is stored only
+// under a condition no lane meets, which keeps the loads alive.
+template <int WT>
+__device__ __forceinline__ void prefetch_g_tail(SrLds &S, int l) {
+    const long long run = pk_wg_bytes(WT, K_G, SS.H, SS.I, SS.qd, SS.cq, SS.ch, SS.ci);
+    const long long lo = (long long)SR_NSLOT * SR_SLOT;
+    if (run <= lo) return;
+    const char *base = pk_run<WT>(K_G, l);
+    const int lane = lane_id();
+    constexpr int NPF = 16;                       // up to 16 slots past the ring
+    unsigned v[NPF];
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+        long long off = lo + (long long)i * SR_SLOT + 128 * lane;
+        off = off < run ? off : lo;               // stays inside the run
+        v[i] = *reinterpret_cast<const volatile unsigned *>(base + off);
+    }
+    unsigned x = 0;
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) x ^= v[i];
+    if (x == 0x9E3779B9u && lane == 64) S.sink_ = x;   // lane ids stop at 63
+}
+
 // Service wave: the rows' 1/rms of every norm-consuming phase (and of the
 // final norm) as soon as the phase opens, from the producers' partial sums
-// of squares, so no GEMM wave starts its share late.
+// of squares, so no GEMM wave starts its share late.  When gate|up opens it
+// first starts the L2 prefetch of the run's tail (the rows' scales are needed
+// only by that phase's epilogue).
+template <int WT>
 __device__ __forceinline__ void service_main(SrLds &S) {
     const int nl = SS.nl, np = npl();
     unsigned p = 1;
@@ -1783,6 +1823,7 @@ __device__ __forceinline__ void service_main(SrLds &S) {
             const int k = kind_at(i);
             if (k == K_Q || k == K_G || k == K_DA || k == K_DM) {
                 if (!wait_phase(S, p, 0u)) return;
+                if (k == K_G) prefetch_g_tail<WT>(S, l);
                 compute_rinv(S, (const float *)(layer_buf(l) + ((k == K_Q || k == K_DA) ? SS.o_ssa : SS.o_ssm)), p, SS.H);
             }
         }
@@ -1830,7 +1871,7 @@ __global__ __launch_bounds__(SR_THREADS, 1) void sround_kernel(SrArgs a) {
         return;
     }
     if (wave == SR_CW + 1) {
-        service_main(S);
+        service_main<WT>(S);
         return;
     }
     // compute waves
