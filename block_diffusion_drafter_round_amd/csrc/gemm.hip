@@ -24,6 +24,8 @@
 //   arrive sums the partials in split order and applies the epilogue.  The
 //   result is therefore independent of scheduling.  Only workgroup-scope
 //   fences are used (no L2 writeback / invalidate).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -37,11 +39,20 @@ template <> struct WCfg<WT_F32>  { static constexpr int KS = 16, ES = 4, FR = 1;
 
 __device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
 
-__device__ __forceinline__ void st_coherent(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Device-coherent 16-byte store / load of split-K partials (SC1: written
+// through to memory, read past the XCD's L2), through a buffer resource whose
+// base is uniform over the wave; the byte offset is per lane.  A lane's four
+// partial sums are one 16-byte access, so a wave writes and reads 1 KB runs
+// (scattered 4-byte write-through stores cost far more per byte).
+constexpr int CPOL_SC1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const float *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, 0x7fffffff, 0x00020000);
 }
-__device__ __forceinline__ float ld_coherent(const float *p) {
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st_coherent16(float *base, uint32_t off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), part_rsrc(base), off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ f32x4 ld_coherent16(const float *base, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(part_rsrc(base), off, 0, CPOL_SC1));
 }
 
 // Stage A[m0 .. m0+16*MT)[k0 .. k0 + NSTEP*KS) into LDS fragments, in two
@@ -130,7 +141,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     constexpr int KS = WCfg<WT>::KS, ES = WCfg<WT>::ES, FR = WCfg<WT>::FR;
     constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
     constexpr int KCH = NSTEP * KS;                      // K per staged chunk
-    __shared__ u32x4 lds[MT * NSTEP * FR * 64];
+    __shared__ u32x4 lds[2][MT * NSTEP * FR * 64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r16 = lane & 15;
@@ -165,36 +176,56 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
         for (int a = 0; a < NACC; ++a) acc[mt][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int lane_koff = g * (KS / 4);                  // this lane's K offset inside a step
-    for (int k0 = kbeg; k0 < kend; k0 += KCH) {
-        const int kvalid = min(KCH, kend - k0);          // a multiple of KS
-        const int nst = kvalid / KS;
-        // 1. the chunk's activation loads, then all of its weight loads
-        AStage<WT, MT, NSTEP> ast;
-        load_a<WT, MT, NSTEP>(ast, p, m0, k0, kvalid);
-        asm volatile("" ::: "memory");                   // keep the activation loads ahead of the weights'
-        u32x4 wv[NSTEP][NACC];
+    // The chunks of this split are software-pipelined: chunk c + 1's
+    // activation and weight loads are issued before chunk c's MFMAs, into the
+    // other of two register buffers (weights) and LDS buffers (activation
+    // fragments).  One barrier per chunk: put_a of chunk c writes LDS buffer
+    // c & 1, last read by the MFMAs of chunk c - 2, which every wave finished
+    // before the barrier of chunk c - 1.
+    AStage<WT, MT, NSTEP> ast;
+    u32x4 wv[2][NSTEP][NACC];
+    auto load_w = [&](u32x4 (&w)[NSTEP][NACC], int k0, int nst) {
 #pragma unroll
         for (int a = 0; a < NACC; ++a) {
             const char *wr = wbase[a] + ((size_t)(ncol + r16) * K + k0 + lane_koff) * ES;
             // unconditional (steps past the chunk reload its last one), so the
             // compiler counts them and waits for the activations alone first
 #pragma unroll
-            for (int s = 0; s < NSTEP; ++s) wv[s][a] = ld_stream16(wr + (size_t)min(s, nst - 1) * KS * ES);
+            for (int s = 0; s < NSTEP; ++s) w[s][a] = ld_stream16(wr + (size_t)min(s, nst - 1) * KS * ES);
         }
-        // 2. activations -> LDS fragments (the weight loads stay in flight)
-        if (k0 != kbeg) __syncthreads();
-        put_a<WT, MT, NSTEP>(lds, ast, p, m0, kvalid);
+    };
+    auto chunk = [&](auto bufc, int k0) -> bool {
+        constexpr int B = decltype(bufc)::value;
+        const int kvalid = min(KCH, kend - k0);           // a multiple of KS
+        const int nst = kvalid / KS;
+        put_a<WT, MT, NSTEP>(lds[B], ast, p, m0, kvalid);
+        const int k1 = k0 + KCH;
+        const bool more = k1 < kend;
+        if (more) {
+            load_a<WT, MT, NSTEP>(ast, p, m0, k1, min(KCH, kend - k1));
+            asm volatile("" ::: "memory");               // activation loads ahead of the weights'
+            load_w(wv[B ^ 1], k1, min(KCH, kend - k1) / KS);
+        }
         __syncthreads();
-        // 3. MFMAs
 #pragma unroll
         for (int s = 0; s < NSTEP; ++s)
             if (s < nst)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const u32x4 *af = lds + ((mt * NSTEP + s) * FR) * 64 + lane;
+                const u32x4 *af = lds[B] + ((mt * NSTEP + s) * FR) * 64 + lane;
 #pragma unroll
-                for (int a = 0; a < NACC; ++a) mac_step<WT>(acc[mt][a], wv[s][a], af);
+                for (int a = 0; a < NACC; ++a) mac_step<WT>(acc[mt][a], wv[B][s][a], af);
             }
+        return more;
+    };
+    if (kbeg < kend) {
+        load_a<WT, MT, NSTEP>(ast, p, m0, kbeg, min(KCH, kend - kbeg));
+        asm volatile("" ::: "memory");
+        load_w(wv[0], kbeg, min(KCH, kend - kbeg) / KS);
+        for (int k0 = kbeg;; k0 += 2 * KCH) {
+            if (!chunk(std::integral_constant<int, 0>{}, k0)) break;
+            if (!chunk(std::integral_constant<int, 1>{}, k0 + KCH)) break;
+        }
     }
 
     // ---- split-K: the last workgroup of the column group reduces in split order ----
@@ -208,9 +239,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int a = 0; a < NACC; ++a)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    st_coherent(mine + ((mt * NACC + a) * 4 + wave) * 256 + lane * 4 + j, acc[mt][a][j]);
+                st_coherent16(mine, (uint32_t)((((mt * NACC + a) * 4 + wave) * 256 + lane * 4) * 4), acc[mt][a]);
         // every partial store must have completed before this workgroup is counted
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -229,14 +258,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int a = 0; a < NACC; ++a) {
                 f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-                const float *q0 = part + ((mt * NACC + a) * 4 + wave) * 256 + lane * 4;
+                const uint32_t q0 = (uint32_t)((((mt * NACC + a) * 4 + wave) * 256 + lane * 4) * 4);
                 for (int s0 = 0; s0 < p.ksplit; s0 += MAXS) {
                     f32x4 pv[MAXS];
 #pragma unroll
                     for (int s = 0; s < MAXS; ++s)
-                        if (s0 + s < p.ksplit)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) pv[s][j] = ld_coherent(q0 + (size_t)(s0 + s) * PER + j);
+                        if (s0 + s < p.ksplit) pv[s] = ld_coherent16(part, q0 + (uint32_t)((s0 + s) * PER * 4));
 #pragma unroll
                     for (int s = 0; s < MAXS; ++s)
                         if (s0 + s < p.ksplit) v += pv[s];
@@ -286,8 +313,8 @@ static int ks_of(int wt) { return wt == WT_BF16 ? 32 : wt == WT_FP8 ? 64 : 16; }
 // steps per staged chunk for a given instantiation
 static int nstep_of(int wt, int mt, int epi) {
     if (mt > 1) return wt == WT_FP8 ? 2 : 4;
-    if (wt == WT_FP8) return epi == EPI_SWIGLU ? 4 : 8;
-    return epi == EPI_SWIGLU ? 8 : 16;
+    if (wt == WT_FP8) return epi == EPI_SWIGLU ? 2 : 4;
+    return epi == EPI_SWIGLU ? 4 : 8;
 }
 
 int gemm_plan(GemmArgs &a) {
@@ -301,14 +328,21 @@ int gemm_plan(GemmArgs &a) {
     const int kch = nstep_of(a.wtype, a.mt, a.epi) * ks_of(a.wtype);
     const int nchunks = (a.K + kch - 1) / kch;
     const int base = a.ngroups * a.mgroups;
-    // split K until there are ~2 workgroups per CU, one or more chunks per split
-    int ksplit = 1;
-    const int target = 512;
-    if (base < target) ksplit = (target + base - 1) / base;
-    if (ksplit > nchunks) ksplit = nchunks;
+    // K split: the one that minimises (workgroups per CU, rounded up) x
+    // (chunks per split + 2), the 2 standing for a split's first round trip
+    // and its reduction; ties go to fewer workgroups.  With whole chunks per
+    // split this lands on multiples of 256 workgroups where the shape allows.
     const size_t per = (size_t)a.mt * nacc * 4 * 256;
-    while (ksplit > 1 && (size_t)base * ksplit * per > GEMM_PART_FLOATS) --ksplit;
-    if (ksplit > 1 && base > GEMM_MAX_COUNTERS) ksplit = 1;
+    int ksplit = 1;
+    long long best = -1;
+    for (int ks = 1; ks <= nchunks; ++ks) {
+        const int cp = (nchunks + ks - 1) / ks, ks2 = (nchunks + cp - 1) / cp;
+        if (ks2 != ks) continue;
+        if (ks > 1 && ((size_t)base * ks * per > GEMM_PART_FLOATS || base > GEMM_MAX_COUNTERS)) break;
+        const long long wg = (long long)base * ks, per_cu = (wg + GEMM_CUS - 1) / GEMM_CUS;
+        const long long cost = per_cu * (cp + 2);
+        if (best < 0 || cost < best) { best = cost; ksplit = ks; }
+    }
     const int chunks_per = (nchunks + ksplit - 1) / ksplit;
     a.kchunk = chunks_per * kch;
     a.ksplit = (a.K + a.kchunk - 1) / a.kchunk;
@@ -319,7 +353,7 @@ template <int WT, int EPI>
 static void launch_wt_epi(const GemmArgs &a, hipStream_t s) {
     dim3 grid(a.ngroups * a.ksplit, a.mgroups), block(256);
     constexpr bool SW = EPI == EPI_SWIGLU;
-    constexpr int N1 = WT == WT_FP8 ? (SW ? 4 : 8) : (SW ? 8 : 16);
+    constexpr int N1 = WT == WT_FP8 ? (SW ? 2 : 4) : (SW ? 4 : 8);
     constexpr int N4 = WT == WT_FP8 ? 2 : 4;
     switch (a.mt) {
         case 1: hipLaunchKernelGGL((gemm_kernel<WT, 1, EPI, N1>), grid, block, 0, s, a); break;

@@ -34,6 +34,7 @@ struct GemmArgs {
 // workspace needed by gemm split-K partials / counters
 constexpr size_t GEMM_PART_FLOATS = 1u << 20;   // 4 MiB
 constexpr int    GEMM_MAX_COUNTERS = 1 << 14;
+constexpr int    GEMM_CUS = 256;                  // compute units the K-split plan is balanced for (MI355X)
 
 // Plans the split and launches.  part/cnt must point at workspace regions of
 // GEMM_PART_FLOATS floats / GEMM_MAX_COUNTERS counters (zero-filled counters).
