@@ -446,8 +446,12 @@ __device__ __forceinline__ void loader_commit(SrLds &S, Loader &ld) {
     }
 }
 
+// Weight bytes are read once per launch: the non-temporal hint lets L2 evict
+// them first, so the stream does not push out the code, the kernel arguments
+// and the activations the workgroups share.
+constexpr int CPOL_NT = 2;
 __device__ __forceinline__ void dma16(const void *g, u32x4 *ldsdst) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void *)ldsdst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)ldsdst, 16, 0, CPOL_NT);
 }
 
 // Slot layout of a group of 4 k steps: for each step, the tiles in order; a
