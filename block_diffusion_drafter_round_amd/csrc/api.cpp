@@ -400,12 +400,11 @@ hipError_t run_round(const dflash_model *m, const dflash_kv *kv, const float *no
     dfl::SrArgs ra{};
     dfl::SrScalars &a = ra.s;
     a.b = b; a.len = kv->len; a.cap = kv->capacity;
-    // attention key splits: at most one item per workgroup, keys per split a multiple of 32
-    int ns = std::max(1, std::min({dfl::SR_MAX_SPLITS, nwg / c.n_kv_heads, (kv->len + 31) / 32}));
-    int kps = kv->len > 0 ? (kv->len + ns - 1) / ns : 32;
-    kps = (kps + 31) / 32 * 32;
-    a.kps = kps;
-    a.nsplit = kv->len > 0 ? (kv->len + kps - 1) / kps : 1;
+    // attention key splits: at most one item per workgroup; one split per
+    // kv head for the block's own keys, the others runs of whole 32-key
+    // blocks of the cache (the kernel spreads the blocks evenly)
+    a.nkb = (kv->len + 31) / 32;
+    a.nsplit = std::max(1, std::min({dfl::SR_MAX_SPLITS, nwg / c.n_kv_heads, a.nkb + 1}));
     a.eps = c.rms_eps; a.mscale = (float)m->mscale;
     a.qscale = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
     a.noise = noise; a.pos = pos; a.out = out; a.g_norm = m->w.g_norm;

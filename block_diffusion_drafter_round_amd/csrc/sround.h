@@ -43,7 +43,7 @@ struct SrScalars {
     int H, I, nq, nkv, d, qd, kvd, G;
     int b, len, cap, nl, first, last, d2;
     int nwg, cq, ch, ci;                   // columns per workgroup: q|k|v, hidden, intermediate
-    int nsplit, kps;                       // attention: key splits per kv head, keys per split
+    int nsplit, nkb;                       // attention: key splits per kv head, 32-key blocks of the cache
     float eps, mscale, qscale;             // qscale = log2(e) / sqrt(head_dim)
     const float *noise;                    // [b][H]
     const int32_t *pos;                    // [b]
