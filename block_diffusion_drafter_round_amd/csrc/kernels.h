@@ -39,7 +39,14 @@ constexpr int    GEMM_CUS = 256;                  // compute units the K-split p
 // Plans the split and launches.  part/cnt must point at workspace regions of
 // GEMM_PART_FLOATS floats / GEMM_MAX_COUNTERS counters (zero-filled counters).
 // The plan never needs more: it lowers the K split until the partials fit.
+// Shapes gemm_tall_ok accepts run the tiled kernel instead (no workspace).
 hipError_t gemm(GemmArgs a, float *part, unsigned *cnt, hipStream_t s);
+
+// Tiled kernel for tall activations (gemm_tall.hip): bf16 weights, M >= 256,
+// store epilogue, K and every segment's width multiples of 64, and at least
+// GEMM_CUS tiles of 128 x 64.
+bool gemm_tall_ok(const GemmArgs &a);
+hipError_t gemm_tall(const GemmArgs &a, hipStream_t s);
 
 // ---- DFlash2 proposal: top-k over draft logits, rank-r hidden projection ----
 constexpr int TOPK_CHUNK = 1024;     // candidates per wave and stage (16 per lane)

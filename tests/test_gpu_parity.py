@@ -66,6 +66,36 @@ def test_ctx_features(cfg, t):
     check(f"{cfg.name} ctx_features t={t}", out, O.ctx_features(m, taps), tol_for(cfg) / 10)
 
 
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_BF16_D128], ids=lambda c: c.name)
+def test_ctx_features_tall(cfg):
+    """4100 rows with bf16 weights take the tiled GEMM for tall activations
+    (at least 256 tiles of 128 x 64): 32 full row tiles and a ragged one."""
+    t = 4100
+    sw, m, dr, D = _setup(cfg, max_rows=t)
+    taps = synth.make_taps(cfg, t, stream=7)
+    out = host(dr.ctx_features(dev(taps)))
+    check(f"{cfg.name} ctx_features t={t} (tiled)", out, O.ctx_features(m, taps), tol_for(cfg) / 10)
+
+
+def test_ingest_tall():
+    """8200 ctx rows in one ingest call: the k|v projection (two weight
+    segments of 128 columns, k and v) runs as the tiled GEMM, 65 x 4 tiles."""
+    cfg = SMALL_BF16_D128
+    n = 8200
+    sw, m, dr, D = _setup(cfg, max_rows=n)
+    taps = synth.make_taps(cfg, n, stream=8)
+    pos = synth.positions(2000, n)
+    kv = D.KVCache(cfg, 8256)
+    dr.ingest_ctx(kv, dr.ctx_features(dev(taps)), dev(pos))
+    assert kv.len == n
+    okv = O.OracleKV(cfg)
+    O.ingest_ctx(m, okv, O.ctx_features(m, taps), pos)
+    for l in range(cfg.n_layers):
+        k, v = kv_rows_f64(kv, l, 0, n)
+        check(f"{cfg.name} layer {l} cached K, {n} rows (tiled)", k, okv.k[l], 1e-2)
+        check(f"{cfg.name} layer {l} cached V, {n} rows (tiled)", v, okv.v[l], 1e-2)
+
+
 @pytest.mark.parametrize("cfg", [synth.TINY_F32, SMALL_BF16, SMALL_BF16_D128, SMALL_FP8, SMALL_YARN],
                          ids=lambda c: c.name)
 def test_ingest_cache_rows(cfg):
