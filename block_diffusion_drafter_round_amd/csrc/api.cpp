@@ -88,8 +88,11 @@ struct WsLayout {
 
 // ingest_ctx projects up to INGEST_FUSE_ROWS / t layers' k|v in one GEMM
 // (at most GEMM_MAX_SEG / 2 and ROPE_MAX_LAYERS): few new rows make a skinny,
-// latency-bound GEMM per layer, so the layers share one launch instead
-constexpr size_t INGEST_FUSE_ROWS = 128;
+// latency-bound GEMM per layer, and many rows a GEMM that fills the device
+// only with several layers' columns (1024 rows x 5 layers: 640 tiles of the
+// tiled kernel, against 128 per layer), so the layers share one launch.  The
+// staging buffer holds INGEST_FUSE_ROWS rows of one layer's k|v.
+constexpr size_t INGEST_FUSE_ROWS = 8192;
 
 int ingest_layers_per_launch(int t) {
     const int n = t > 0 ? (int)(INGEST_FUSE_ROWS / (size_t)t) : 1;

@@ -121,10 +121,10 @@ def test_ingest_cache_rows(cfg):
 
 @pytest.mark.parametrize("n_layers", [5, 10])
 def test_ingest_layer_groups(n_layers):
-    """ingest_ctx projects several layers' k|v in one launch when few rows come
-    in (up to 8 layers at 16 rows or fewer, 3 at 40, 2 at 64, 1 at 129), with a
-    ragged last group when the layer count does not divide: every layer's
-    cache rows must still match the oracle."""
+    """ingest_ctx projects several layers' k|v in one launch (up to 8, fewer
+    once rows x layers would pass 8192), with a ragged last group when the
+    layer count does not divide: every layer's cache rows must still match
+    the oracle."""
     cfg = SMALL_BF16.replace(name=f"small_bf16_l{n_layers}", n_layers=n_layers, seed=40 + n_layers)
     sw, m, dr, D = _setup(cfg, max_rows=129)
     sizes = (1, 16, 40, 64, 129)
