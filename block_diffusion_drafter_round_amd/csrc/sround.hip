@@ -397,18 +397,33 @@ __device__ __forceinline__ bool attn_item(AItem &it) {
     return true;
 }
 
-// K/V parts of one 32-key block: K parts (key tile kt, d chunk c), then V^T
-// parts (d tile t, half hv); eight parts fill one ring slot
+// K/V parts of one 32-key block: KP parts of K, then V^T parts (d tile t,
+// half hv); eight parts fill one ring slot.
+// The block's K rows are one contiguous run of the cache, so K part p is the
+// contiguous 1 KB of keys p KPP .. p KPP + KPP - 1, with the 16-byte chunks of
+// each row permuted: chunk cc of key k sits at chunk cc ^ kswz(k) of its row.
+// An MFMA fragment read (16 keys, one chunk) then meets 16 distinct bank
+// groups.
 template <int WT, int D> struct AT {
     static constexpr bool F32 = WT == WT_F32;
     static constexpr int KVB = F32 ? 4 : 2;          // bytes per cached K/V value
     static constexpr int NC = D * KVB / 64;          // d chunks of 16 bytes per lane group
     static constexpr int KP = 2 * NC;
+    static constexpr int RB = D * KVB;               // bytes per cached K row
+    static constexpr int KPP = 1024 / RB, CPR = RB / 16;   // keys per K part, chunks per row
     static constexpr int VH = F32 ? 2 : 1;
     static constexpr int VP = (D / 16) * VH;
     static constexpr int SLOTS = (KP + VP) / 8;
     static constexpr int PQ = F32 ? 4 : 8;           // values per lane per d chunk
     static constexpr int NQV = D / 4;                // values per lane per head row
+    static_assert(KPP * KP == 32 && (CPR == 8 || CPR == 16 || CPR == 32), "K part layout");
+    // key k of a block (k = 8a + 4 kt + b): the fragment read of key tile kt
+    // takes (a, b) over all 16 lanes, and (k % KPP) CPR + (cc ^ kswz) must
+    // be distinct modulo 16 chunks
+    __device__ static int kswz(int k) {
+        const int a = (k >> 3) & 3, b = k & 3;
+        return CPR == 8 ? (((b >> 1) & 1) | (a << 1)) : (b | (a << 2));
+    }
 };
 
 // ---------------------------------------------------------------------------
@@ -629,10 +644,12 @@ __device__ __forceinline__ bool load_attn(SrLds &S, Loader &ld, int l) {
                 const int idx = sl * 8 + v;
                 const char *src;
                 if (idx < A::KP) {
-                    const int kt = idx / A::NC, c = idx - kt * A::NC;
-                    int key = k0 + 8 * (n16 >> 2) + 4 * kt + (n16 & 3);
+                    // part idx, LDS chunk `lane`: row lane / CPR, chunk lane % CPR
+                    const int kk = idx * A::KPP + lane / A::CPR;
+                    const int cc = (lane % A::CPR) ^ A::kswz(kk);
+                    int key = k0 + kk;
                     key = key < it.k_hi ? key : it.k_lo;                      // masked later
-                    src = kc + (((size_t)it.h * cap + key) * D) * A::KVB + c * 64 + g * 16;
+                    src = kc + (((size_t)it.h * cap + key) * D) * A::KVB + cc * 16;
                 } else {
                     const int q = idx - A::KP, t = q / A::VH, hv = q - t * A::VH;
                     int key = k0 + 8 * g + 4 * hv;
@@ -1574,8 +1591,9 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
             const unsigned s0 = cs.seq;
             if (actw) {
                 auto kf = [&](int kt, int c) -> u32x4 {
-                    const int idx = kt * NC + c;
-                    return S.ring[(s0 + idx / 8) % SR_NSLOT][idx & 7][lane];
+                    const int kk = 8 * (r16 >> 2) + 4 * kt + (r16 & 3), cc = 4 * c + g;
+                    const int idx = kk / A::KPP, pos = (kk % A::KPP) * A::CPR + (cc ^ A::kswz(kk));
+                    return S.ring[(s0 + idx / 8) % SR_NSLOT][idx & 7][pos];
                 };
                 auto vf = [&](int t, int hv) -> u32x4 {
                     const int idx = A::KP + t * A::VH + hv;
