@@ -4,11 +4,13 @@
 // drafter layer, one block table shared by every layer).
 //
 // Storage of one layer, with P rows per page:
-//   K [pages][nkv][P][d]      V [pages][nkv][d][P]   (V transposed per page)
-// A contiguous cache is the one-page case: P = capacity, no block table.
-// Logical row r of a sequence lives in physical page table[r / P] (page 0
-// without a table), at row r % P.  P is a multiple of 64, so an aligned
-// block of 32 keys never straddles a page.
+//   K [pages][nkv][P][d]      V [pages][nkv][P / 32][d][32]
+// (V transposed per tile of 32 rows, so that a 32-key block's V is one
+// contiguous run and P.V streams contiguous keys).  A contiguous cache is
+// the one-page case: P = capacity, no block table.  Logical row r of a
+// sequence lives in physical page table[r / P] (page 0 without a table), at
+// row r % P.  P is a multiple of 64, so an aligned block of 32 keys never
+// straddles a page.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -37,7 +39,8 @@ __device__ __forceinline__ size_t kv_k_off(const KvView &v, int page, int nkv, i
     return ((((size_t)page * nkv + h) * v.page_rows + (r % v.page_rows)) * d + dd) * v.esize;
 }
 __device__ __forceinline__ size_t kv_v_off(const KvView &v, int page, int nkv, int h, int r, int d, int dd) {
-    return ((((size_t)page * nkv + h) * d + dd) * v.page_rows + (r % v.page_rows)) * v.esize;
+    const int rp = r % v.page_rows;
+    return (((((size_t)page * nkv + h) * (v.page_rows / 32) + rp / 32) * d + dd) * 32 + (rp % 32)) * v.esize;
 }
 
 }  // namespace dfl

@@ -651,10 +651,12 @@ __device__ __forceinline__ bool load_attn(SrLds &S, Loader &ld, int l) {
                     key = key < it.k_hi ? key : it.k_lo;                      // masked later
                     src = kc + (((size_t)it.h * cap + key) * D) * A::KVB + cc * 16;
                 } else {
+                    // V [nkv][cap / 32][d][32]: a part (16 d rows of the
+                    // block's 32-key tile) is one contiguous 1 KB (bf16)
                     const int q = idx - A::KP, t = q / A::VH, hv = q - t * A::VH;
                     int key = k0 + 8 * g + 4 * hv;
                     key = key < it.k_hi ? key : it.k_lo;                      // masked later
-                    src = vc + (((size_t)it.h * D + 16 * t + n16) * cap + key) * A::KVB;
+                    src = vc + ((((size_t)it.h * (cap / 32) + key / 32) * D + 16 * t + n16) * 32 + key % 32) * A::KVB;
                 }
                 dma16(src, dst + v * 64);
             }
@@ -974,7 +976,8 @@ __device__ __forceinline__ void gemm_epilogue(SrLds &S, int kind, int l, unsigne
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const size_t e = ((size_t)hh * D + dd + i) * 16 + r;          // V^T of the block
-                    const size_t ce = ((size_t)hh * D + dd + i) * SS.cap + SS.len + r;
+                    const int key = SS.len + r;                                    // V [nkv][cap / 32][d][32]
+                    const size_t ce = (((size_t)hh * (SS.cap / 32) + key / 32) * D + dd + i) * 32 + key % 32;
                     if constexpr (AB == 4) {
                         st4(qkv + voff, e * 4, __float_as_uint(y[i]));
                         if (r < b) st4(vcache, ce * 4, __float_as_uint(y[i]));

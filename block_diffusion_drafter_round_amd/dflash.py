@@ -431,13 +431,16 @@ class DeviceWeights:
 
 
 class KVCache:
-    """Device storage for one dflash_kv: K [L][nkv][cap][d], V [L][nkv][d][cap]."""
+    """Device storage for one dflash_kv: K [L][nkv][cap][d], V
+    [L][nkv][cap/32][d][32] (transposed per tile of 32 rows)."""
 
     def __init__(self, cfg, capacity: int, device="cuda"):
         dt = torch.float32 if cfg.kv_dtype == "f32" else torch.bfloat16
         L, h, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+        if capacity % 64:
+            raise ValueError("capacity must be a multiple of 64")
         self.k = torch.zeros((max(L, 1), h, capacity, d), dtype=dt, device=device)
-        self.v = torch.zeros((max(L, 1), h, d, capacity), dtype=dt, device=device)
+        self.v = torch.zeros((max(L, 1), h, capacity // 32, d, 32), dtype=dt, device=device)
         self.c = dflash_kv(self.k.data_ptr(), self.v.data_ptr(), capacity, 0)
 
     @property
@@ -455,18 +458,21 @@ class KVCache:
         k = _to_device(k_stored, self.k.device).view(self.k.dtype)
         v = _to_device(v_stored, self.k.device).view(self.v.dtype)
         self.k[:, :, :rows] = k
-        self.v[:, :, :, :rows] = v.transpose(-1, -2)
+        r = torch.arange(rows, device=self.k.device)
+        # [L][h][rows][d] -> V[l][h][r / 32][d][r % 32]
+        self.v[:, :, r // 32, :, r % 32] = v.permute(2, 0, 1, 3)
         self.c.len = rows
 
     def rows(self, layer: int, start: int, stop: int):
         """(K, V) of rows [start, stop) of one layer as [rows, nkv, d] tensors."""
+        r = torch.arange(start, stop, device=self.k.device)
         return (self.k[layer, :, start:stop].transpose(0, 1),
-                self.v[layer, :, :, start:stop].permute(2, 0, 1))
+                self.v[layer][:, r // 32, :, r % 32])
 
 
 class PagedKVCache(KVCache):
     """Paged storage for one dflash_kv: K [L][pages][nkv][P][d], V
-    [L][pages][nkv][d][P], a device block table mapping logical page i to
+    [L][pages][nkv][P/32][d][32], a device block table mapping logical page i to
     physical page table[i] (by default a fixed seeded permutation of the
     pool, so logical order and storage order differ)."""
 
@@ -479,7 +485,7 @@ class PagedKVCache(KVCache):
         pool = pool_pages if pool_pages is not None else npg
         self.page_rows, self.pool_pages = page_rows, pool
         self.k = torch.zeros((max(L, 1), pool, h, page_rows, d), dtype=dt, device=device)
-        self.v = torch.zeros((max(L, 1), pool, h, d, page_rows), dtype=dt, device=device)
+        self.v = torch.zeros((max(L, 1), pool, h, page_rows // 32, d, 32), dtype=dt, device=device)
         if table is None:
             table = np.random.default_rng(seed).permutation(pool)[:npg]
         self.table_host = np.asarray(table, dtype=np.int32)
@@ -497,16 +503,16 @@ class PagedKVCache(KVCache):
         pg, off = self._locate(0, rows)
         pg_t = torch.from_numpy(pg).to(self.k.device)
         off_t = torch.from_numpy(off).to(self.k.device)
-        # [L][h][rows][d] -> K[l][page][h][off][d], V[l][page][h][d][off]
+        # [L][h][rows][d] -> K[l][page][h][off][d], V[l][page][h][off / 32][d][off % 32]
         self.k[:, pg_t, :, off_t, :] = k.permute(2, 0, 1, 3)
-        self.v[:, pg_t, :, :, off_t] = v.permute(2, 0, 1, 3)
+        self.v[:, pg_t, :, off_t // 32, :, off_t % 32] = v.permute(2, 0, 1, 3)
         self.c.len = rows
 
     def rows(self, layer: int, start: int, stop: int):
         pg, off = self._locate(start, stop)
         pg_t = torch.from_numpy(pg).to(self.k.device)
         off_t = torch.from_numpy(off).to(self.k.device)
-        return self.k[layer, pg_t, :, off_t, :], self.v[layer, pg_t, :, :, off_t]
+        return self.k[layer, pg_t, :, off_t, :], self.v[layer][pg_t, :, off_t // 32, :, off_t % 32]
 
 
 class Drafter:

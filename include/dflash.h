@@ -151,15 +151,16 @@ typedef struct dflash_weights {
  *
  * Contiguous storage (page_rows = 0):
  *   k: device, [n_layers][n_kv_heads][capacity][head_dim]   (row-major rows)
- *   v: device, [n_layers][n_kv_heads][head_dim][capacity]   (transposed: one
- *      row per head dimension, so that the attention's P.V product streams
- *      contiguous keys)
+ *   v: device, [n_layers][n_kv_heads][capacity / 32][head_dim][32]
+ *      (transposed per tile of 32 rows: row r, dimension j at
+ *      [r / 32][j][r % 32], so that a 32-key block's V is one contiguous run
+ *      and the attention's P.V product streams contiguous keys)
  *   capacity is a positive multiple of 64.
  *
  * Paged storage (page_rows > 0; [atlas dflash_head] "DflashProposerState":
  * one paged cache per drafter layer, one block table shared by all layers):
  *   k: device, [n_layers][pool_pages][n_kv_heads][page_rows][head_dim]
- *   v: device, [n_layers][pool_pages][n_kv_heads][head_dim][page_rows]
+ *   v: device, [n_layers][pool_pages][n_kv_heads][page_rows / 32][head_dim][32]
  *   block_table: device int32 [capacity / page_rows]; logical row r lives in
  *      physical page block_table[r / page_rows], row r % page_rows, of every
  *      layer.  page_rows is a positive multiple of 64 that divides capacity;
