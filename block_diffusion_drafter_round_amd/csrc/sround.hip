@@ -50,6 +50,8 @@
 // reset: the workspace's epoch word counts the phases of earlier launches.
 // Every spin is bounded; on expiry the kernel sets the error word and all
 // waves leave.
+#include <type_traits>
+
 #include "common.h"
 #include "sround.h"
 
@@ -1359,74 +1361,94 @@ struct AttnState {
     f32x4 o[NDT];
 };
 
-// one 32-key block: S^T = K Q^T (two key tiles; lane (q, g) ends up with keys
-// 8g..8g+7), online softmax, O^T += V^T P^T.  kf(kt, c) / vf(t, hv) return
-// the A fragments; valid(i) tells whether key 8g + i of the block exists.
-template <int WT, int D, class KF, class VF, class VALID>
-__device__ __forceinline__ void attn_block(AttnState<WT, D> &st, const u32x4 *qf, KF kf, VF vf, VALID valid) {
+// NB 32-key blocks at once: S^T = K Q^T (two key tiles per block; lane
+// (q, g) ends up with keys 8g..8g+7 of each), one online-softmax update over
+// all NB blocks' scores, O^T += V^T P^T.  kf(b, kt, c) / vf(b, t, hv) return
+// block b's A fragments; valid(b, i) tells whether key 8g + i of block b
+// exists.  Two blocks per update halve the serial max / exp / sum steps and
+// the accumulator rescales per key, and let one block's MFMAs overlap the
+// other's.
+template <int WT, int D, int NB, class KF, class VF, class VALID>
+__device__ __forceinline__ void attn_blocks(AttnState<WT, D> &st, const u32x4 *qf, KF kf, VF vf, VALID valid) {
     using A = AT<WT, D>;
     constexpr int NDT = D / 16;
-    f32x4 sc4[2];
+    f32x4 sc4[NB][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int c = 0; c < A::NC; ++c) {
-            const u32x4 k = kf(kt, c);
-            if constexpr (WT == WT_F32) {
-                acc = mfma_f32(f_of(k.x), f_of(qf[c].x), acc);
-                acc = mfma_f32(f_of(k.y), f_of(qf[c].y), acc);
-                acc = mfma_f32(f_of(k.z), f_of(qf[c].z), acc);
-                acc = mfma_f32(f_of(k.w), f_of(qf[c].w), acc);
-            } else {
-                acc = mfma_bf16(__builtin_bit_cast(bf16x8, k), __builtin_bit_cast(bf16x8, qf[c]), acc);
+        for (int kt = 0; kt < 2; ++kt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < A::NC; ++c) {
+                const u32x4 k = kf(b, kt, c);
+                if constexpr (WT == WT_F32) {
+                    acc = mfma_f32(f_of(k.x), f_of(qf[c].x), acc);
+                    acc = mfma_f32(f_of(k.y), f_of(qf[c].y), acc);
+                    acc = mfma_f32(f_of(k.z), f_of(qf[c].z), acc);
+                    acc = mfma_f32(f_of(k.w), f_of(qf[c].w), acc);
+                } else {
+                    acc = mfma_bf16(__builtin_bit_cast(bf16x8, k), __builtin_bit_cast(bf16x8, qf[c]), acc);
+                }
             }
+            sc4[b][kt] = acc;
         }
-        sc4[kt] = acc;
-    }
-    float sc[8];
+    float sc[NB][8];
     float bmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float x = sc4[i >> 2][i & 3];
-        sc[i] = valid(i) ? x : -INFINITY;
-        bmax = fmaxf(bmax, sc[i]);
-    }
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float x = sc4[b][i >> 2][i & 3];
+            sc[b][i] = valid(b, i) ? x : -INFINITY;
+            bmax = fmaxf(bmax, sc[b][i]);
+        }
     bmax = group4_max(bmax);
     const float m_new = fmaxf(st.m, bmax);
     const float corr = __builtin_amdgcn_exp2f(st.m - m_new);
     float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        sc[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
-        psum += sc[i];
-    }
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            sc[b][i] = __builtin_amdgcn_exp2f(sc[b][i] - m_new);
+            psum += sc[b][i];
+        }
     psum = group4_sum(psum);
     st.l = st.l * corr + psum;
     st.m = m_new;
 #pragma unroll
     for (int t = 0; t < NDT; ++t) st.o[t] *= corr;
-    if constexpr (WT == WT_F32) {
 #pragma unroll
-        for (int t = 0; t < NDT; ++t) {
-            const u32x4 v0 = vf(t, 0), v1 = vf(t, 1);
-            const float vk[8] = {f_of(v0.x), f_of(v0.y), f_of(v0.z), f_of(v0.w), f_of(v1.x), f_of(v1.y), f_of(v1.z), f_of(v1.w)};
+    for (int b = 0; b < NB; ++b) {
+        if constexpr (WT == WT_F32) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) st.o[t] = mfma_f32(valid(i) ? vk[i] : 0.f, sc[i], st.o[t]);
-        }
-    } else {
-        const bf16x8 pb = to_bf16x8(sc);
+            for (int t = 0; t < NDT; ++t) {
+                const u32x4 v0 = vf(b, t, 0), v1 = vf(b, t, 1);
+                const float vk[8] = {f_of(v0.x), f_of(v0.y), f_of(v0.z), f_of(v0.w), f_of(v1.x), f_of(v1.y), f_of(v1.z), f_of(v1.w)};
 #pragma unroll
-        for (int t = 0; t < NDT; ++t) {
-            u32x4 vv = vf(t, 0);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t msk = (valid(2 * w) ? 0x0000FFFFu : 0u) | (valid(2 * w + 1) ? 0xFFFF0000u : 0u);
-                vv[w] &= msk;
+                for (int i = 0; i < 8; ++i) st.o[t] = mfma_f32(valid(b, i) ? vk[i] : 0.f, sc[b][i], st.o[t]);
             }
-            st.o[t] = mfma_bf16(__builtin_bit_cast(bf16x8, vv), pb, st.o[t]);
+        } else {
+            const bf16x8 pb = to_bf16x8(sc[b]);
+#pragma unroll
+            for (int t = 0; t < NDT; ++t) {
+                u32x4 vv = vf(b, t, 0);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t msk = (valid(b, 2 * w) ? 0x0000FFFFu : 0u) | (valid(b, 2 * w + 1) ? 0xFFFF0000u : 0u);
+                    vv[w] &= msk;
+                }
+                st.o[t] = mfma_bf16(__builtin_bit_cast(bf16x8, vv), pb, st.o[t]);
+            }
         }
     }
+}
+
+// one 32-key block (kf(kt, c), vf(t, hv), valid(i))
+template <int WT, int D, class KF, class VF, class VALID>
+__device__ __forceinline__ void attn_block(AttnState<WT, D> &st, const u32x4 *qf, KF kf, VF vf, VALID valid) {
+    attn_blocks<WT, D, 1>(st, qf, [&](int, int kt, int c) { return kf(kt, c); },
+                          [&](int, int t, int hv) { return vf(t, hv); }, [&](int, int i) { return valid(i); });
 }
 
 template <int WT, int D>
@@ -1588,27 +1610,33 @@ __device__ __forceinline__ bool attn_phase(SrLds &S, Cons &cs, int l, unsigned p
             auto valid = [&](int i) { return i < 4 && i < b4; };
             attn_block<WT, D>(st, qf, kf, vf, valid);
         }
-        for (int blk = 0; blk < it.nblk; ++blk) {
-            const int k0 = it.k_lo + 32 * blk;
-            if (!ring_wait(S, cs, cs.seq + A::SLOTS)) return false;
+        // cached keys, two blocks per softmax update (an odd last block alone)
+        auto cache_blocks = [&](auto nbc, int blk) -> bool {
+            constexpr int NB = decltype(nbc)::value;
+            if (!ring_wait(S, cs, cs.seq + NB * A::SLOTS)) return false;
             const unsigned s0 = cs.seq;
             if (actw) {
-                auto kf = [&](int kt, int c) -> u32x4 {
+                auto kf = [&](int b, int kt, int c) -> u32x4 {
                     const int kk = 8 * (r16 >> 2) + 4 * kt + (r16 & 3), cc = 4 * c + g;
-                    const int idx = kk / A::KPP, pos = (kk % A::KPP) * A::CPR + (cc ^ A::kswz(kk));
+                    const int idx = b * A::SLOTS * 8 + kk / A::KPP, pos = (kk % A::KPP) * A::CPR + (cc ^ A::kswz(kk));
                     return S.ring[(s0 + idx / 8) % SR_NSLOT][idx & 7][pos];
                 };
-                auto vf = [&](int t, int hv) -> u32x4 {
-                    const int idx = A::KP + t * A::VH + hv;
+                auto vf = [&](int b, int t, int hv) -> u32x4 {
+                    const int idx = b * A::SLOTS * 8 + A::KP + t * A::VH + hv;
                     return S.ring[(s0 + idx / 8) % SR_NSLOT][idx & 7][lane];
                 };
-                const int kend = it.k_hi - k0 - 8 * g;
-                auto valid = [&](int i) { return i < kend; };
-                attn_block<WT, D>(st, qf, kf, vf, valid);
+                const int kend = it.k_hi - (it.k_lo + 32 * blk) - 8 * g;
+                auto valid = [&](int b, int i) { return i < kend - 32 * b; };
+                attn_blocks<WT, D, NB>(st, qf, kf, vf, valid);
             }
-            cs.seq = __builtin_amdgcn_readfirstlane(cs.seq + A::SLOTS);
+            cs.seq = __builtin_amdgcn_readfirstlane(cs.seq + NB * A::SLOTS);
             ring_release(S, cs.seq);
-        }
+            return true;
+        };
+        int blk = 0;
+        for (; blk + 1 < it.nblk; blk += 2)
+            if (!cache_blocks(std::integral_constant<int, 2>{}, blk)) return false;
+        if (blk < it.nblk && !cache_blocks(std::integral_constant<int, 1>{}, blk)) return false;
         if (actw) {
             const int item = blockIdx.x;
             const int GQ = SS.G * 16, qi = v * 16 + r16;
