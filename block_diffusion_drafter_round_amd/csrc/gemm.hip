@@ -373,7 +373,7 @@ static void launch_wt(const GemmArgs &a, hipStream_t s) {
 
 hipError_t gemm(GemmArgs a, float *part, unsigned *cnt, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
-    if (gemm_tall_ok(a)) return gemm_tall(a, s);
+    if (gemm_tall_ok(a)) return gemm_tall(a, cnt, s);
     gemm_plan(a);
     a.part = part;
     a.cnt = cnt;

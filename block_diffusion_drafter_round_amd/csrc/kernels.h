@@ -43,10 +43,12 @@ constexpr int    GEMM_CUS = 256;                  // compute units the K-split p
 hipError_t gemm(GemmArgs a, float *part, unsigned *cnt, hipStream_t s);
 
 // Tiled kernel for tall activations (gemm_tall.hip): bf16 weights, M >= 256,
-// store epilogue, K and every segment's width multiples of 64, and at least
-// GEMM_CUS tiles of 128 x 64.
+// store epilogue, K a multiple of 64, every segment's width a multiple of
+// 128, and at least GEMM_CUS work items (tiles of 128 x 128, each split
+// into two K halves when the tiles alone are fewer).  The K halves use two
+// of the zero-filled counters per tile in `cnt` and leave them zero.
 bool gemm_tall_ok(const GemmArgs &a);
-hipError_t gemm_tall(const GemmArgs &a, hipStream_t s);
+hipError_t gemm_tall(const GemmArgs &a, unsigned *cnt, hipStream_t s);
 
 // ---- DFlash2 proposal: top-k over draft logits, rank-r hidden projection ----
 constexpr int TOPK_CHUNK = 1024;     // candidates per wave and stage (16 per lane)

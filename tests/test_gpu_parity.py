@@ -66,11 +66,15 @@ def test_ctx_features(cfg, t):
     check(f"{cfg.name} ctx_features t={t}", out, O.ctx_features(m, taps), tol_for(cfg) / 10)
 
 
-@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_BF16_D128], ids=lambda c: c.name)
-def test_ctx_features_tall(cfg):
-    """4100 rows with bf16 weights take the tiled GEMM for tall activations
-    (at least 256 tiles of 128 x 64): 32 full row tiles and a ragged one."""
-    t = 4100
+@pytest.mark.parametrize("cfg,t", [(SMALL_BF16_D128, 4100), (SMALL_BF16_D128, 2000), (SMALL_BF16, 4096)],
+                         ids=["d128_t4100", "d128_t2000", "bf16_t4096"])
+def test_ctx_features_tall(cfg, t):
+    """Tall activations with bf16 weights take the tiled GEMM (128 x 128
+    tiles).  4100 rows of hidden 1024: 33 x 8 tiles over the whole K, the
+    last row tile holding 4 rows.  2000 rows: 16 x 8 tiles, so K is split
+    into two halves that meet in Y; the last row tile holds 80 rows (its
+    upper 16-row tiles lie past M).  4096 rows of hidden 512: 32 x 4 tiles,
+    K halves."""
     sw, m, dr, D = _setup(cfg, max_rows=t)
     taps = synth.make_taps(cfg, t, stream=7)
     out = host(dr.ctx_features(dev(taps)))
@@ -78,10 +82,11 @@ def test_ctx_features_tall(cfg):
 
 
 def test_ingest_tall():
-    """8200 ctx rows in one ingest call: the k|v projection (two weight
-    segments of 128 columns, k and v) runs as the tiled GEMM, 65 x 4 tiles."""
+    """8208 ctx rows in one ingest call: the k|v projection (two weight
+    segments of 128 columns, k and v) runs as the tiled GEMM, 65 x 2 tiles
+    with K split into two halves; the last row tile holds 16 rows."""
     cfg = SMALL_BF16_D128
-    n = 8200
+    n = 8208
     sw, m, dr, D = _setup(cfg, max_rows=n)
     taps = synth.make_taps(cfg, n, stream=8)
     pos = synth.positions(2000, n)
