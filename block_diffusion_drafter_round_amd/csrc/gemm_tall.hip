@@ -176,18 +176,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_tall_kernel(GemmArgs p, int nrt,
 
     if (nsplit > 1) {
         // K halves: the first to arrive leaves its partial in Y, the second
-        // adds it.  A lane's four sums of a 16 x 16 tile travel as one
-        // 16-byte piece, placed at row lane / 4, columns 4 (lane % 4) .. + 3
-        // of that tile's own 16 rows x 64 bytes of Y (M is a multiple of 16
-        // here, so a 16-row tile is either wholly inside or wholly past M).
+        // adds it.  Lane (r16, g) holds rows 4g .. 4g + 3 of column r16 of a
+        // 16 x 16 tile; those four sums travel as one 16-byte piece, placed
+        // in the same four rows of Y: row 4g + r16 % 4, columns
+        // 4 (r16 / 4) .. + 3.  M is a multiple of 4 here, so a group of
+        // four rows is either wholly inside or wholly past M.
         unsigned *cnt = p.cnt + 2 * t;
         auto piece = [&](int rt, int ct) -> uint32_t {
-            const int row = w0 + 16 * rt + lane / 4;
-            return (uint32_t)(((size_t)row * p.ldy + n0 + 16 * ct + 4 * (lane % 4)) * 4);
+            const int row = w0 + 16 * rt + 4 * g + (r16 & 3);
+            return (uint32_t)(((size_t)row * p.ldy + n0 + 16 * ct + 4 * (r16 >> 2)) * 4);
         };
         bool rows_in[RT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) rows_in[rt] = w0 + 16 * rt < p.M;
+        for (int rt = 0; rt < RT; ++rt) rows_in[rt] = w0 + 16 * rt + 4 * g < p.M;
         if (threadIdx.x == 0) role = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if (role == 0) {
@@ -240,9 +241,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_tall_kernel(GemmArgs p, int nrt,
 }
 
 // K halves when the tiles alone do not fill the device (and the split
-// bookkeeping applies: M a multiple of 16, both halves whole stages)
+// bookkeeping applies: M a multiple of 4, both halves whole stages)
 int tall_split(const GemmArgs &a, int ntile) {
-    return ntile < GEMM_CUS && a.M % 16 == 0 && a.K % (2 * TK) == 0 && 2 * ntile <= GEMM_MAX_COUNTERS &&
+    return ntile < GEMM_CUS && a.M % 4 == 0 && a.K % (2 * TK) == 0 && 2 * ntile <= GEMM_MAX_COUNTERS &&
                    (long long)a.M * a.ldy * 4 < 0x7fffffffLL
                ? 2
                : 1;

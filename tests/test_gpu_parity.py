@@ -66,15 +66,15 @@ def test_ctx_features(cfg, t):
     check(f"{cfg.name} ctx_features t={t}", out, O.ctx_features(m, taps), tol_for(cfg) / 10)
 
 
-@pytest.mark.parametrize("cfg,t", [(SMALL_BF16_D128, 4100), (SMALL_BF16_D128, 2000), (SMALL_BF16, 4096)],
-                         ids=["d128_t4100", "d128_t2000", "bf16_t4096"])
+@pytest.mark.parametrize("cfg,t", [(SMALL_BF16_D128, 4100), (SMALL_BF16_D128, 2020), (SMALL_BF16, 4096)],
+                         ids=["d128_t4100", "d128_t2020", "bf16_t4096"])
 def test_ctx_features_tall(cfg, t):
     """Tall activations with bf16 weights take the tiled GEMM (128 x 128
     tiles).  4100 rows of hidden 1024: 33 x 8 tiles over the whole K, the
-    last row tile holding 4 rows.  2000 rows: 16 x 8 tiles, so K is split
-    into two halves that meet in Y; the last row tile holds 80 rows (its
-    upper 16-row tiles lie past M).  4096 rows of hidden 512: 32 x 4 tiles,
-    K halves."""
+    last row tile holding 4 rows.  2020 rows: 16 x 8 tiles, so K is split
+    into two halves that meet in Y; the last row tile holds 100 rows, so one
+    wave's 16 rows end inside it (4 in, 12 past M) and the waves above lie
+    wholly past M.  4096 rows of hidden 512: 32 x 4 tiles, K halves."""
     sw, m, dr, D = _setup(cfg, max_rows=t)
     taps = synth.make_taps(cfg, t, stream=7)
     out = host(dr.ctx_features(dev(taps)))
