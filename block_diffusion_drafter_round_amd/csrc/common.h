@@ -93,15 +93,21 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // sum / max over the 4 lane groups that share l % 16 (lanes l, l^16, l^32, l^48)
+// Over lanes l, l ^ 16, l ^ 32, l ^ 48, with the gfx950 lane swaps (VALU,
+// no LDS round trip): swapping a register with itself between 16-lane rows
+// (32-lane halves) leaves every lane holding its own value in one result
+// and its partner's, lane ^ 16 (lane ^ 32), in the other.
 __device__ __forceinline__ float group4_sum(float v) {
-    v += __shfl_xor(v, 16, DFL_WAVE);
-    v += __shfl_xor(v, 32, DFL_WAVE);
-    return v;
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 __device__ __forceinline__ float group4_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16, DFL_WAVE));
-    v = fmaxf(v, __shfl_xor(v, 32, DFL_WAVE));
-    return v;
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 // streaming (non-temporal) 16-byte load for weights that are read once

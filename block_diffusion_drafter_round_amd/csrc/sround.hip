@@ -771,8 +771,7 @@ __device__ __forceinline__ void compute_rinv(SrLds &S, const float *ssq, unsigne
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) s += q + 4 * i < nwg ? v[i] : 0.f;
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
+    s = group4_sum(s);
     if (q == 0) S.rinv[r] = 1.f / sqrtf(s / (float)width + SS.eps);
     cbar();
     if (lane == 0) lds_st(&S.rphase, p + 1);
@@ -1286,8 +1285,7 @@ __device__ __forceinline__ void norm_rope(float (&x)[D / 4], const float *gk, co
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < NQV; ++i) ss += x[i] * x[i];
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
+    ss = group4_sum(ss);
     const float inv = 1.f / sqrtf(ss / (float)D + SS.eps);
 #pragma unroll
     for (int s = 0; s < NS; ++s)
