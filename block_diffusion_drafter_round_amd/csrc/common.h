@@ -86,29 +86,56 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 // ---------------------------------------------------------------------------
 // wave reductions
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, DFL_WAVE);
-    return v;
+// All of these stay in the VALU (no LDS round trip).  Within a 16-lane row
+// the DPP row rotations combine lane i with lanes i - n (mod 16); across
+// rows the gfx950 lane swaps: swapping a register with itself between
+// 16-lane rows (32-lane halves) leaves every lane holding its own value in
+// one result and its partner's, lane ^ 16 (lane ^ 32), in the other.
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {   // lane i gets lane (i - N) mod 16 of its row
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
-// sum / max over the 4 lane groups that share l % 16 (lanes l, l^16, l^32, l^48)
-// Over lanes l, l ^ 16, l ^ 32, l ^ 48, with the gfx950 lane swaps (VALU,
-// no LDS round trip): swapping a register with itself between 16-lane rows
-// (32-lane halves) leaves every lane holding its own value in one result
-// and its partner's, lane ^ 16 (lane ^ 32), in the other.
-__device__ __forceinline__ float group4_sum(float v) {
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+// over all 64 lanes
+__device__ __forceinline__ float wave_sum(float v) {
+    v += row_ror<1>(v);
+    v += row_ror<2>(v);
+    v += row_ror<4>(v);
+    v += row_ror<8>(v);
+    return xor32_sum(xor16_sum(v));
 }
-__device__ __forceinline__ float group4_max(float v) {
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, row_ror<1>(v));
+    v = fmaxf(v, row_ror<2>(v));
+    v = fmaxf(v, row_ror<4>(v));
+    v = fmaxf(v, row_ror<8>(v));
+    return xor32_max(xor16_max(v));
 }
+// over the 16 lanes that share l % 4
+__device__ __forceinline__ float stride4_sum(float v) {
+    v += row_ror<4>(v);
+    v += row_ror<8>(v);
+    return xor32_sum(xor16_sum(v));
+}
+// over the 4 lanes that share l % 16 (lanes l, l ^ 16, l ^ 32, l ^ 48)
+__device__ __forceinline__ float group4_sum(float v) { return xor32_sum(xor16_sum(v)); }
+__device__ __forceinline__ float group4_max(float v) { return xor32_max(xor16_max(v)); }
 
 // streaming (non-temporal) 16-byte load for weights that are read once
 __device__ __forceinline__ u32x4 ld_stream16(const void *p) {

@@ -1711,26 +1711,27 @@ __device__ __forceinline__ bool merge_phase(SrLds &S, int l, unsigned p) {
             // every load (the splits' m, l and partial O) before the first use
             float2 ml = make_float2(-1e30f, 0.f);
             if (lane < ns) ml = *reinterpret_cast<const float2 *>(pml + ((size_t)(h * ns + lane) * GQ + qi) * 2);
+            // the m of each split this lane sums, so its weight is computed
+            // here rather than fetched from the lane that loaded it
             u32x4 raw[NPS][AB == 4 ? 2 : 1];
+            float msp[NPS];
 #pragma unroll
             for (int i = 0; i < NPS; ++i) {
                 int sp = sg + NSG * i;
                 sp = sp < ns ? sp : 0;
+                msp[i] = pml[((size_t)(h * ns + sp) * GQ + qi) * 2];
                 const size_t e = ((size_t)(h * ns + sp) * GQ + qi) * D + DP * dq + 8 * dg;
                 raw[i][0] = *reinterpret_cast<const u32x4 *>(po + e * AB);
                 if constexpr (AB == 4) raw[i][AB == 4 ? 1 : 0] = *reinterpret_cast<const u32x4 *>(po + e * AB + 16);
             }
             const float m = ml.x, lv = ml.y;
-            float M = m;
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+            const float M = wave_max(m);
             const float w = lane < ns ? __builtin_amdgcn_exp2f(m - M) : 0.f;
             L = wave_sum(w * lv);
 #pragma unroll
             for (int i = 0; i < NPS; ++i) {
                 const int sp = sg + NSG * i;
-                float ws = __shfl(w, sp < 64 ? sp : 63, 64);
-                ws = sp < ns ? ws : 0.f;
+                const float ws = sp < ns ? __builtin_amdgcn_exp2f(msp[i] - M) : 0.f;
                 if constexpr (AB == 4) {
                     const u32x4 a0 = raw[i][0], a1 = raw[i][AB == 4 ? 1 : 0];
                     acc[0] += ws * f_of(a0.x); acc[1] += ws * f_of(a0.y); acc[2] += ws * f_of(a0.z); acc[3] += ws * f_of(a0.w);
@@ -1745,10 +1746,9 @@ __device__ __forceinline__ bool merge_phase(SrLds &S, int l, unsigned p) {
                 }
             }
         }
+        static_assert(NDG == 4, "the split groups are the lanes that share lane % 4");
 #pragma unroll
-        for (int o = NDG; o < 64; o <<= 1)
-#pragma unroll
-            for (int k = 0; k < 8; ++k) acc[k] += __shfl_xor(acc[k], o, 64);
+        for (int k = 0; k < 8; ++k) acc[k] = stride4_sum(acc[k]);
         if (sg == 0) {
             const float il = 1.f / L;
             const int c = hq * D + DP * dq + 8 * dg;
