@@ -81,6 +81,19 @@ def test_ctx_features_tall(cfg, t):
     check(f"{cfg.name} ctx_features t={t} (tiled)", out, O.ctx_features(m, taps), tol_for(cfg) / 10)
 
 
+def test_ctx_features_tall_halves_deterministic():
+    """The tiled GEMM's two K halves meet in Y in whichever order they finish;
+    a sum of two f32 terms does not depend on that order, so repeated calls
+    give the same bits (2020 rows of hidden 1024: 16 x 8 tiles, K halves)."""
+    cfg, t = SMALL_BF16_D128, 2020
+    sw, m, dr, D = _setup(cfg, max_rows=t)
+    taps = dev(synth.make_taps(cfg, t, stream=9))
+    first = host(dr.ctx_features(taps)).copy()
+    for _ in range(4):
+        again = host(dr.ctx_features(taps))
+        assert np.array_equal(first.view(np.uint64), again.view(np.uint64))
+
+
 def test_ingest_tall():
     """8208 ctx rows in one ingest call: the k|v projection (two weight
     segments of 128 columns, k and v) runs as the tiled GEMM, 65 x 2 tiles
