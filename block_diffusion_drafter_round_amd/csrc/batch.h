@@ -11,7 +11,7 @@ constexpr int BATCH_MAX_SEQ = 8;          // sequences per call (128 stacked row
 constexpr int BATCH_MAX_ITEMS = 512;      // attention items (sequence, kv head, split) per launch
 constexpr int BATCH_MAX_SPLITS = 64;      // key splits per (sequence, kv head): one per lane in the merge
 constexpr int BATCH_ATTN_THREADS = 512;   // eight waves: one q head each (G <= 8)
-constexpr int BATCH_CHUNK_KEYS = 128;     // keys staged per step; key splits are multiples of it
+constexpr int BATCH_CHUNK_KEYS = 64;      // keys staged per step; key splits are multiples of it
 
 struct BatchSeq {
     KvView kv;

@@ -13,10 +13,13 @@
 //   batch_attn     non-causal attention of the G q heads of one kv head over
 //                  one key split of one sequence (the window's ctx keys and
 //                  the block keys alike come from the cache).  The key
-//                  blocks are staged through LDS, 128 keys at a time, by all
+//                  blocks are staged through LDS, 64 keys at a time, by all
 //                  eight waves; wave v computes q head v with MFMA 16x16x32
 //                  bf16 (S^T = K Q^T, online softmax, O^T += V^T P^T) and
-//                  writes the split's partial (m, l, O);
+//                  writes the split's partial (m, l, O).  Each wave's
+//                  dependent chain (reads, MFMAs, softmax) is what bounds
+//                  it, so the kernel is held to 128 VGPRs and two
+//                  workgroups share a compute unit;
 //   batch_merge    the splits' log-sum-exp merge into the attention output;
 //   d2_dyn/d2_conv the DFlash2 conv wrap: the dynamic coefficients of a
 //                  sublayer's normed input, its prepare conv, and its finish
@@ -94,14 +97,14 @@ template <int D> struct BA {
     static constexpr int NC = D / 32;                  // 32-wide d chunks (8 bf16 per lane)
     static constexpr int NDT = D / 16;                 // 16-wide d tiles of V^T
     static constexpr int NPART = 2 * NC + NDT;
-    static constexpr int NB = 4;                       // blocks per staged chunk
+    static constexpr int NB = BATCH_CHUNK_KEYS / 32;   // blocks per staged chunk
     static constexpr int PIECES = NB * NPART * 64;     // 16-byte pieces per chunk
     static constexpr int PER_THREAD = PIECES / BATCH_ATTN_THREADS;
     static_assert(PIECES % BATCH_ATTN_THREADS == 0, "pieces split evenly over the threads");
 };
 
 template <int D>
-__global__ __launch_bounds__(BATCH_ATTN_THREADS) void batch_attn(BatchArgs a) {
+__global__ __launch_bounds__(BATCH_ATTN_THREADS, 2) void batch_attn(BatchArgs a) {
     using T = BA<D>;
     constexpr int NC = T::NC, NDT = T::NDT, NPART = T::NPART, NB = T::NB;
     __shared__ u32x4 stage[NB * NPART * 64];
