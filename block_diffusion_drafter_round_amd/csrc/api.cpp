@@ -523,6 +523,9 @@ hipError_t run_round_layered(const dflash_model *m, const dflash_kv *kvs, int S,
         g.A = A; g.lda = lda; g.M = M; g.K = K;
         for (const dfl::GemmSeg &sg : segs) g.seg[g.nseg++] = sg;
         g.Y = Y; g.ldy = ldy; g.epi = epi; g.wtype = wtype(c);
+        // the round's projections take single-plane bf16 activations (as the
+        // persistent kernel does) except under the DFlash2 wrap
+        g.planes = c.d2_groups > 0 ? 2 : 1;
         ProfScope p(cls, s);
         return dfl::gemm(g, part, cnt, s);
     };

@@ -81,7 +81,13 @@ __device__ __forceinline__ void load_a(AStage<WT, MT, NSTEP> &st, const GemmArgs
     }
 }
 
-template <int WT, int MT, int NSTEP>
+// PL: activation planes (2: hi + lo, 1: bf16 rounding only); FRP fragments
+// per step and m-tile in LDS
+template <int WT, int PL> struct Planes {
+    static constexpr int FRP = (WT == WT_F32 || PL == 2) ? WCfg<WT>::FR : WCfg<WT>::FR / 2;
+};
+
+template <int WT, int MT, int NSTEP, int PL>
 __device__ __forceinline__ void put_a(u32x4 *lds, const AStage<WT, MT, NSTEP> &st, const GemmArgs &p, int m0, int kvalid) {
     using S = AStage<WT, MT, NSTEP>;
 #pragma unroll
@@ -103,30 +109,39 @@ __device__ __forceinline__ void put_a(u32x4 *lds, const AStage<WT, MT, NSTEP> &s
             lds[(mt * NSTEP + s) * 64 + g0 * 16 + r16] = f0;
             lds[(mt * NSTEP + s) * 64 + (g0 + 1) * 16 + r16] = f1;
         } else {
-            bf16x8 hi, lo;
-            split_bf16x8(x, hi, lo);
             int s, f, g;
             if constexpr (WT == WT_BF16) { s = j >> 2; g = j & 3; f = 0; }
             else { s = j >> 3; const int jj = j & 7; g = jj >> 1; f = (jj & 1) * 2; }  // fp8: lane group g holds 16 K
             const int lane = g * 16 + r16;
-            lds[((mt * NSTEP + s) * WCfg<WT>::FR + f) * 64 + lane] = __builtin_bit_cast(u32x4, hi);
-            lds[((mt * NSTEP + s) * WCfg<WT>::FR + f + 1) * 64 + lane] = __builtin_bit_cast(u32x4, lo);
+            if constexpr (PL == 1) {
+                lds[((mt * NSTEP + s) * Planes<WT, PL>::FRP + f / 2) * 64 + lane] = __builtin_bit_cast(u32x4, to_bf16x8(x));
+            } else {
+                bf16x8 hi, lo;
+                split_bf16x8(x, hi, lo);
+                lds[((mt * NSTEP + s) * WCfg<WT>::FR + f) * 64 + lane] = __builtin_bit_cast(u32x4, hi);
+                lds[((mt * NSTEP + s) * WCfg<WT>::FR + f + 1) * 64 + lane] = __builtin_bit_cast(u32x4, lo);
+            }
         }
     }
 }
 
-template <int WT>
+template <int WT, int PL>
 __device__ __forceinline__ void mac_step(f32x4 &acc, const u32x4 &wv, const u32x4 *af) {
     if constexpr (WT == WT_BF16) {
         const bf16x8 b = __builtin_bit_cast(bf16x8, wv);
         acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[0]), b, acc);
-        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[64]), b, acc);
+        if constexpr (PL == 2) acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[64]), b, acc);
     } else if constexpr (WT == WT_FP8) {
         const bf16x8 b0 = fp8x8_to_bf16x8(wv.x, wv.y), b1 = fp8x8_to_bf16x8(wv.z, wv.w);
-        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[0]), b0, acc);
-        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[64]), b0, acc);
-        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[128]), b1, acc);
-        acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[192]), b1, acc);
+        if constexpr (PL == 2) {
+            acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[0]), b0, acc);
+            acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[64]), b0, acc);
+            acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[128]), b1, acc);
+            acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[192]), b1, acc);
+        } else {
+            acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[0]), b0, acc);
+            acc = mfma_bf16(__builtin_bit_cast(bf16x8, af[64]), b1, acc);
+        }
     } else {
         const u32x4 a = af[0];
         acc = mfma_f32(__uint_as_float(a.x), __uint_as_float(wv.x), acc);
@@ -136,9 +151,9 @@ __device__ __forceinline__ void mac_step(f32x4 &acc, const u32x4 &wv, const u32x
     }
 }
 
-template <int WT, int MT, int EPI, int NSTEP>
+template <int WT, int MT, int EPI, int NSTEP, int PL>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
-    constexpr int KS = WCfg<WT>::KS, ES = WCfg<WT>::ES, FR = WCfg<WT>::FR;
+    constexpr int KS = WCfg<WT>::KS, ES = WCfg<WT>::ES, FR = Planes<WT, PL>::FRP;
     constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
     constexpr int KCH = NSTEP * KS;                      // K per staged chunk
     __shared__ u32x4 lds[2][MT * NSTEP * FR * 64];
@@ -198,7 +213,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
         constexpr int B = decltype(bufc)::value;
         const int kvalid = min(KCH, kend - k0);           // a multiple of KS
         const int nst = kvalid / KS;
-        put_a<WT, MT, NSTEP>(lds[B], ast, p, m0, kvalid);
+        put_a<WT, MT, NSTEP, PL>(lds[B], ast, p, m0, kvalid);
         const int k1 = k0 + KCH;
         const bool more = k1 < kend;
         if (more) {
@@ -214,7 +229,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
             for (int mt = 0; mt < MT; ++mt) {
                 const u32x4 *af = lds[B] + ((mt * NSTEP + s) * FR) * 64 + lane;
 #pragma unroll
-                for (int a = 0; a < NACC; ++a) mac_step<WT>(acc[mt][a], wv[B][s][a], af);
+                for (int a = 0; a < NACC; ++a) mac_step<WT, PL>(acc[mt][a], wv[B][s][a], af);
             }
         return more;
     };
@@ -349,17 +364,22 @@ int gemm_plan(GemmArgs &a) {
     return base * a.ksplit;
 }
 
-template <int WT, int EPI>
-static void launch_wt_epi(const GemmArgs &a, hipStream_t s) {
+template <int WT, int EPI, int PL>
+static void launch_wt_epi_pl(const GemmArgs &a, hipStream_t s) {
     dim3 grid(a.ngroups * a.ksplit, a.mgroups), block(256);
     constexpr bool SW = EPI == EPI_SWIGLU;
     constexpr int N1 = WT == WT_FP8 ? (SW ? 2 : 4) : (SW ? 4 : 8);
     constexpr int N4 = WT == WT_FP8 ? 2 : 4;
     switch (a.mt) {
-        case 1: hipLaunchKernelGGL((gemm_kernel<WT, 1, EPI, N1>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((gemm_kernel<WT, 2, EPI, N4>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((gemm_kernel<WT, 4, EPI, N4>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((gemm_kernel<WT, 1, EPI, N1, PL>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((gemm_kernel<WT, 2, EPI, N4, PL>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((gemm_kernel<WT, 4, EPI, N4, PL>), grid, block, 0, s, a); break;
     }
+}
+template <int WT, int EPI>
+static void launch_wt_epi(const GemmArgs &a, hipStream_t s) {
+    if (WT != WT_F32 && a.planes == 1) launch_wt_epi_pl<WT, EPI, 1>(a, s);
+    else launch_wt_epi_pl<WT, EPI, 2>(a, s);
 }
 
 template <int WT>

@@ -26,6 +26,7 @@ struct GemmArgs {
     float *Y; int ldy;
     int epi;
     int wtype;
+    int planes;       // bf16 / fp8 weights: activations as 2 bf16 planes (hi + lo; also when 0) or 1 (bf16 rounding)
     // filled by the launcher
     int ksplit, kchunk, mt, ngroups, mgroups;   // ngroups: 64-column groups
     float *part; unsigned *cnt;
