@@ -21,6 +21,34 @@ namespace {
 __device__ __forceinline__ bool before(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
 }
+__device__ __forceinline__ void keep_best(float &wv, int &wi, float ov, int oi) {
+    if (before(ov, oi, wv, wi)) { wv = ov; wi = oi; }
+}
+// The wave's best (value, index): the selection order is total, so any
+// reduction tree picks the same entry.  Within 16-lane rows by DPP row
+// rotations, across rows by the lane swaps (a register swapped with itself
+// leaves a lane its own entry in one result and its partner's in the
+// other; values and indices move alike).  No LDS round trip.
+template <int N>
+__device__ __forceinline__ int ror_i(int x) { return __builtin_amdgcn_update_dpp(0, x, 0x120 + N, 0xF, 0xF, false); }
+__device__ __forceinline__ void wave_best(float &wv, int &wi) {
+    keep_best(wv, wi, __int_as_float(ror_i<1>(__float_as_int(wv))), ror_i<1>(wi));
+    keep_best(wv, wi, __int_as_float(ror_i<2>(__float_as_int(wv))), ror_i<2>(wi));
+    keep_best(wv, wi, __int_as_float(ror_i<4>(__float_as_int(wv))), ror_i<4>(wi));
+    keep_best(wv, wi, __int_as_float(ror_i<8>(__float_as_int(wv))), ror_i<8>(wi));
+    {
+        const auto pv = __builtin_amdgcn_permlane16_swap(__float_as_uint(wv), __float_as_uint(wv), false, false);
+        const auto pi = __builtin_amdgcn_permlane16_swap((unsigned)wi, (unsigned)wi, false, false);
+        wv = __uint_as_float(pv[0]); wi = (int)pi[0];
+        keep_best(wv, wi, __uint_as_float(pv[1]), (int)pi[1]);
+    }
+    {
+        const auto pv = __builtin_amdgcn_permlane32_swap(__float_as_uint(wv), __float_as_uint(wv), false, false);
+        const auto pi = __builtin_amdgcn_permlane32_swap((unsigned)wi, (unsigned)wi, false, false);
+        wv = __uint_as_float(pv[0]); wi = (int)pi[0];
+        keep_best(wv, wi, __uint_as_float(pv[1]), (int)pi[1]);
+    }
+}
 
 template <int VPL>
 __global__ __launch_bounds__(64) void topk_wave(const float *in, const int32_t *in_idx, int n, long long ld, int chunk,
@@ -53,12 +81,7 @@ __global__ __launch_bounds__(64) void topk_wave(const float *in, const int32_t *
         // wave-wide best (value, index)
         float wv = bv;
         int wi = bi;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const float ov2 = __shfl_xor(wv, o, 64);
-            const int oi2 = __shfl_xor(wi, o, 64);
-            if (before(ov2, oi2, wv, wi)) { wv = ov2; wi = oi2; }
-        }
+        wave_best(wv, wi);
         if (lane == 0) { ov[r] = wv; oi[r] = wi; }
         // the owner marks it taken (indices are unique within a row)
         if (bi == wi && bv == wv) {
