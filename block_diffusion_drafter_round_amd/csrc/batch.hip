@@ -242,9 +242,7 @@ __global__ __launch_bounds__(256) void batch_merge(BatchArgs a) {
     const size_t item0 = (((size_t)s * a.nkv + h) * ns) * a.G + j;     // split sp: item0 + sp * G
     float2 ml = make_float2(-1e30f, 0.f);
     if (lane < ns) ml = *reinterpret_cast<const float2 *>(a.pml + ((item0 + (size_t)lane * a.G) * 16 + r) * 2);
-    float M = ml.x;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float M = wave_max(ml.x);
     const float w = lane < ns ? __builtin_amdgcn_exp2f(ml.x - M) : 0.f;
     const float L = wave_sum(w * ml.y);
     const float *po = a.po + (item0 * 16 + r) * d + lane;
@@ -262,7 +260,8 @@ __global__ __launch_bounds__(256) void batch_merge(BatchArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float ws = sp0 + u < ns ? __shfl(w, sp0 + u, 64) : 0.f;
+            // the split index is the same on every lane: a scalar read of lane sp
+            const float ws = sp0 + u < ns ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sp0 + u)) : 0.f;
             acc0 += ws * v0[u];
             acc1 += ws * v1[u];
         }

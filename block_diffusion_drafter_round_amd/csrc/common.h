@@ -95,6 +95,10 @@ template <int N>
 __device__ __forceinline__ float row_ror(float v) {   // lane i gets lane (i - N) mod 16 of its row
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
 }
+// lane i gets lane i - 1 of its 16-lane row (the first lane of a row gets 0)
+__device__ __forceinline__ float row_shr1(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float xor16_sum(float v) {
     const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);

@@ -890,7 +890,7 @@ __device__ __forceinline__ void d2_prepare(SrLds &S, u32x4 *a, u32x4 *alo, int k
     float y[P];
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-        const float xp = __shfl(x[i], lane - 1, 64);
+        const float xp = row_shr1(x[i]);            // row r - 1 (unused for r = 0)
         const float2 bb = *reinterpret_cast<const float2 *>(base + (size_t)(c0 + i) * 2);
         y[i] = (bb.x + d0) * (r > 0 ? xp * rp : 0.f) + (bb.y + d1) * (x[i] * ri);
     }
@@ -931,7 +931,7 @@ __device__ __forceinline__ void d2_finish(float (&y)[4], int r, int c, const flo
     const float *b1 = base + 2 * (size_t)SS.H;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float yp = __shfl(y[i], lane - 1, 64);
+        const float yp = row_shr1(y[i]);            // row r - 1 (unused for r = 0)
         const float2 bb = *reinterpret_cast<const float2 *>(b1 + (size_t)(c + i) * 2);
         y[i] = (bb.x + d0) * (r > 0 ? yp : 0.f) + (bb.y + d1) * y[i];
     }
