@@ -792,7 +792,7 @@ __device__ __forceinline__ bool arrive(SrLds &S) {
     cbar();
     unsigned old = 0;
     if ((threadIdx.x & 63) == 0) old = lds_add(&S.done, 1u);
-    old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
+    old = __builtin_amdgcn_readfirstlane(old);      // every lane is active again: lane 0's value
     cbar();
     return (old & 7u) == 7u;
 }
