@@ -6,9 +6,17 @@
 // candidates of one row, 16 per lane in registers, and extracts the chunk's
 // k best by k rounds of a wave-wide argmax (order: larger value first, then
 // lower index), marking each winner as taken.  Each stage keeps k of every
-// 1024 candidates, until a single chunk holds them all (three stages for a
-// 151,936-token vocabulary).  Every load is in bounds (lanes past the chunk
-// hold "taken" entries), and every wave runs exactly k rounds.
+// 1024 candidates, until a single chunk holds them all.  Every load is in
+// bounds (lanes past the chunk hold "taken" entries), and every wave runs
+// exactly k rounds.
+//
+// A chunk's k best come out in selection order, so after the first stage a
+// row holds one sorted list per chunk.  When those lists fit in LDS (149
+// lists of 32 for a 151,936-token vocabulary), one wave per row merges them
+// instead of the further stages: lane j owns lists j, j + 64, ..., each
+// round picks the best list head across the wave, and the owner advances
+// that list.  The merge of sorted lists yields the row's k best in the same
+// total order, so both routes give the same result.
 #include <climits>
 
 #include "common.h"
@@ -92,6 +100,62 @@ __global__ __launch_bounds__(64) void topk_wave(const float *in, const int32_t *
     }
 }
 
+// Merge of a row's nl sorted lists of k (value, index) entries (one per
+// first-stage chunk, row stride ld) into the row's k best, in order.  The
+// four waves copy the lists to LDS (several loads in flight per lane), then
+// wave 0 merges them: lane j holds the heads of lists j + 64 u.
+constexpr int MERGE_THREADS = 256;
+template <int LMAX>
+__global__ __launch_bounds__(MERGE_THREADS) void topk_merge(const float *in_v, const int32_t *in_i, int nl, int k,
+                                                            long long ld, float *out_v, int32_t *out_i) {
+    extern __shared__ float2 lst[];                          // [nl][k]: (value, index bits)
+    const int lane = threadIdx.x, row = blockIdx.x;
+    const float *sv = in_v + (size_t)row * ld;
+    const int32_t *si = in_i + (size_t)row * ld;
+    const int ne = nl * k;
+#pragma unroll 4
+    for (int e = threadIdx.x; e < ne; e += MERGE_THREADS) lst[e] = make_float2(sv[e], __int_as_float(si[e]));
+    __syncthreads();
+    if (threadIdx.x >= 64) return;
+    float hv[LMAX];
+    int hi[LMAX], pos[LMAX];
+#pragma unroll
+    for (int u = 0; u < LMAX; ++u) {
+        const int li = lane + 64 * u;
+        const bool ok = li < nl;
+        const float2 h = lst[ok ? li * k : 0];
+        hv[u] = ok ? h.x : -INFINITY;
+        hi[u] = ok ? __float_as_int(h.y) : INT_MAX;
+        pos[u] = ok ? 0 : k;
+    }
+    float *ov = out_v + (size_t)row * k;
+    int32_t *oi = out_i + (size_t)row * k;
+    for (int r = 0; r < k; ++r) {
+        float bv = hv[0];
+        int bi = hi[0], bu = 0;
+#pragma unroll
+        for (int u = 1; u < LMAX; ++u)
+            if (before(hv[u], hi[u], bv, bi)) { bv = hv[u]; bi = hi[u]; bu = u; }
+        float wv = bv;
+        int wi = bi;
+        wave_best(wv, wi);
+        if (lane == 0) { ov[r] = wv; oi[r] = wi; }
+        // the owner of the winning head moves to that list's next entry (a
+        // "taken" entry past the list's end).  Several lanes match only when
+        // the winner is such an entry, and then every head left is one too.
+        if (bi == wi && bv == wv) {
+#pragma unroll
+            for (int u = 0; u < LMAX; ++u)
+                if (u == bu) {
+                    const int nx = ++pos[u];
+                    const float2 h = lst[nx < k ? (lane + 64 * u) * k + nx : 0];
+                    hv[u] = nx < k ? h.x : -INFINITY;
+                    hi[u] = nx < k ? __float_as_int(h.y) : INT_MAX;
+                }
+        }
+    }
+}
+
 // hproj[r][j] = sum_c hidden[r][c] * W[j][c]: one wave per output, f32
 // accumulation; lane l takes 8 consecutive columns per 512, with the loads
 // of up to four such groups in flight at once (H is a multiple of 256)
@@ -150,6 +214,17 @@ hipError_t topk_rows(const float *logits, long long ld, int rows, int vocab, int
     // second's; every later stage is smaller than both
     const size_t region_b = (size_t)rows * topk_chunks(vocab) * k;
     size_t off = 0;
+    const int nc1 = topk_chunks(vocab);
+    if (nc1 > 1 && nc1 <= TOPK_MERGE_LISTS && (size_t)nc1 * k * sizeof(float2) <= TOPK_MERGE_LDS) {
+        // first stage, then the merge of its sorted per-chunk lists
+        hipLaunchKernelGGL(topk_wave<TOPK_CHUNK / 64>, dim3(nc1, rows), dim3(64), 0, s, logits, (const int32_t *)nullptr,
+                           vocab, ld, TOPK_CHUNK, k, part_v, part_i, nc1 * k);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(topk_merge<TOPK_MERGE_LISTS / 64>, dim3(rows), dim3(MERGE_THREADS), (size_t)nc1 * k * sizeof(float2), s,
+                           part_v, part_i, nc1, k, (long long)nc1 * k, vals, idx);
+        return hipGetLastError();
+    }
     while (true) {
         const int nc = topk_chunks(n);
         const bool last = nc == 1;

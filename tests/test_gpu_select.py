@@ -33,8 +33,12 @@ def drafter():
     return cfg, D.Drafter(synth.make_weights(cfg), max_rows=16), D
 
 
+# (151936, 32): first stage + merge of 149 sorted lists (three per lane at
+# most); (151936, 64): lists past the merge's LDS, so three stages; (1025,
+# 64): a merge whose second list is one entry and 63 "taken" ones;
+# (70000, 17): 69 lists, two on lanes 0-4; 1000 and 100: one stage
 @pytest.mark.parametrize("vocab,k,rank,b", [(151936, 32, 64, 16), (151936, 64, 128, 3), (1000, 8, 16, 16),
-                                             (100, 64, 8, 2), (4097, 5, 64, 9)])
+                                             (100, 64, 8, 2), (4097, 5, 64, 9), (1025, 64, 8, 2), (70000, 17, 16, 5)])
 def test_propose_greedy_matches_oracle(drafter, vocab, k, rank, b):
     cfg, dr, D = drafter
     H = cfg.hidden
