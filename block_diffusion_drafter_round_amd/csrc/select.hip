@@ -3,9 +3,10 @@
 // rows' hidden states, packed for one small device-to-host copy.
 //
 // Top-k runs in stages of one kernel.  One wave takes a chunk of 1024
-// candidates of one row, 16 per lane in registers, and extracts the chunk's
-// k best by k rounds of a wave-wide argmax (order: larger value first, then
-// lower index), marking each winner as taken.  Each stage keeps k of every
+// candidates of one row, 16 per lane in registers, sorts each lane's 16
+// once (Batcher's odd-even merge network), and extracts the chunk's k best
+// by k rounds of a wave-wide argmax over the lanes' heads (order: larger
+// value first, then lower index); the winner's lane shifts its list up.  Each stage keeps k of every
 // 1024 candidates, until a single chunk holds them all.  Every load is in
 // bounds (lanes past the chunk hold "taken" entries), and every wave runs
 // exactly k rounds.
@@ -58,6 +59,41 @@ __device__ __forceinline__ void wave_best(float &wv, int &wi) {
     }
 }
 
+// Batcher's odd-even merge sort network on N (a power of two) entries: the
+// comparator list, built at compile time, so that every register index in
+// the sort is a constant.
+struct Cmp {
+    int a, b;
+};
+template <int N>
+struct OemNet {
+    Cmp c[8 * N];
+    int n;
+    constexpr OemNet() : c{}, n(0) {
+        for (int p = 1; p < N; p <<= 1)
+            for (int k = p; k >= 1; k >>= 1)
+                for (int j = k % p; j + k < N; j += 2 * k)
+                    for (int i = 0; i < (k < N - j - k ? k : N - j - k); ++i)
+                        if ((i + j) / (2 * p) == (i + j + k) / (2 * p)) c[n++] = Cmp{i + j, i + j + k};
+    }
+};
+static_assert(OemNet<16>{}.n == 63, "odd-even merge sort of 16 takes 63 comparators");
+// comparators I.. of the network: entry a ends up ranking before entry b
+template <int I, int N>
+__device__ __forceinline__ void oem_sort(float (&v)[N], int (&id)[N]) {
+    if constexpr (I < OemNet<N>{}.n) {
+        constexpr Cmp c = OemNet<N>{}.c[I];
+        const bool sw = before(v[c.b], id[c.b], v[c.a], id[c.a]);
+        const float va = v[c.a], vb = v[c.b];
+        const int ia = id[c.a], ib = id[c.b];
+        v[c.a] = sw ? vb : va;
+        id[c.a] = sw ? ib : ia;
+        v[c.b] = sw ? va : vb;
+        id[c.b] = sw ? ia : ib;
+        oem_sort<I + 1, N>(v, id);
+    }
+}
+
 template <int VPL>
 __global__ __launch_bounds__(64) void topk_wave(const float *in, const int32_t *in_idx, int n, long long ld, int chunk,
                                                 int k, float *out_v, int32_t *out_i, int out_ld) {
@@ -79,23 +115,22 @@ __global__ __launch_bounds__(64) void topk_wave(const float *in, const int32_t *
     }
     float *ov = out_v + (size_t)row * out_ld + (size_t)c * k;
     int32_t *oi = out_i + (size_t)row * out_ld + (size_t)c * k;
+    static_assert((VPL & (VPL - 1)) == 0, "the sort network takes a power of two");
+    oem_sort<0, VPL>(v, id);                                // v[0] is this lane's best
     for (int r = 0; r < k; ++r) {
-        // this lane's best remaining entry
-        float bv = v[0];
-        int bi = id[0], bj = 0;
-#pragma unroll
-        for (int j = 1; j < VPL; ++j)
-            if (before(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; bj = j; }
-        // wave-wide best (value, index)
-        float wv = bv;
-        int wi = bi;
+        // wave-wide best (value, index) of the lanes' heads
+        float wv = v[0];
+        int wi = id[0];
         wave_best(wv, wi);
         if (lane == 0) { ov[r] = wv; oi[r] = wi; }
-        // the owner marks it taken (indices are unique within a row)
-        if (bi == wi && bv == wv) {
+        // the owner's list moves up (indices are unique within a row; several
+        // lanes match only when the winner is a "taken" entry, and then all
+        // their entries are)
+        if (v[0] == wv && id[0] == wi) {
 #pragma unroll
-            for (int j = 0; j < VPL; ++j)
-                if (j == bj) { v[j] = -INFINITY; id[j] = INT_MAX; }
+            for (int j = 0; j + 1 < VPL; ++j) { v[j] = v[j + 1]; id[j] = id[j + 1]; }
+            v[VPL - 1] = -INFINITY;
+            id[VPL - 1] = INT_MAX;
         }
     }
 }
