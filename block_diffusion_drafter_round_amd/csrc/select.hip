@@ -6,10 +6,11 @@
 // candidates of one row, 16 per lane in registers, sorts each lane's 16
 // once (Batcher's odd-even merge network), and extracts the chunk's k best
 // by k rounds of a wave-wide argmax over the lanes' heads (order: larger
-// value first, then lower index); the winner's lane shifts its list up.  Each stage keeps k of every
-// 1024 candidates, until a single chunk holds them all.  Every load is in
-// bounds (lanes past the chunk hold "taken" entries), and every wave runs
-// exactly k rounds.
+// value first, then lower index; a -0 logit is reported as +0); the
+// winner's lane shifts its list up.  Each stage keeps k of every 1024
+// candidates, until a single chunk holds them all.  Every load is in bounds
+// (lanes past the chunk hold "taken" entries), and every wave runs exactly
+// k rounds.
 //
 // A chunk's k best come out in selection order, so after the first stage a
 // row holds one sorted list per chunk.  When those lists fit in LDS (149
@@ -26,37 +27,53 @@
 namespace dfl {
 namespace {
 
-// (value, index) ordering of the selection: true if a ranks before b
-__device__ __forceinline__ bool before(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
+// The selection order (larger value first, then lower index) as the
+// unsigned order of one 64-bit key: the high word is the value's bits made
+// monotonic (positive values with the sign bit set, negative ones
+// complemented; -0 is taken as +0, which compares equal to it), the low word
+// the complemented index.  Every comparison below is one 64-bit compare.
+// "Taken" entries are the key of (-inf, INT_MAX), below every real entry.
+typedef unsigned long long Key;
+__device__ __forceinline__ Key sel_key(float v, int i) {
+    unsigned u = __float_as_uint(v == 0.f ? 0.f : v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((Key)u << 32) | (unsigned)~i;
 }
-__device__ __forceinline__ void keep_best(float &wv, int &wi, float ov, int oi) {
-    if (before(ov, oi, wv, wi)) { wv = ov; wi = oi; }
+__device__ __forceinline__ float key_value(Key k) {
+    const unsigned u = (unsigned)(k >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
-// The wave's best (value, index): the selection order is total, so any
-// reduction tree picks the same entry.  Within 16-lane rows by DPP row
-// rotations, across rows by the lane swaps (a register swapped with itself
-// leaves a lane its own entry in one result and its partner's in the
-// other; values and indices move alike).  No LDS round trip.
+__device__ __forceinline__ int key_index(Key k) { return (int)~(unsigned)k; }
+__device__ __forceinline__ Key taken_key() { return sel_key(-INFINITY, INT_MAX); }
+
+// The wave's best key: the order is total, so any reduction tree picks the
+// same entry.  Within 16-lane rows by DPP row rotations, across rows by the
+// lane swaps (a register swapped with itself leaves a lane its own word in
+// one result and its partner's in the other).  No LDS round trip.
 template <int N>
-__device__ __forceinline__ int ror_i(int x) { return __builtin_amdgcn_update_dpp(0, x, 0x120 + N, 0xF, 0xF, false); }
-__device__ __forceinline__ void wave_best(float &wv, int &wi) {
-    keep_best(wv, wi, __int_as_float(ror_i<1>(__float_as_int(wv))), ror_i<1>(wi));
-    keep_best(wv, wi, __int_as_float(ror_i<2>(__float_as_int(wv))), ror_i<2>(wi));
-    keep_best(wv, wi, __int_as_float(ror_i<4>(__float_as_int(wv))), ror_i<4>(wi));
-    keep_best(wv, wi, __int_as_float(ror_i<8>(__float_as_int(wv))), ror_i<8>(wi));
+__device__ __forceinline__ unsigned ror_u(unsigned x) { return __builtin_amdgcn_update_dpp(0u, x, 0x120 + N, 0xF, 0xF, false); }
+template <int N>
+__device__ __forceinline__ Key ror_key(Key k) {
+    return ((Key)ror_u<N>((unsigned)(k >> 32)) << 32) | ror_u<N>((unsigned)k);
+}
+__device__ __forceinline__ Key wave_best(Key k) {
+    Key o = ror_key<1>(k); k = o > k ? o : k;
+    o = ror_key<2>(k); k = o > k ? o : k;
+    o = ror_key<4>(k); k = o > k ? o : k;
+    o = ror_key<8>(k); k = o > k ? o : k;
     {
-        const auto pv = __builtin_amdgcn_permlane16_swap(__float_as_uint(wv), __float_as_uint(wv), false, false);
-        const auto pi = __builtin_amdgcn_permlane16_swap((unsigned)wi, (unsigned)wi, false, false);
-        wv = __uint_as_float(pv[0]); wi = (int)pi[0];
-        keep_best(wv, wi, __uint_as_float(pv[1]), (int)pi[1]);
+        const auto h = __builtin_amdgcn_permlane16_swap((unsigned)(k >> 32), (unsigned)(k >> 32), false, false);
+        const auto l = __builtin_amdgcn_permlane16_swap((unsigned)k, (unsigned)k, false, false);
+        const Key a = ((Key)h[0] << 32) | l[0], c = ((Key)h[1] << 32) | l[1];
+        k = a > c ? a : c;
     }
     {
-        const auto pv = __builtin_amdgcn_permlane32_swap(__float_as_uint(wv), __float_as_uint(wv), false, false);
-        const auto pi = __builtin_amdgcn_permlane32_swap((unsigned)wi, (unsigned)wi, false, false);
-        wv = __uint_as_float(pv[0]); wi = (int)pi[0];
-        keep_best(wv, wi, __uint_as_float(pv[1]), (int)pi[1]);
+        const auto h = __builtin_amdgcn_permlane32_swap((unsigned)(k >> 32), (unsigned)(k >> 32), false, false);
+        const auto l = __builtin_amdgcn_permlane32_swap((unsigned)k, (unsigned)k, false, false);
+        const Key a = ((Key)h[0] << 32) | l[0], c = ((Key)h[1] << 32) | l[1];
+        k = a > c ? a : c;
     }
+    return k;
 }
 
 // Batcher's odd-even merge sort network on N (a power of two) entries: the
@@ -80,17 +97,13 @@ struct OemNet {
 static_assert(OemNet<16>{}.n == 63, "odd-even merge sort of 16 takes 63 comparators");
 // comparators I.. of the network: entry a ends up ranking before entry b
 template <int I, int N>
-__device__ __forceinline__ void oem_sort(float (&v)[N], int (&id)[N]) {
+__device__ __forceinline__ void oem_sort(Key (&x)[N]) {
     if constexpr (I < OemNet<N>{}.n) {
         constexpr Cmp c = OemNet<N>{}.c[I];
-        const bool sw = before(v[c.b], id[c.b], v[c.a], id[c.a]);
-        const float va = v[c.a], vb = v[c.b];
-        const int ia = id[c.a], ib = id[c.b];
-        v[c.a] = sw ? vb : va;
-        id[c.a] = sw ? ib : ia;
-        v[c.b] = sw ? va : vb;
-        id[c.b] = sw ? ia : ib;
-        oem_sort<I + 1, N>(v, id);
+        const Key a = x[c.a], b = x[c.b];
+        x[c.a] = a > b ? a : b;
+        x[c.b] = a > b ? b : a;
+        oem_sort<I + 1, N>(x);
     }
 }
 
@@ -101,91 +114,80 @@ __global__ __launch_bounds__(64) void topk_wave(const float *in, const int32_t *
     const int lo = c * chunk, hi = min(n, lo + chunk);
     const float *src = in + (size_t)row * ld;
     const int32_t *isrc = in_idx ? in_idx + (size_t)row * ld : nullptr;
-    float v[VPL];
-    int id[VPL];
+    Key x[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
         const int e = lo + j * 64 + lane;
         const bool ok = e < hi;
         const int es = ok ? e : lo;                         // in-bounds address for every lane
-        const float x = src[es];
-        const int xi = isrc ? isrc[es] : es;
-        v[j] = ok ? x : -INFINITY;
-        id[j] = ok ? xi : INT_MAX;                          // never ranks before a real entry
+        const float v = src[es];
+        const int vi = isrc ? isrc[es] : es;
+        x[j] = ok ? sel_key(v, vi) : taken_key();
     }
     float *ov = out_v + (size_t)row * out_ld + (size_t)c * k;
     int32_t *oi = out_i + (size_t)row * out_ld + (size_t)c * k;
     static_assert((VPL & (VPL - 1)) == 0, "the sort network takes a power of two");
-    oem_sort<0, VPL>(v, id);                                // v[0] is this lane's best
+    oem_sort<0, VPL>(x);                                    // x[0] is this lane's best
     for (int r = 0; r < k; ++r) {
-        // wave-wide best (value, index) of the lanes' heads
-        float wv = v[0];
-        int wi = id[0];
-        wave_best(wv, wi);
-        if (lane == 0) { ov[r] = wv; oi[r] = wi; }
-        // the owner's list moves up (indices are unique within a row; several
-        // lanes match only when the winner is a "taken" entry, and then all
-        // their entries are)
-        if (v[0] == wv && id[0] == wi) {
+        const Key w = wave_best(x[0]);                      // the best of the lanes' heads
+        if (lane == 0) { ov[r] = key_value(w); oi[r] = key_index(w); }
+        // the owner's list moves up (keys are unique within a row except
+        // "taken" ones, and a lane whose head is taken holds only those)
+        if (x[0] == w) {
 #pragma unroll
-            for (int j = 0; j + 1 < VPL; ++j) { v[j] = v[j + 1]; id[j] = id[j + 1]; }
-            v[VPL - 1] = -INFINITY;
-            id[VPL - 1] = INT_MAX;
+            for (int j = 0; j + 1 < VPL; ++j) x[j] = x[j + 1];
+            x[VPL - 1] = taken_key();
         }
     }
 }
 
 // Merge of a row's nl sorted lists of k (value, index) entries (one per
 // first-stage chunk, row stride ld) into the row's k best, in order.  The
-// four waves copy the lists to LDS (several loads in flight per lane), then
-// wave 0 merges them: lane j holds the heads of lists j + 64 u.
+// four waves copy the lists to LDS as keys (several loads in flight per
+// lane), then wave 0 merges them: lane j holds the heads of lists j + 64 u.
 constexpr int MERGE_THREADS = 256;
 template <int LMAX>
 __global__ __launch_bounds__(MERGE_THREADS) void topk_merge(const float *in_v, const int32_t *in_i, int nl, int k,
                                                             long long ld, float *out_v, int32_t *out_i) {
-    extern __shared__ float2 lst[];                          // [nl][k]: (value, index bits)
+    extern __shared__ Key lst[];                             // [nl][k]
     const int lane = threadIdx.x, row = blockIdx.x;
     const float *sv = in_v + (size_t)row * ld;
     const int32_t *si = in_i + (size_t)row * ld;
     const int ne = nl * k;
 #pragma unroll 4
-    for (int e = threadIdx.x; e < ne; e += MERGE_THREADS) lst[e] = make_float2(sv[e], __int_as_float(si[e]));
+    for (int e = threadIdx.x; e < ne; e += MERGE_THREADS) lst[e] = sel_key(sv[e], si[e]);
     __syncthreads();
     if (threadIdx.x >= 64) return;
-    float hv[LMAX];
-    int hi[LMAX], pos[LMAX];
+    Key h[LMAX];
+    int pos[LMAX];
 #pragma unroll
     for (int u = 0; u < LMAX; ++u) {
         const int li = lane + 64 * u;
         const bool ok = li < nl;
-        const float2 h = lst[ok ? li * k : 0];
-        hv[u] = ok ? h.x : -INFINITY;
-        hi[u] = ok ? __float_as_int(h.y) : INT_MAX;
+        const Key e = lst[ok ? li * k : 0];
+        h[u] = ok ? e : taken_key();
         pos[u] = ok ? 0 : k;
     }
     float *ov = out_v + (size_t)row * k;
     int32_t *oi = out_i + (size_t)row * k;
     for (int r = 0; r < k; ++r) {
-        float bv = hv[0];
-        int bi = hi[0], bu = 0;
+        Key b = h[0];
+        int bu = 0;
 #pragma unroll
         for (int u = 1; u < LMAX; ++u)
-            if (before(hv[u], hi[u], bv, bi)) { bv = hv[u]; bi = hi[u]; bu = u; }
-        float wv = bv;
-        int wi = bi;
-        wave_best(wv, wi);
-        if (lane == 0) { ov[r] = wv; oi[r] = wi; }
+            if (h[u] > b) { b = h[u]; bu = u; }
+        const Key w = wave_best(b);
+        if (lane == 0) { ov[r] = key_value(w); oi[r] = key_index(w); }
         // the owner of the winning head moves to that list's next entry (a
         // "taken" entry past the list's end).  Several lanes match only when
         // the winner is such an entry, and then every head left is one too.
-        if (bi == wi && bv == wv) {
+        if (b == w) {
 #pragma unroll
             for (int u = 0; u < LMAX; ++u)
                 if (u == bu) {
                     const int nx = ++pos[u];
-                    const float2 h = lst[nx < k ? (lane + 64 * u) * k + nx : 0];
-                    hv[u] = nx < k ? h.x : -INFINITY;
-                    hi[u] = nx < k ? __float_as_int(h.y) : INT_MAX;
+                    const Key e = lst[nx < k ? (lane + 64 * u) * k + nx : 0];
+                    h[u] = nx < k ? e : taken_key();
                 }
         }
     }
@@ -250,13 +252,13 @@ hipError_t topk_rows(const float *logits, long long ld, int rows, int vocab, int
     const size_t region_b = (size_t)rows * topk_chunks(vocab) * k;
     size_t off = 0;
     const int nc1 = topk_chunks(vocab);
-    if (nc1 > 1 && nc1 <= TOPK_MERGE_LISTS && (size_t)nc1 * k * sizeof(float2) <= TOPK_MERGE_LDS) {
+    if (nc1 > 1 && nc1 <= TOPK_MERGE_LISTS && (size_t)nc1 * k * sizeof(unsigned long long) <= TOPK_MERGE_LDS) {
         // first stage, then the merge of its sorted per-chunk lists
         hipLaunchKernelGGL(topk_wave<TOPK_CHUNK / 64>, dim3(nc1, rows), dim3(64), 0, s, logits, (const int32_t *)nullptr,
                            vocab, ld, TOPK_CHUNK, k, part_v, part_i, nc1 * k);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(topk_merge<TOPK_MERGE_LISTS / 64>, dim3(rows), dim3(MERGE_THREADS), (size_t)nc1 * k * sizeof(float2), s,
+        hipLaunchKernelGGL(topk_merge<TOPK_MERGE_LISTS / 64>, dim3(rows), dim3(MERGE_THREADS), (size_t)nc1 * k * sizeof(unsigned long long), s,
                            part_v, part_i, nc1, k, (long long)nc1 * k, vals, idx);
         return hipGetLastError();
     }
