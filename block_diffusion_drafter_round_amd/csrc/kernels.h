@@ -55,6 +55,7 @@ hipError_t gemm_tall(const GemmArgs &a, unsigned *cnt, hipStream_t s);
 constexpr int TOPK_CHUNK = 1024;     // candidates per wave and stage (16 per lane)
 constexpr int TOPK_MERGE_LISTS = 256; // first-stage lists one merge wave takes (4 per lane)
 constexpr int TOPK_MERGE_LDS = 65536; // LDS bytes of those lists (8 per entry)
+constexpr int TOPK_QUOTA = 8;         // entries per chunk the first stage keeps before the merge
 int topk_chunks(int n);
 // entries part_v / part_i must hold for rows of a vocabulary (k <= 64, so
 // each stage shrinks the candidates at least 16-fold)

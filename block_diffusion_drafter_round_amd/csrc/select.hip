@@ -12,13 +12,16 @@
 // (lanes past the chunk hold "taken" entries), and every wave runs exactly
 // k rounds.
 //
-// A chunk's k best come out in selection order, so after the first stage a
-// row holds one sorted list per chunk.  When those lists fit in LDS (149
-// lists of 32 for a 151,936-token vocabulary), one wave per row merges them
-// instead of the further stages: lane j owns lists j, j + 64, ..., each
-// round picks the best list head across the wave, and the owner advances
-// that list.  The merge of sorted lists yields the row's k best in the same
-// total order, so both routes give the same result.
+// A chunk's best come out in selection order, so after the first stage a
+// row holds one sorted list per chunk.  When k-entry lists fit in LDS (149
+// lists of 32 for a 151,936-token vocabulary), the first stage keeps only
+// each chunk's TOPK_QUOTA best and one wave per row merges the lists instead
+// of the further stages: lane j owns lists j, j + 64, ..., each round picks
+// the best list head across the wave, and the owner advances that list; a
+// list that runs out before the row's k are found is refilled with its
+// chunk's k best.  The merge of sorted lists yields the row's k best in the
+// same total order, so both routes give the same result.
+#include <algorithm>
 #include <climits>
 
 #include "common.h"
@@ -107,59 +110,79 @@ __device__ __forceinline__ void oem_sort(Key (&x)[N]) {
     }
 }
 
+// Loads one chunk [lo, hi) of a row (16 candidates per lane; lanes past
+// the chunk hold "taken" entries, every address in bounds) and sorts each
+// lane's candidates, best first.
+template <int VPL>
+__device__ __forceinline__ void load_sorted(Key (&x)[VPL], const float *src, const int32_t *isrc, int lo, int hi) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        const int e = lo + j * 64 + lane;
+        const bool ok = e < hi;
+        const int es = ok ? e : lo;
+        const float v = src[es];
+        const int vi = isrc ? isrc[es] : es;
+        x[j] = ok ? sel_key(v, vi) : taken_key();
+    }
+    static_assert((VPL & (VPL - 1)) == 0, "the sort network takes a power of two");
+    oem_sort<0, VPL>(x);
+}
+// The best key left in the wave (of the lanes' heads); the owner's list
+// moves up (keys are unique within a row except "taken" ones, and a lane
+// whose head is taken holds only those).
+template <int VPL>
+__device__ __forceinline__ Key take_best(Key (&x)[VPL]) {
+    const Key w = wave_best(x[0]);
+    if (x[0] == w) {
+#pragma unroll
+        for (int j = 0; j + 1 < VPL; ++j) x[j] = x[j + 1];
+        x[VPL - 1] = taken_key();
+    }
+    return w;
+}
+
 template <int VPL>
 __global__ __launch_bounds__(64) void topk_wave(const float *in, const int32_t *in_idx, int n, long long ld, int chunk,
                                                 int k, float *out_v, int32_t *out_i, int out_ld) {
     const int lane = threadIdx.x, row = blockIdx.y, c = blockIdx.x;
     const int lo = c * chunk, hi = min(n, lo + chunk);
-    const float *src = in + (size_t)row * ld;
-    const int32_t *isrc = in_idx ? in_idx + (size_t)row * ld : nullptr;
     Key x[VPL];
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-        const int e = lo + j * 64 + lane;
-        const bool ok = e < hi;
-        const int es = ok ? e : lo;                         // in-bounds address for every lane
-        const float v = src[es];
-        const int vi = isrc ? isrc[es] : es;
-        x[j] = ok ? sel_key(v, vi) : taken_key();
-    }
+    load_sorted(x, in + (size_t)row * ld, in_idx ? in_idx + (size_t)row * ld : nullptr, lo, hi);
     float *ov = out_v + (size_t)row * out_ld + (size_t)c * k;
     int32_t *oi = out_i + (size_t)row * out_ld + (size_t)c * k;
-    static_assert((VPL & (VPL - 1)) == 0, "the sort network takes a power of two");
-    oem_sort<0, VPL>(x);                                    // x[0] is this lane's best
     for (int r = 0; r < k; ++r) {
-        const Key w = wave_best(x[0]);                      // the best of the lanes' heads
+        const Key w = take_best(x);
         if (lane == 0) { ov[r] = key_value(w); oi[r] = key_index(w); }
-        // the owner's list moves up (keys are unique within a row except
-        // "taken" ones, and a lane whose head is taken holds only those)
-        if (x[0] == w) {
-#pragma unroll
-            for (int j = 0; j + 1 < VPL; ++j) x[j] = x[j + 1];
-            x[VPL - 1] = taken_key();
-        }
     }
 }
 
-// Merge of a row's nl sorted lists of k (value, index) entries (one per
-// first-stage chunk, row stride ld) into the row's k best, in order.  The
-// four waves copy the lists to LDS as keys (several loads in flight per
-// lane), then wave 0 merges them: lane j holds the heads of lists j + 64 u.
+// Merge of a row's nl sorted lists (one per first-stage chunk: that
+// chunk's q best, row stride ld) into the row's k best, in order.  The four
+// waves copy the lists to LDS as keys, list c at c * k, then wave 0 merges
+// them: lane j holds the heads of lists j + 64 u.  A chunk may hold more
+// than q of the row's k best: when a list of q runs out, the wave extracts
+// that chunk's k best from the logits into the list's LDS row (its first q
+// are the same entries), and the merge goes on.
 constexpr int MERGE_THREADS = 256;
-template <int LMAX>
-__global__ __launch_bounds__(MERGE_THREADS) void topk_merge(const float *in_v, const int32_t *in_i, int nl, int k,
-                                                            long long ld, float *out_v, int32_t *out_i) {
+template <int LMAX, int VPL>
+__global__ __launch_bounds__(MERGE_THREADS) void topk_merge(const float *in_v, const int32_t *in_i, int nl, int q, int k,
+                                                            long long ld, const float *logits, long long lld, int vocab,
+                                                            float *out_v, int32_t *out_i) {
     extern __shared__ Key lst[];                             // [nl][k]
     const int lane = threadIdx.x, row = blockIdx.x;
     const float *sv = in_v + (size_t)row * ld;
     const int32_t *si = in_i + (size_t)row * ld;
-    const int ne = nl * k;
+    const int ne = nl * q;
 #pragma unroll 4
-    for (int e = threadIdx.x; e < ne; e += MERGE_THREADS) lst[e] = sel_key(sv[e], si[e]);
+    for (int e = threadIdx.x; e < ne; e += MERGE_THREADS) {
+        const int c = e / q;
+        lst[c * k + (e - c * q)] = sel_key(sv[e], si[e]);
+    }
     __syncthreads();
     if (threadIdx.x >= 64) return;
     Key h[LMAX];
-    int pos[LMAX];
+    int pos[LMAX], len[LMAX];
 #pragma unroll
     for (int u = 0; u < LMAX; ++u) {
         const int li = lane + 64 * u;
@@ -167,7 +190,9 @@ __global__ __launch_bounds__(MERGE_THREADS) void topk_merge(const float *in_v, c
         const Key e = lst[ok ? li * k : 0];
         h[u] = ok ? e : taken_key();
         pos[u] = ok ? 0 : k;
+        len[u] = ok ? q : k;
     }
+    const float *lrow = logits + (size_t)row * lld;
     float *ov = out_v + (size_t)row * k;
     int32_t *oi = out_i + (size_t)row * k;
     for (int r = 0; r < k; ++r) {
@@ -179,16 +204,43 @@ __global__ __launch_bounds__(MERGE_THREADS) void topk_merge(const float *in_v, c
         const Key w = wave_best(b);
         if (lane == 0) { ov[r] = key_value(w); oi[r] = key_index(w); }
         // the owner of the winning head moves to that list's next entry (a
-        // "taken" entry past the list's end).  Several lanes match only when
-        // the winner is such an entry, and then every head left is one too.
+        // "taken" entry past a list of k).  Several lanes match only when the
+        // winner is such an entry, and then every head left is one too.
+        bool need = false;
+        int nli = 0;
         if (b == w) {
 #pragma unroll
             for (int u = 0; u < LMAX; ++u)
                 if (u == bu) {
                     const int nx = ++pos[u];
-                    const Key e = lst[nx < k ? (lane + 64 * u) * k + nx : 0];
-                    h[u] = nx < k ? e : taken_key();
+                    need = nx == len[u] && len[u] < k;
+                    nli = lane + 64 * u;
+                    const Key e = lst[nx < len[u] ? nli * k + nx : 0];
+                    h[u] = nx < len[u] ? e : taken_key();
                 }
+        }
+        // lists of q that ran out: the whole wave refills each from its chunk
+        unsigned long long m = __ballot(need);
+        while (m) {
+            const int L = __builtin_ctzll(m);
+            m &= m - 1;
+            const int li = __builtin_amdgcn_readlane(nli, L);
+            const int lo = li * TOPK_CHUNK;
+            Key x[VPL];
+            load_sorted(x, lrow, nullptr, lo, min(vocab, lo + TOPK_CHUNK));
+            for (int t = 0; t < k; ++t) {
+                const Key y = take_best(x);
+                if (lane == 0) lst[li * k + t] = y;
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (lane == L) {
+#pragma unroll
+                for (int u = 0; u < LMAX; ++u)
+                    if (u == bu) {
+                        len[u] = k;
+                        h[u] = lst[li * k + pos[u]];
+                    }
+            }
         }
     }
 }
@@ -253,13 +305,15 @@ hipError_t topk_rows(const float *logits, long long ld, int rows, int vocab, int
     size_t off = 0;
     const int nc1 = topk_chunks(vocab);
     if (nc1 > 1 && nc1 <= TOPK_MERGE_LISTS && (size_t)nc1 * k * sizeof(unsigned long long) <= TOPK_MERGE_LDS) {
-        // first stage, then the merge of its sorted per-chunk lists
+        // first stage (each chunk's q best), then the merge of its sorted lists
+        const int q = std::min(k, TOPK_QUOTA);
         hipLaunchKernelGGL(topk_wave<TOPK_CHUNK / 64>, dim3(nc1, rows), dim3(64), 0, s, logits, (const int32_t *)nullptr,
-                           vocab, ld, TOPK_CHUNK, k, part_v, part_i, nc1 * k);
+                           vocab, ld, TOPK_CHUNK, q, part_v, part_i, nc1 * q);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(topk_merge<TOPK_MERGE_LISTS / 64>, dim3(rows), dim3(MERGE_THREADS), (size_t)nc1 * k * sizeof(unsigned long long), s,
-                           part_v, part_i, nc1, k, (long long)nc1 * k, vals, idx);
+        hipLaunchKernelGGL((topk_merge<TOPK_MERGE_LISTS / 64, TOPK_CHUNK / 64>), dim3(rows), dim3(MERGE_THREADS),
+                           (size_t)nc1 * k * sizeof(unsigned long long), s, part_v, part_i, nc1, q, k, (long long)nc1 * q,
+                           logits, ld, vocab, vals, idx);
         return hipGetLastError();
     }
     while (true) {

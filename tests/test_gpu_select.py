@@ -98,3 +98,37 @@ def test_propose_rejects_bad_arguments(drafter):
         with pytest.raises(D.DflashError) as ei:
             D.dflash2_propose_greedy(dr.model, sel, logits, hidden, b, 0, dr.ws, dr.ws_bytes)
         assert ei.value.code == D.DFLASH_E_INVAL
+
+
+@pytest.mark.parametrize("hot", [(7,), (7, 100), (0, 148)])
+def test_propose_topk_concentrated(drafter, hot):
+    """The row's k best packed into one or two 1024-entry chunks (more than
+    the 8 per chunk the first stage keeps before the merge), with ties:
+    the device top-k must still equal the oracle's bit for bit."""
+    cfg, dr, D = drafter
+    vocab, k, rank, b = 151936, 32, 16, 4
+    rng = np.random.default_rng(1000 + sum(hot))
+    logits = (np.round(rng.standard_normal((b, vocab)) * 8) / 8).astype(np.float32)
+    for r in range(b):
+        for c in hot:
+            lo, hi = c * 1024, min(vocab, c * 1024 + 1024)
+            pick = rng.choice(hi - lo, size=min(40, hi - lo), replace=False) + lo
+            logits[r, pick] = 100.0 + np.round(rng.standard_normal(len(pick)) * 2) / 2    # ties among them too
+    hidden = rng.standard_normal((b, cfg.hidden)).astype(np.float32)
+    w_hp = synth.encode_bf16((rng.standard_normal((rank, cfg.hidden)) * 0.02).astype(np.float32))
+    tab = synth.encode_bf16(rng.standard_normal((vocab, rank)).astype(np.float32))
+    sel = D.make_selector(tab, tab, k, torch.from_numpy(w_hp.view(np.int16)).cuda())
+    nd = b - 1
+    packed = torch.zeros(nd * (2 * k + rank), dtype=torch.int32, device="cuda")
+    D.dflash2_propose_prepare(dr.model, sel, dev(logits), dev(hidden), b, packed, dr.ws, dr.ws_bytes)
+    torch.cuda.synchronize()
+    pk = packed.cpu().numpy()
+    g_vals = pk[:nd * k].view(np.float32).reshape(nd, k)
+    g_idx = pk[nd * k:2 * nd * k].reshape(nd, k)
+    o_vals, o_idx = P.topk_rows(logits[1:], k)
+    print(f"[select] concentrated top-k, hot chunks {hot}", flush=True)
+    assert np.array_equal(g_idx, o_idx), "top-k ids differ"
+    assert np.array_equal(g_vals, o_vals), "top-k values differ"
+    # the k best do come from the hot chunks, more than 8 from some chunk
+    assert np.all(np.isin(o_idx // 1024, hot))
+    assert max(np.bincount(o_idx[r] // 1024).max() for r in range(nd)) > 8
