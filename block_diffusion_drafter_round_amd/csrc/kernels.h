@@ -54,7 +54,7 @@ hipError_t gemm_tall(const GemmArgs &a, unsigned *cnt, hipStream_t s);
 // ---- DFlash2 proposal: top-k over draft logits, rank-r hidden projection ----
 constexpr int TOPK_CHUNK = 1024;     // candidates per wave and stage (16 per lane)
 constexpr int TOPK_MERGE_LISTS = 256; // first-stage lists one merge wave takes (4 per lane)
-constexpr int TOPK_MERGE_LDS = 65536; // LDS bytes of those lists (8 per entry)
+constexpr int TOPK_MERGE_LDS = 57344; // LDS bytes of those lists (8 per entry; 8 KiB more for the ranking)
 constexpr int TOPK_QUOTA = 8;         // entries per chunk the first stage keeps before the merge
 int topk_chunks(int n);
 // entries part_v / part_i must hold for rows of a vocabulary (k <= 64, so

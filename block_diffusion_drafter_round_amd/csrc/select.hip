@@ -20,7 +20,9 @@
 // the best list head across the wave, and the owner advances that list; a
 // list that runs out before the row's k are found is refilled with its
 // chunk's k best.  The merge of sorted lists yields the row's k best in the
-// same total order, so both routes give the same result.
+// same total order, so both routes give the same result.  Most rows skip
+// the k rounds: the merge ranks the few candidates that can reach the k
+// best among themselves instead (see topk_merge).
 #include <algorithm>
 #include <climits>
 
@@ -165,21 +167,72 @@ __global__ __launch_bounds__(64) void topk_wave(const float *in, const int32_t *
 // that chunk's k best from the logits into the list's LDS row (its first q
 // are the same entries), and the merge goes on.
 constexpr int MERGE_THREADS = 256;
+constexpr int MERGE_SMAX = 512;        // candidates the ranking route takes (more: the sequential merge)
 template <int LMAX, int VPL>
 __global__ __launch_bounds__(MERGE_THREADS) void topk_merge(const float *in_v, const int32_t *in_i, int nl, int q, int k,
                                                             long long ld, const float *logits, long long lld, int vocab,
                                                             float *out_v, int32_t *out_i) {
     extern __shared__ Key lst[];                             // [nl][k]
+    __shared__ Key surv[MERGE_SMAX], thr;
+    __shared__ int srank[MERGE_SMAX], ns, fb;
+    __shared__ unsigned char slast[MERGE_SMAX];
     const int lane = threadIdx.x, row = blockIdx.x;
     const float *sv = in_v + (size_t)row * ld;
     const int32_t *si = in_i + (size_t)row * ld;
+    float *ov = out_v + (size_t)row * k;
+    int32_t *oi = out_i + (size_t)row * k;
     const int ne = nl * q;
+    if (threadIdx.x == 0) { ns = 0; fb = 0; }
 #pragma unroll 4
     for (int e = threadIdx.x; e < ne; e += MERGE_THREADS) {
         const int c = e / q;
         lst[c * k + (e - c * q)] = sel_key(sv[e], si[e]);
     }
     __syncthreads();
+    if (nl >= k) {
+        // Ranking route.  The k-th best list head L bounds the row's k-th
+        // best from below (k real keys are >= L), so the k best are among
+        // the candidates >= L: rank those among themselves by counting.  If
+        // a list's last kept entry (position q - 1 < k - 1) ranks among the
+        // k best, its chunk may hold more of them: the sequential merge
+        // below, which refills such lists, decides the row instead.
+        for (int t = threadIdx.x; t < nl; t += MERGE_THREADS) {
+            const Key hk = lst[t * k];
+            int rk = 0;
+            for (int c = 0; c < nl; ++c) rk += lst[c * k] > hk ? 1 : 0;
+            if (rk == k - 1) thr = hk;                      // heads are distinct real keys: exactly one
+        }
+        __syncthreads();
+        const Key L = thr;
+        for (int e = threadIdx.x; e < ne; e += MERGE_THREADS) {
+            const int c = e / q, j = e - c * q;
+            const Key x = lst[c * k + j];
+            if (x >= L) {
+                const int sl = atomicAdd(&ns, 1);
+                if (sl < MERGE_SMAX) {
+                    surv[sl] = x;
+                    slast[sl] = j == q - 1 && q < k;
+                }
+            }
+        }
+        __syncthreads();
+        const int S = ns;
+        if (S <= MERGE_SMAX) {
+            for (int t = threadIdx.x; t < S; t += MERGE_THREADS) {
+                const Key x = surv[t];
+                int rk = 0;
+                for (int u = 0; u < S; ++u) rk += surv[u] > x ? 1 : 0;
+                srank[t] = rk;
+                if (rk < k && slast[t]) fb = 1;
+            }
+            __syncthreads();
+            if (!fb) {
+                for (int t = threadIdx.x; t < S; t += MERGE_THREADS)
+                    if (srank[t] < k) { ov[srank[t]] = key_value(surv[t]); oi[srank[t]] = key_index(surv[t]); }
+                return;
+            }
+        }
+    }
     if (threadIdx.x >= 64) return;
     Key h[LMAX];
     int pos[LMAX], len[LMAX];
@@ -193,8 +246,6 @@ __global__ __launch_bounds__(MERGE_THREADS) void topk_merge(const float *in_v, c
         len[u] = ok ? q : k;
     }
     const float *lrow = logits + (size_t)row * lld;
-    float *ov = out_v + (size_t)row * k;
-    int32_t *oi = out_i + (size_t)row * k;
     for (int r = 0; r < k; ++r) {
         Key b = h[0];
         int bu = 0;
