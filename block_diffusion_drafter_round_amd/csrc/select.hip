@@ -25,6 +25,7 @@
 // best among themselves instead (see topk_merge).
 #include <algorithm>
 #include <climits>
+#include <cstdint>
 
 #include "common.h"
 #include "kernels.h"
@@ -114,18 +115,37 @@ __device__ __forceinline__ void oem_sort(Key (&x)[N]) {
 
 // Loads one chunk [lo, hi) of a row (16 candidates per lane; lanes past
 // the chunk hold "taken" entries, every address in bounds) and sorts each
-// lane's candidates, best first.
+// lane's candidates, best first.  A whole chunk of 16-byte aligned logits
+// is read as 16 contiguous candidates per lane in 16-byte loads; otherwise
+// lane l takes candidates l, l + 64, ... (the choice is the same for the
+// whole wave, so each candidate is read exactly once).
 template <int VPL>
 __device__ __forceinline__ void load_sorted(Key (&x)[VPL], const float *src, const int32_t *isrc, int lo, int hi) {
     const int lane = threadIdx.x & 63;
+    const bool vec = !isrc && hi - lo == 64 * VPL && (reinterpret_cast<uintptr_t>(src + lo) & 15) == 0;
+    if (vec) {
+        static_assert(VPL % 4 == 0, "16-byte loads");
+        const int e0 = lo + lane * VPL;
+        float4 v[VPL / 4];
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-        const int e = lo + j * 64 + lane;
-        const bool ok = e < hi;
-        const int es = ok ? e : lo;
-        const float v = src[es];
-        const int vi = isrc ? isrc[es] : es;
-        x[j] = ok ? sel_key(v, vi) : taken_key();
+        for (int j = 0; j < VPL / 4; ++j) v[j] = *reinterpret_cast<const float4 *>(src + e0 + 4 * j);
+#pragma unroll
+        for (int j = 0; j < VPL / 4; ++j) {
+            x[4 * j] = sel_key(v[j].x, e0 + 4 * j);
+            x[4 * j + 1] = sel_key(v[j].y, e0 + 4 * j + 1);
+            x[4 * j + 2] = sel_key(v[j].z, e0 + 4 * j + 2);
+            x[4 * j + 3] = sel_key(v[j].w, e0 + 4 * j + 3);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            const int e = lo + j * 64 + lane;
+            const bool ok = e < hi;
+            const int es = ok ? e : lo;
+            const float v = src[es];
+            const int vi = isrc ? isrc[es] : es;
+            x[j] = ok ? sel_key(v, vi) : taken_key();
+        }
     }
     static_assert((VPL & (VPL - 1)) == 0, "the sort network takes a power of two");
     oem_sort<0, VPL>(x);
