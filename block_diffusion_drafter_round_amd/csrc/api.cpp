@@ -946,14 +946,25 @@ int dflash2_propose_greedy(const dflash_model *m, const dflash2_selector *sel, c
     hipStream_t s = (hipStream_t)stream;
     int rc = propose_prepare(m, sel, draft_logits, hidden, b, packed, ws, ws_bytes, s);
     if (rc) return rc;
-    // the one small device-to-host copy of the round, then the host walk
-    std::vector<uint32_t> host(words);
-    hipError_t e = hipMemcpyAsync(host.data(), packed, 4 * words, hipMemcpyDeviceToHost, s);
+    // the one small device-to-host copy of the round, into pinned memory (a
+    // copy into pageable memory goes through the runtime's staging buffer),
+    // then the host walk.  Each host thread allocates its buffer once, at
+    // the largest packed block, and holds it until the process ends.
+    constexpr size_t MAX_WORDS = (size_t)(MAX_BLOCK - 1) * (2 * DFLASH2_MAX_TOPK + DFLASH2_MAX_RANK);
+    thread_local uint32_t *host = nullptr;
+    if (!host) {
+        void *p = nullptr;
+        hipError_t ea = hipHostMalloc(&p, 4 * MAX_WORDS, hipHostMallocDefault);
+        if (ea != hipSuccess) return hip_fail(ea, "dflash2_propose_greedy pinned host buffer");
+        host = static_cast<uint32_t *>(p);
+    }
+    if (words > MAX_WORDS) return fail(DFLASH_E_INVAL, "packed block larger than its bound");
+    hipError_t e = hipMemcpyAsync(host, packed, 4 * words, hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "dflash2_propose_greedy copy");
-    const float *vals = reinterpret_cast<const float *>(host.data());
-    const int32_t *idx = reinterpret_cast<const int32_t *>(host.data() + (size_t)nd * k);
-    const float *hp = reinterpret_cast<const float *>(host.data() + (size_t)2 * nd * k);
+    const float *vals = reinterpret_cast<const float *>(host);
+    const int32_t *idx = reinterpret_cast<const int32_t *>(host + (size_t)nd * k);
+    const float *hp = reinterpret_cast<const float *>(host + (size_t)2 * nd * k);
     rc = dflash2_walk_greedy(sel, vals, idx, hp, nd, anchor, drafts);
     return rc ? fail(rc, "dflash2_propose_greedy: walk rejected its inputs") : DFLASH_OK;
 }

@@ -127,7 +127,10 @@ int dflash2_propose_prepare(const struct dflash_model *m, const dflash2_selector
  * device step into the workspace, ONE device-to-host copy of its
  * nd*(2*top_k + rank) words, then dflash2_walk_greedy from `anchor` on the
  * host codebooks.  Writes the nd = b - 1 drafted tokens to host `drafts`.
- * Synchronises `stream` (the walk needs the copied values). */
+ * Synchronises `stream` (the walk needs the copied values).  The copy lands
+ * in pinned host memory: each calling host thread allocates one buffer of
+ * 15 * (2 * DFLASH2_MAX_TOPK + DFLASH2_MAX_RANK) words (23 KiB) on its first
+ * call and keeps it until the process ends. */
 int dflash2_propose_greedy(const struct dflash_model *m, const dflash2_selector *sel, const float *draft_logits,
                            const float *hidden, int32_t b, int32_t anchor, int32_t *drafts, void *ws, size_t ws_bytes,
                            void *stream);
