@@ -33,18 +33,40 @@ float bf16_to_f32(uint16_t h) {
 }
 
 // pair scores of one slot: unary[k] + sum_r pred[prev][r] * hproj[r] * succ[cand[k]][r]
-// (float64 over the stored values); returns false on an out-of-vocabulary token
+// (float64 over the stored values, r in increasing order); returns false on
+// an out-of-vocabulary token.  pred[prev][r] * hproj[r] is formed once per
+// slot (the product is evaluated left to right either way), and four
+// candidates' sums run side by side, each in its own order, so every score
+// has the same bits as a one-at-a-time evaluation.
 bool slot_scores(const dflash2_selector *s, const float *unary, const int32_t *cand, int32_t prev,
                  const float *hproj, double *score) {
     if (prev < 0 || prev >= s->vocab) return false;
-    const uint16_t *pv = s->pred_codebook + (size_t)prev * s->rank;
-    for (int k = 0; k < s->top_k; ++k) {
-        const int32_t c = cand[k];
-        if (c < 0 || c >= s->vocab) return false;
-        const uint16_t *sv = s->succ_codebook + (size_t)c * s->rank;
+    const int R = s->rank, K = s->top_k;
+    for (int k = 0; k < K; ++k)
+        if (cand[k] < 0 || cand[k] >= s->vocab) return false;
+    const uint16_t *pv = s->pred_codebook + (size_t)prev * R;
+    double w[DFLASH2_MAX_RANK];
+    for (int r = 0; r < R; ++r) w[r] = (double)bf16_to_f32(pv[r]) * (double)hproj[r];
+    int k = 0;
+    for (; k + 4 <= K; k += 4) {
+        const uint16_t *s0 = s->succ_codebook + (size_t)cand[k] * R, *s1 = s->succ_codebook + (size_t)cand[k + 1] * R,
+                       *s2 = s->succ_codebook + (size_t)cand[k + 2] * R, *s3 = s->succ_codebook + (size_t)cand[k + 3] * R;
+        double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+        for (int r = 0; r < R; ++r) {
+            a0 += w[r] * (double)bf16_to_f32(s0[r]);
+            a1 += w[r] * (double)bf16_to_f32(s1[r]);
+            a2 += w[r] * (double)bf16_to_f32(s2[r]);
+            a3 += w[r] * (double)bf16_to_f32(s3[r]);
+        }
+        score[k] = (double)unary[k] + a0;
+        score[k + 1] = (double)unary[k + 1] + a1;
+        score[k + 2] = (double)unary[k + 2] + a2;
+        score[k + 3] = (double)unary[k + 3] + a3;
+    }
+    for (; k < K; ++k) {
+        const uint16_t *sv = s->succ_codebook + (size_t)cand[k] * R;
         double pair = 0.0;
-        for (int r = 0; r < s->rank; ++r)
-            pair += (double)bf16_to_f32(pv[r]) * (double)hproj[r] * (double)bf16_to_f32(sv[r]);
+        for (int r = 0; r < R; ++r) pair += w[r] * (double)bf16_to_f32(sv[r]);
         score[k] = (double)unary[k] + pair;
     }
     return true;
