@@ -911,9 +911,8 @@ int propose_prepare(const dflash_model *m, const dflash2_selector *sel, const fl
     int32_t *idx = reinterpret_cast<int32_t *>(packed + (size_t)nd * k);
     float *hp = reinterpret_cast<float *>(packed + (size_t)2 * nd * k);
     const long long V = sel->vocab;
-    hipError_t e = dfl::topk_rows(logits + V, V, nd, sel->vocab, k, pv, pi, vals, idx, s);
-    if (e == hipSuccess)
-        e = dfl::hidden_projection(hidden + m->cfg.hidden, m->cfg.hidden, sel->w_hidden_proj, sel->rank, nd, hp, s);
+    hipError_t e = dfl::topk_rows(logits + V, V, nd, sel->vocab, k, pv, pi, vals, idx, hidden + m->cfg.hidden,
+                                  m->cfg.hidden, sel->w_hidden_proj, sel->rank, hp, s);
     return e == hipSuccess ? DFLASH_OK : hip_fail(e, "dflash2_propose");
 }
 

@@ -61,9 +61,11 @@ int topk_chunks(int n);
 // each stage shrinks the candidates at least 16-fold)
 size_t topk_scratch_entries(int rows, int vocab, int k);
 // Per row: the k largest logits (larger first, then lower index) and their
-// indices.
+// indices; with them, hout[r][j] = hidden[r] . w[j] (as hidden_projection,
+// in the same launch as the last top-k step where it can be).
 hipError_t topk_rows(const float *logits, long long ld, int rows, int vocab, int k, float *part_v, int32_t *part_i,
-                     float *vals, int32_t *idx, hipStream_t s);
+                     float *vals, int32_t *idx, const float *hidden, int H, const void *w, int rank, float *hout,
+                     hipStream_t s);
 // out[r][j] = hidden[r] . w[j] for bf16 w [rank][H], f32 accumulation
 hipError_t hidden_projection(const float *hidden, int H, const void *w, int rank, int rows, float *out, hipStream_t s);
 

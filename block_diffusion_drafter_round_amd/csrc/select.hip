@@ -179,6 +179,46 @@ __global__ __launch_bounds__(64) void topk_wave(const float *in, const int32_t *
     }
 }
 
+// hproj[r][j] = sum_c hidden[r][c] * W[j][c]: one wave per output, f32
+// accumulation; lane l takes 8 consecutive columns per 512, with the loads
+// of up to four such groups in flight at once (H is a multiple of 256)
+__device__ __forceinline__ void hproj_wave(const float *hidden, int H, const uint16_t *w, int rank, int rows, float *out,
+                                           int wave) {
+    const int lane = threadIdx.x & 63;
+    if (wave >= rows * rank) return;
+    const int r = wave / rank, j = wave - r * rank;
+    const float *x = hidden + (size_t)r * H;
+    const uint16_t *wr = w + (size_t)j * H;
+    float s = 0.f;
+    for (int c0 = 0; c0 < H; c0 += 4 * 512) {
+        u32x4 wv[4];
+        float4 xa[4], xb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = min(c0 + u * 512 + 8 * lane, H - 8);
+            wv[u] = *reinterpret_cast<const u32x4 *>(wr + c);
+            xa[u] = *reinterpret_cast<const float4 *>(x + c);
+            xb[u] = *reinterpret_cast<const float4 *>(x + c + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (c0 + u * 512 + 8 * lane >= H) continue;
+            const float xs[8] = {xa[u].x, xa[u].y, xa[u].z, xa[u].w, xb[u].x, xb[u].y, xb[u].z, xb[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s += xs[2 * i] * bf16_bits_to_f32(wv[u][i] & 0xFFFFu);
+                s += xs[2 * i + 1] * __uint_as_float(wv[u][i] & 0xFFFF0000u);
+            }
+        }
+    }
+    s = wave_sum(s);
+    if (lane == 0) out[(size_t)r * rank + j] = s;
+}
+__global__ __launch_bounds__(256) void hidden_proj(const float *hidden, int H, const uint16_t *w, int rank, int rows,
+                                                   float *out) {
+    hproj_wave(hidden, H, w, rank, rows, out, blockIdx.x * 4 + (threadIdx.x >> 6));
+}
+
 // Merge of a row's nl sorted lists (one per first-stage chunk: that
 // chunk's q best, row stride ld) into the row's k best, in order.  The four
 // waves copy the lists to LDS as keys, list c at c * k, then wave 0 merges
@@ -187,11 +227,24 @@ __global__ __launch_bounds__(64) void topk_wave(const float *in, const int32_t *
 // that chunk's k best from the logits into the list's LDS row (its first q
 // are the same entries), and the merge goes on.
 constexpr int MERGE_THREADS = 256;
+static_assert(MERGE_THREADS == 256, "projection blocks are four waves");
+struct HProjArgs {
+    const float *hidden;
+    int H;
+    const uint16_t *w;
+    int rank, rows;
+    float *out;
+};
 constexpr int MERGE_SMAX = 512;        // candidates the ranking route takes (more: the sequential merge)
 template <int LMAX, int VPL>
 __global__ __launch_bounds__(MERGE_THREADS) void topk_merge(const float *in_v, const int32_t *in_i, int nl, int q, int k,
                                                             long long ld, const float *logits, long long lld, int vocab,
-                                                            float *out_v, int32_t *out_i) {
+                                                            float *out_v, int32_t *out_i, int rows, HProjArgs hp) {
+    // blocks past the rows run the rank-r projection, four output waves each
+    if ((int)blockIdx.x >= rows) {
+        hproj_wave(hp.hidden, hp.H, hp.w, hp.rank, hp.rows, hp.out, ((int)blockIdx.x - rows) * 4 + (threadIdx.x >> 6));
+        return;
+    }
     extern __shared__ Key lst[];                             // [nl][k]
     __shared__ Key surv[MERGE_SMAX], thr;
     __shared__ int srank[MERGE_SMAX], ns, fb;
@@ -316,42 +369,6 @@ __global__ __launch_bounds__(MERGE_THREADS) void topk_merge(const float *in_v, c
     }
 }
 
-// hproj[r][j] = sum_c hidden[r][c] * W[j][c]: one wave per output, f32
-// accumulation; lane l takes 8 consecutive columns per 512, with the loads
-// of up to four such groups in flight at once (H is a multiple of 256)
-__global__ __launch_bounds__(256) void hidden_proj(const float *hidden, int H, const uint16_t *w, int rank, int rows,
-                                                   float *out) {
-    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (wave >= rows * rank) return;
-    const int r = wave / rank, j = wave - r * rank;
-    const float *x = hidden + (size_t)r * H;
-    const uint16_t *wr = w + (size_t)j * H;
-    float s = 0.f;
-    for (int c0 = 0; c0 < H; c0 += 4 * 512) {
-        u32x4 wv[4];
-        float4 xa[4], xb[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = min(c0 + u * 512 + 8 * lane, H - 8);
-            wv[u] = *reinterpret_cast<const u32x4 *>(wr + c);
-            xa[u] = *reinterpret_cast<const float4 *>(x + c);
-            xb[u] = *reinterpret_cast<const float4 *>(x + c + 4);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (c0 + u * 512 + 8 * lane >= H) continue;
-            const float xs[8] = {xa[u].x, xa[u].y, xa[u].z, xa[u].w, xb[u].x, xb[u].y, xb[u].z, xb[u].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s += xs[2 * i] * bf16_bits_to_f32(wv[u][i] & 0xFFFFu);
-                s += xs[2 * i + 1] * __uint_as_float(wv[u][i] & 0xFFFF0000u);
-            }
-        }
-    }
-    s = wave_sum(s);
-    if (lane == 0) out[(size_t)r * rank + j] = s;
-}
-
 }  // namespace
 
 int topk_chunks(int vocab) { return (vocab + TOPK_CHUNK - 1) / TOPK_CHUNK; }
@@ -363,7 +380,8 @@ size_t topk_scratch_entries(int rows, int vocab, int k) {
 }
 
 hipError_t topk_rows(const float *logits, long long ld, int rows, int vocab, int k, float *part_v, int32_t *part_i,
-                     float *vals, int32_t *idx, hipStream_t s) {
+                     float *vals, int32_t *idx, const float *hidden, int H, const void *w, int rank, float *hout,
+                     hipStream_t s) {
     // each stage keeps the k best of every TOPK_CHUNK candidates, until one
     // chunk holds them all; stages alternate between two candidate regions
     const float *in = logits;
@@ -382,9 +400,11 @@ hipError_t topk_rows(const float *logits, long long ld, int rows, int vocab, int
                            vocab, ld, TOPK_CHUNK, q, part_v, part_i, nc1 * q);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((topk_merge<TOPK_MERGE_LISTS / 64, TOPK_CHUNK / 64>), dim3(rows), dim3(MERGE_THREADS),
+        const HProjArgs ha{hidden, H, (const uint16_t *)w, rank, rows, hout};
+        const int pblocks = (rows * rank + 3) / 4;
+        hipLaunchKernelGGL((topk_merge<TOPK_MERGE_LISTS / 64, TOPK_CHUNK / 64>), dim3(rows + pblocks), dim3(MERGE_THREADS),
                            (size_t)nc1 * k * sizeof(unsigned long long), s, part_v, part_i, nc1, q, k, (long long)nc1 * q,
-                           logits, ld, vocab, vals, idx);
+                           logits, ld, vocab, vals, idx, rows, ha);
         return hipGetLastError();
     }
     while (true) {
@@ -396,7 +416,8 @@ hipError_t topk_rows(const float *logits, long long ld, int rows, int vocab, int
         hipLaunchKernelGGL(topk_wave<TOPK_CHUNK / 64>, dim3(nc, rows), dim3(64), 0, s, in, in_i, n, in_ld, TOPK_CHUNK,
                            k, ov, oi, out_ld);
         hipError_t e = hipGetLastError();
-        if (e != hipSuccess || last) return e;
+        if (e != hipSuccess) return e;
+        if (last) return hidden_projection(hidden, H, w, rank, rows, hout, s);
         in = ov;
         in_i = oi;
         in_ld = out_ld;
